@@ -1,0 +1,171 @@
+"""CPU fp64 oracle for the LSE-weighted combine and its pack / unpack layout.
+
+TEST INFRASTRUCTURE: only the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package. The HIP library and its
+Python binding never do; the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, no fast-math); this module
+only marshals numpy arrays through ctypes. Each function follows the page
+"vllm.v1.attention.ops.dcp_alltoall": ``lse_combine`` / ``combine_f64`` are its
+``_lse_weighted_combine``; ``pack_send``, ``unpack`` and ``unpack_combine`` are
+the steps of its ``dcp_a2a_lse_reduce`` (``_dcp_a2a_pack_send``, the
+all-to-all's chunk-r-to-rank-r placement, ``_dcp_a2a_unpack_combine``).
+
+Parity status: every function here is pinned by the CPU tests (closed forms,
+brute-force sharded attention, library log-sum-exp / softmax, the second
+formulation of the merge on the Ascend SFA context-parallel page, the simulated
+all-to-all). One reading is not pinned against any source: the order of the
+LSE's bytes inside the two tail elements of a packed row (memory order is
+taken); the round trip through pack and unpack is.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liblsec_oracle.so")
+
+BF16, F16 = 0, 1
+_DT = {"bf16": BF16, "f16": F16}
+
+
+def build() -> str:
+    """Compile ``oracle.c`` with gcc (no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f64.restype = ctypes.c_double
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bits_to_f64.argtypes = [_P, ctypes.c_int, _I, _P]
+        lib.oracle_combine_f64.restype = None
+        lib.oracle_combine_f64.argtypes = [_P, _P, _I, _I, _I, ctypes.c_int, _P, _P]
+        lib.oracle_lse_combine.argtypes = [_P, ctypes.c_int, _P, _I, _I, _I, _I, ctypes.c_int,
+                                           _P, _P]
+        lib.oracle_pack_dim.argtypes = [ctypes.c_int]
+        lib.oracle_pack_send.argtypes = [_P, _P, _I, _I, _I, _I, _P]
+        lib.oracle_unpack.argtypes = [_P, _I, _I, _I, _I, _P, _P]
+        lib.oracle_unpack_combine.argtypes = [_P, ctypes.c_int, _I, _I, _I, _I, ctypes.c_int,
+                                              _P, _P]
+        _lib = lib
+    return _lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what}: bad arguments (rc={rc})")
+
+
+def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """bf16 / fp16 bit patterns -> exact fp64 values."""
+    b = _c(bits, np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    _check(_load().oracle_bits_to_f64(b.ctypes.data, _DT[dtype], b.size, out.ctypes.data),
+           "bits_to_f64")
+    return out
+
+
+def combine_f64(o: np.ndarray, lse: np.ndarray, base2: bool = False):
+    """The combine on fp64 planes: o [N, R, D], lse [N, R] -> (y [R, D], L [R])."""
+    o = _c(o, np.float64)
+    lse = _c(lse, np.float64)
+    N, R, D = o.shape
+    if lse.shape != (N, R):
+        raise ValueError("lse shape must be o.shape[:2]")
+    y = np.empty((R, D), dtype=np.float64)
+    L = np.empty((R,), dtype=np.float64)
+    _load().oracle_combine_f64(o.ctypes.data, lse.ctypes.data, N, R, D, int(base2),
+                               y.ctypes.data, L.ctypes.data)
+    return y, L
+
+
+def lse_combine(outputs: np.ndarray, lses: np.ndarray, dtype: str, base2: bool = False):
+    """outputs [N,B,H,D] bf16/fp16 bits, lses [N,B,H] fp32 -> (y [B,H,D] f64, L [B,H] f64)."""
+    o = _c(outputs, np.uint16)
+    l = _c(lses, np.float32)
+    N, B, H, D = o.shape
+    if l.shape != (N, B, H):
+        raise ValueError("lses shape must be outputs.shape[:3]")
+    y = np.empty((B, H, D), dtype=np.float64)
+    L = np.empty((B, H), dtype=np.float64)
+    _check(_load().oracle_lse_combine(o.ctypes.data, _DT[dtype], l.ctypes.data, N, B, H, D,
+                                      int(base2), y.ctypes.data, L.ctypes.data), "lse_combine")
+    return y, L
+
+
+def pack_dim(elem_bytes: int) -> int:
+    return int(_load().oracle_pack_dim(elem_bytes))
+
+
+def pack_send(out: np.ndarray, lse: np.ndarray, N: int) -> np.ndarray:
+    """out [B,H,D] 16-bit bits, lse [B,H] fp32 -> send [N,B,H/N,D+2] 16-bit bits."""
+    o = _c(out, np.uint16)
+    l = _c(lse, np.float32)
+    B, H, D = o.shape
+    if l.shape != (B, H) or N < 1 or H % N:
+        raise ValueError("bad pack_send arguments")
+    send = np.empty((N, B, H // N, D + 2), dtype=np.uint16)
+    _check(_load().oracle_pack_send(o.ctypes.data, l.ctypes.data, N, B, H, D, send.ctypes.data),
+           "pack_send")
+    return send
+
+
+def unpack(recv: np.ndarray, D: int):
+    """recv [N,B,Hl,D+2] -> (outputs [N,B,Hl,D] bits, lses [N,B,Hl] fp32)."""
+    r = _c(recv, np.uint16)
+    N, B, Hl, W = r.shape
+    if W != D + 2:
+        raise ValueError("recv last dim must be D + 2")
+    outs = np.empty((N, B, Hl, D), dtype=np.uint16)
+    lses = np.empty((N, B, Hl), dtype=np.float32)
+    _check(_load().oracle_unpack(r.ctypes.data, N, B, Hl, D, outs.ctypes.data, lses.ctypes.data),
+           "unpack")
+    return outs, lses
+
+
+def unpack_combine(recv: np.ndarray, D: int, dtype: str, base2: bool = False):
+    """recv [N,B,Hl,D+2] -> (y [B,Hl,D] f64, L [B,Hl] f64)."""
+    r = _c(recv, np.uint16)
+    N, B, Hl, W = r.shape
+    if W != D + 2:
+        raise ValueError("recv last dim must be D + 2")
+    y = np.empty((B, Hl, D), dtype=np.float64)
+    L = np.empty((B, Hl), dtype=np.float64)
+    _check(_load().oracle_unpack_combine(r.ctypes.data, _DT[dtype], N, B, Hl, D, int(base2),
+                                         y.ctypes.data, L.ctypes.data), "unpack_combine")
+    return y, L
+
+
+def exchange(sends: list) -> list:
+    """All-to-all placement on N simulated ranks: recv_p[r] = send_r[p].
+
+    ``all_to_all_single`` on a flat buffer sends the r-th equal chunk to rank r
+    and stores what rank r sent in the r-th chunk of the receive buffer.
+    """
+    N = len(sends)
+    return [np.stack([sends[r][p] for r in range(N)]) for p in range(N)]

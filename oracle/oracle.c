@@ -1,0 +1,204 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for the LSE-weighted combine
+ * and its pack / unpack layout.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the package's smoke check and the
+ * benchmark's CPU-baseline leg may load or call this code. The product path
+ * (the HIP library and its Python binding) never does, and shares no code,
+ * header, table or helper with it.
+ *
+ * Sources (the web pages this follows):
+ *  - "vllm.v1.attention.ops.dcp_alltoall", function `_lse_weighted_combine`:
+ *    the combine, step by step (sanitise, max, weights, NaN-weight guard,
+ *    clamped normalisation, weighted sum, global LSE).
+ *  - same page, function `dcp_a2a_lse_reduce`: the packed exchange buffer
+ *    [N, B, H/N, D + P] in the output dtype, filled by `_dcp_a2a_pack_send`,
+ *    moved by an all-to-all whose chunk r goes to rank r, and consumed by
+ *    `_dcp_a2a_unpack_combine`.
+ *
+ * Readings where the pages leave a step open:
+ *  - P (`_dcp_a2a_lse_pack_dim`) is the number of 16-bit output elements that
+ *    hold one fp32 LSE: 4 / sizeof(dtype) = 2 for bf16 and fp16.
+ *  - The fp32 LSE occupies the P tail elements in memory order (its four
+ *    bytes copied verbatim, little-endian on every target here).
+ *  - Plane r of the send buffer holds heads [r*Hl, (r+1)*Hl) in order.
+ *  - Arithmetic is fp64 throughout; inputs are converted exactly (every bf16,
+ *    fp16 and fp32 value is a double). The combined output is returned
+ *    unrounded, in fp64.
+ *
+ * Build: gcc -O2 -std=c11 (no fast-math: the NaN / inf tests must survive).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_BF16 = 0, ORACLE_F16 = 1 };
+
+/* ---- exact storage-to-fp64 conversions ---- */
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_to_f64(uint16_t h) {
+    uint32_t x = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &x, 4);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0x1f) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)m, -24);            /* subnormal: m * 2^-24 */
+    else v = ldexp((double)(m | 0x400), e - 25);            /* (1024+m) * 2^(e-15-10) */
+    return sign ? -v : v;
+}
+
+static double load_elem(const uint16_t* p, int dtype) {
+    return dtype == ORACLE_BF16 ? oracle_bf16_to_f64(*p) : oracle_f16_to_f64(*p);
+}
+
+/* Array form of the conversions above. Returns 0, or -1 on a bad dtype. */
+int oracle_bits_to_f64(const uint16_t* bits, int dtype, int64_t n, double* out) {
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = load_elem(&bits[i], dtype);
+    return 0;
+}
+
+/* ---- the combine on fp64 planes ----
+ *
+ * o   : [N][R][D] partial outputs, R = independent (token, head) rows
+ * lse : [N][R]    per-shard log-sum-exp (base e, or base 2 when base2 != 0)
+ * y   : [R][D]    combined output
+ * L   : [R]       global LSE (may be NULL)
+ *
+ * Follows `_lse_weighted_combine` one row at a time.
+ */
+void oracle_combine_f64(const double* o, const double* lse, int64_t N, int64_t R, int64_t D,
+                        int base2, double* y, double* L) {
+    for (int64_t r = 0; r < R; ++r) {
+        double l[N > 0 ? N : 1];
+        double w[N > 0 ? N : 1];
+        /* NaN and +-inf shard LSEs become -inf. */
+        for (int64_t n = 0; n < N; ++n) {
+            double v = lse[n * R + r];
+            l[n] = (isnan(v) || isinf(v)) ? -INFINITY : v;
+        }
+        /* max over shards; an all -inf max is replaced by 0. */
+        double m = -INFINITY;
+        for (int64_t n = 0; n < N; ++n)
+            if (l[n] > m) m = l[n];
+        if (m == -INFINITY) m = 0.0;
+        /* weights exp(l - m) or 2^(l - m); a NaN weight becomes 0. */
+        for (int64_t n = 0; n < N; ++n) {
+            w[n] = base2 ? pow(2.0, l[n] - m) : exp(l[n] - m);
+            if (isnan(w[n])) w[n] = 0.0;
+        }
+        /* sum of weights (in shard order); normalise by the sum clamped at 1e-10. */
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n) s += w[n];
+        double denom = s < 1e-10 ? 1e-10 : s;
+        double wn[N > 0 ? N : 1];
+        for (int64_t n = 0; n < N; ++n) wn[n] = w[n] / denom;
+        /* weighted sum over shards. */
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) acc += o[(n * R + r) * D + d] * wn[n];
+            y[r * D + d] = acc;
+        }
+        /* global LSE from the unclamped sum. */
+        if (L) L[r] = (base2 ? log2(s) : log(s)) + m;
+    }
+}
+
+/* ---- the combine on storage-typed inputs ----
+ *
+ * outputs : [N][B][H][D] bf16 or fp16 bits;  lses : [N][B][H] fp32
+ * y : [B][H][D] fp64;  L : [B][H] fp64 or NULL.
+ * Converts each row's inputs exactly to fp64, then runs oracle_combine_f64 on
+ * that row. Returns 0, or -1 on a bad argument.
+ */
+int oracle_lse_combine(const uint16_t* outputs, int dtype, const float* lses, int64_t N,
+                       int64_t B, int64_t H, int64_t D, int base2, double* y, double* L) {
+    if (N < 1 || B < 0 || H < 1 || D < 1 || (dtype != ORACLE_BF16 && dtype != ORACLE_F16))
+        return -1;
+    int64_t R = B * H;
+    double* ob = (double*)malloc(sizeof(double) * (size_t)(N * D + N));
+    if (!ob) return -2;
+    double* lb = ob + N * D;
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t n = 0; n < N; ++n) {
+            lb[n] = (double)lses[n * R + r];
+            for (int64_t d = 0; d < D; ++d)
+                ob[n * D + d] = load_elem(&outputs[(n * R + r) * D + d], dtype);
+        }
+        oracle_combine_f64(ob, lb, N, 1, D, base2, &y[r * D], L ? &L[r] : 0);
+    }
+    free(ob);
+    return 0;
+}
+
+/* ---- pack / unpack (pure byte moves) ----
+ *
+ * pack:   out [B][H][D] (16-bit elements), lse [B][H] fp32
+ *      -> send [N][B][Hl][D+2], Hl = H / N:
+ *         send[r][b][h][0:D]   = out[b][r*Hl + h][0:D]
+ *         send[r][b][h][D:D+2] = the 4 bytes of lse[b][r*Hl + h]
+ * unpack: recv [N][B][Hl][D+2] -> outputs [N][B][Hl][D], lses [N][B][Hl]
+ *         (plane n of recv is what source rank n sent).
+ */
+int oracle_pack_dim(int elem_bytes) { return elem_bytes > 0 && elem_bytes <= 4 ? 4 / elem_bytes : -1; }
+
+int oracle_pack_send(const uint16_t* out, const float* lse, int64_t N, int64_t B, int64_t H,
+                     int64_t D, uint16_t* send) {
+    if (N < 1 || B < 0 || H < 1 || D < 1 || H % N != 0) return -1;
+    const int64_t P = 2, Hl = H / N, W = D + P;
+    for (int64_t r = 0; r < N; ++r)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t h = 0; h < Hl; ++h) {
+                int64_t src = b * H + r * Hl + h;
+                uint16_t* dst = &send[((r * B + b) * Hl + h) * W];
+                for (int64_t d = 0; d < D; ++d) dst[d] = out[src * D + d];
+                memcpy(&dst[D], &lse[src], 4);
+            }
+    return 0;
+}
+
+int oracle_unpack(const uint16_t* recv, int64_t N, int64_t B, int64_t Hl, int64_t D,
+                  uint16_t* outputs, float* lses) {
+    if (N < 1 || B < 0 || Hl < 1 || D < 1) return -1;
+    const int64_t P = 2, W = D + P, R = B * Hl;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t r = 0; r < R; ++r) {
+            const uint16_t* src = &recv[(n * R + r) * W];
+            for (int64_t d = 0; d < D; ++d) outputs[(n * R + r) * D + d] = src[d];
+            memcpy(&lses[n * R + r], &src[D], 4);
+        }
+    return 0;
+}
+
+/* unpack, then combine: recv [N][B][Hl][D+2] -> y [B][Hl][D] fp64, L [B][Hl]. */
+int oracle_unpack_combine(const uint16_t* recv, int dtype, int64_t N, int64_t B, int64_t Hl,
+                          int64_t D, int base2, double* y, double* L) {
+    if (N < 1 || B < 0 || Hl < 1 || D < 1 || (dtype != ORACLE_BF16 && dtype != ORACLE_F16))
+        return -1;
+    const int64_t P = 2, W = D + P, R = B * Hl;
+    double* ob = (double*)malloc(sizeof(double) * (size_t)(N * D + N));
+    if (!ob) return -2;
+    double* lb = ob + N * D;
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t* src = &recv[(n * R + r) * W];
+            float lf;
+            memcpy(&lf, &src[D], 4);
+            lb[n] = (double)lf;
+            for (int64_t d = 0; d < D; ++d) ob[n * D + d] = load_elem(&src[d], dtype);
+        }
+        oracle_combine_f64(ob, lb, N, 1, D, base2, &y[r * D], L ? &L[r] : 0);
+    }
+    free(ob);
+    return 0;
+}
