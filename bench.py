@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Throughput of the LSE-weighted combine on one MI355X.
+
+One step is one pass of the hot path over one batch of synthetic input that is
+already resident in HBM:
+
+* ``large_batch`` (default): lsec_combine of N=16 partial outputs
+  [16, 16384, 32, 128] bf16 + LSEs [16, 16384, 32] (base e, global LSE
+  returned) -- the largest workload; 2.3 GB per step, far beyond the 256 MB
+  last-level cache, so every step streams from HBM.
+* ``mla_decode``: lsec_combine, N=8 [8, 4096, 16, 512] bf16, base 2.
+* ``fp16_base2``: lsec_combine, N=4 [4, 256, 32, 128] fp16, base 2, LSE out.
+* ``packed``: one rank's lsec_pack_send ([2048, 64, 128] -> [8, 2048, 8, 130])
+  followed by lsec_unpack_combine of an 8-rank receive buffer (the exchange
+  in between is not part of a single GPU's work).
+
+Workloads under 1 GiB are timed cold: a 1 GiB buffer is rewritten before each
+step, outside the timed events. Kernel time comes from HIP events recorded on
+the stream the kernels run on (torch's current stream). The JSON line also
+carries the roofline of the dominant kernel and the CPU oracle's throughput on
+the host cores (a baseline for context, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "LSE-combine achieved HBM GB/s and (token·head) rows/s; % of peak HBM BW"
+KERNEL_SRC = os.path.join(ROOT, "lse_weighted_merge_combine_amd", "csrc", "lsec.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def combine_bytes(N, B, H, D, s=2, return_lse=False):
+    return N * B * H * (D * s + 4) + B * H * D * s + (B * H * 4 if return_lse else 0)
+
+
+def unpack_combine_bytes(N, B, Hl, D, s=2, return_lse=False):
+    return N * B * Hl * (D + 2) * s + B * Hl * D * s + (B * Hl * 4 if return_lse else 0)
+
+
+def pack_bytes(N, B, H, D, s=2):
+    return B * H * (D * s + 4) + B * H * (D + 2) * s
+
+
+def source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_sha() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- workloads
+
+def build_workload(name: str, dev):
+    """Inputs on the device, preallocated outputs and the step's kernels."""
+    import numpy as np
+    import torch
+
+    import lse_weighted_merge_combine_amd as lsec
+    import synth
+
+    w = synth.WORKLOADS[name]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+
+    def dev_bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+
+    info = {"workload": name, "desc": w.desc, "N": w.N, "B": w.B, "H": w.H, "D": w.D,
+            "io_dtype": w.dtype, "lse_base": "2" if w.base2 else "e",
+            "return_lse": w.return_lse, "parallelism": "none (one GPU)"}
+    if w.kind == "combine":
+        t0 = time.time()
+        o, l = synth.combine_inputs(w)
+        log(f"[bench] generated {name} inputs in {time.time() - t0:.1f}s")
+        og, lg = dev_bits(o), torch.from_numpy(l).to(dev)
+        out = torch.empty((w.B, w.H, w.D), dtype=tdt, device=dev)
+        out_lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev) if w.return_lse else None
+        nbytes = combine_bytes(w.N, w.B, w.H, w.D, 2, w.return_lse)
+        kname = f"combine_rows_kernel<{w.dtype},N={w.N}>"
+
+        def step():
+            lsec.lsec_combine(og, lg, base_e=not w.base2, return_lse=w.return_lse, out=out,
+                              out_lse=out_lse)
+
+        kernels = [(kname, nbytes, step)]
+        host = (o, l)
+        rows = w.B * w.H
+    else:
+        Hl = w.H // w.N
+        outs = [synth.rank_inputs(w, r) for r in range(w.N)]
+        a0 = dev_bits(outs[0][0])
+        l0 = torch.from_numpy(outs[0][1]).to(dev)
+        send = torch.empty((w.N, w.B, Hl, w.D + 2), dtype=tdt, device=dev)
+        # rank 0's receive buffer: plane r is what rank r's pack put in its plane 0
+        recv = torch.empty_like(send)
+        for r in range(w.N):
+            s_r = lsec.lsec_pack_send(dev_bits(outs[r][0]), torch.from_numpy(outs[r][1]).to(dev),
+                                      w.N)
+            recv[r].copy_(s_r[0])
+        torch.cuda.synchronize()
+        out = torch.empty((w.B, Hl, w.D), dtype=tdt, device=dev)
+        out_lse = torch.empty((w.B, Hl), dtype=torch.float32, device=dev)
+
+        def pack():
+            lsec.lsec_pack_send(a0, l0, w.N, send=send)
+
+        def unpack_combine():
+            lsec.lsec_unpack_combine(recv, base_e=not w.base2, return_lse=True, out=out,
+                                     out_lse=out_lse)
+
+        kernels = [("pack_rows_kernel", pack_bytes(w.N, w.B, w.H, w.D), pack),
+                   (f"combine_rows_kernel<{w.dtype},N={w.N},packed>",
+                    unpack_combine_bytes(w.N, w.B, Hl, w.D, 2, True), unpack_combine)]
+        host = None
+        rows = w.B * Hl
+    return w, info, kernels, host, rows
+
+
+# ---------------------------------------------------------------- timing
+
+def time_steps(kernels, steps, warmup, flush_bytes, dev):
+    import torch
+
+    flush = torch.empty(max(flush_bytes // 4, 1), dtype=torch.float32, device=dev) \
+        if flush_bytes else None
+    for i in range(warmup):
+        for _, _, fn in kernels:
+            fn()
+    torch.cuda.synchronize()
+    nk = len(kernels)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))
+        ev[i][0].record()
+        for k, (_, _, fn) in enumerate(kernels):
+            fn()
+            ev[i][k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel_ms = [0.0] * nk
+    for i in range(steps):
+        for k in range(nk):
+            per_kernel_ms[k] += ev[i][k].elapsed_time(ev[i][k + 1])
+    return wall, per_kernel_ms
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, host, threads: int):
+    """Time the fp64 oracle over the workload's rows on `threads` host threads
+    (token ranges split statically; input slicing is not timed)."""
+    import numpy as np
+
+    import oracle
+
+    o, l = host
+    B = w.B
+    threads = max(1, min(threads, B))
+    bounds = np.linspace(0, B, threads + 1).astype(int)
+    parts = [(np.ascontiguousarray(o[:, a:b]), np.ascontiguousarray(l[:, a:b]))
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    oracle._load()
+    errs = []
+
+    def run(p):
+        try:
+            oracle.lse_combine(p[0], p[1], w.dtype, base2=w.base2)
+        except Exception as e:  # noqa: BLE001 - reported below
+            errs.append(e)
+
+    ts = [threading.Thread(target=run, args=(p,)) for p in parts]
+    t0 = time.perf_counter()
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    dt = time.perf_counter() - t0
+    if errs:
+        raise errs[0]
+    nbytes = combine_bytes(w.N, w.B, w.H, w.D, 2, w.return_lse)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "rows_per_s": round(w.B * w.H / dt, 1),
+            "sample": f"the whole workload ({w.B * w.H} rows, N={w.N}, D={w.D}) through the fp64 "
+                      f"C oracle, token ranges split over {threads} threads"}
+
+
+def cpu_info():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large_batch",
+                    choices=["large_batch", "mla_decode", "fp16_base2", "packed", "small"])
+    ap.add_argument("--flush-mib", type=int, default=-1,
+                    help="cache flush before each step (default: 1024 MiB if the step's "
+                         "working set is under 1 GiB, else none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a 1 GiB device copy (PMC calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported; the combine's multi-GPU exchange is not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import __graft_entry__
+    __graft_entry__._ensure_built()
+    import lse_weighted_merge_combine_amd as lsec
+    lsec.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    w, info, kernels, host, rows = build_workload(args.workload, dev)
+    step_bytes = sum(b for _, b, _ in kernels)
+    flush_mib = args.flush_mib if args.flush_mib >= 0 else (1024 if step_bytes < (1 << 30) else 0)
+    log(f"[bench] {args.workload}: {step_bytes / 1e6:.1f} MB per step, warmup {args.warmup}, "
+        f"steps {args.steps}, flush {flush_mib} MiB")
+    wall, per_kernel_ms = time_steps(kernels, args.steps, args.warmup, flush_mib << 20, dev)
+    gpu_ms = sum(per_kernel_ms)
+    ms_per_step = gpu_ms / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] wall {wall:.3f}s for {args.steps} steps; kernels {gpu_ms:.3f} ms")
+
+    # dominant kernel: the one with the largest share of the step's time
+    k = max(range(len(kernels)), key=lambda i: per_kernel_ms[i])
+    kname, kbytes, _ = kernels[k]
+    k_ms = per_kernel_ms[k] / args.steps
+    achieved = kbytes / (k_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "bytes_per_launch": kbytes, "avg_launch_us": round(k_ms * 1e3, 3),
+                "traffic": load_traffic(args.workload, kname)}
+    kernel_detail = [{"kernel": n, "bytes": b, "avg_us": round(per_kernel_ms[i] / args.steps * 1e3, 3),
+                      "GB/s": round(b / (per_kernel_ms[i] / args.steps * 1e-3) / 1e9, 1)}
+                     for i, (n, b, _) in enumerate(kernels)]
+
+    cpu = None
+    if not args.no_cpu_baseline and host is not None:
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(w, host, args.cpu_threads)
+        cpu["cpu_model"] = cpu_info()
+        log(f"[bench] oracle {cpu['seconds']}s on {cpu['cores']} threads")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator)", "config": info,
+        "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "step_bytes": step_bytes, "cache_flush_mib": flush_mib,
+        "wall_s": round(wall, 4), "kernels": kernel_detail,
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

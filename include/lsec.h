@@ -1,0 +1,134 @@
+/*
+ * lsec.h -- C ABI of the LSE-weighted combine library (liblsec.so), gfx950.
+ *
+ * The operations are those of the page "vllm.v1.attention.ops.dcp_alltoall":
+ *  - lsec_combine        : `_lse_weighted_combine` (merge N partial attention
+ *                          outputs by their log-sum-exp weights);
+ *  - lsec_pack_send      : `_dcp_a2a_pack_send` inside `dcp_a2a_lse_reduce`
+ *                          (output + fp32 LSE packed into one output-dtype
+ *                          buffer, one plane per destination rank);
+ *  - lsec_unpack_combine : `_dcp_a2a_unpack_combine` (the receive side: read
+ *                          the packed planes and combine them);
+ *  - lsec_unpack         : the layout half of that step alone;
+ *  - lsec_pack_dim       : `_dcp_a2a_lse_pack_dim`.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers unless stated otherwise. Tensors are dense,
+ *    row-major, last dimension fastest, with no padding between rows.
+ *  - The caller owns and allocates every buffer; the library never allocates,
+ *    frees or synchronises. Work is enqueued on `stream` (a hipStream_t; NULL
+ *    means the null stream) and the call returns at once.
+ *  - Elements of `outputs`, `out`, `send`, `recv` are 16-bit (bf16 or fp16,
+ *    selected by `dtype`) and must be 2-byte aligned; LSE arrays are fp32 and
+ *    must be 4-byte aligned. Faster kernels are chosen when the buffers are
+ *    16-byte aligned (separate layout) or 4-byte aligned (packed layout) and D
+ *    is a multiple of 8 no larger than 2048; other cases take a general path
+ *    with the same results.
+ *  - Every argument is checked before anything is enqueued; on an error
+ *    nothing is enqueued and a status other than LSEC_OK is returned. A
+ *    pointer may be NULL only when the array it names has no elements.
+ *  - Input and output buffers must not overlap.
+ *  - Arithmetic: fp32 accumulation; outputs are rounded to the input dtype
+ *    (round to nearest even); the global LSE is fp32. NaN and +-inf shard LSEs
+ *    count as -inf; a row whose shard LSEs are all non-finite yields a zero
+ *    output and a -inf global LSE. Zero-weight shards are still multiplied, so
+ *    a NaN in any shard's output propagates to the combined output.
+ */
+#ifndef LSEC_H
+#define LSEC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    LSEC_OK = 0,
+    LSEC_ERR_NULL = 1,         /* a required pointer is NULL */
+    LSEC_ERR_SHAPE = 2,        /* N < 1, B < 0, H < 1, D < 1, or a size overflows int64 */
+    LSEC_ERR_DIVISIBILITY = 3, /* H is not a multiple of N (pack_send) */
+    LSEC_ERR_DTYPE = 4,        /* dtype is neither LSEC_BF16 nor LSEC_FP16 */
+    LSEC_ERR_ALIGNMENT = 5,    /* a pointer is not aligned to its element size */
+    LSEC_ERR_BASE = 6,         /* base is neither LSEC_BASE_E nor LSEC_BASE_2 */
+    LSEC_ERR_LAUNCH = 7        /* the HIP runtime rejected the kernel launch */
+};
+
+/* Element types of the attention outputs. */
+enum { LSEC_BF16 = 0, LSEC_FP16 = 1 };
+
+/* Base of the log-sum-exp values (`is_lse_base_on_e` true / false). */
+enum { LSEC_BASE_E = 0, LSEC_BASE_2 = 1 };
+
+/*
+ * lsec_pack_dim -- number of output-dtype elements that carry one fp32 LSE in
+ * a packed row: 4 / sizeof(element) = 2 for bf16 and fp16. Returns -1 for an
+ * unknown dtype. (`_dcp_a2a_lse_pack_dim`; its body is not on the page, this
+ * is the reading that makes the packed row D + P elements wide.)
+ */
+int lsec_pack_dim(int dtype);
+
+/*
+ * lsec_combine -- `_lse_weighted_combine`.
+ *   outputs : [N, B, H, D] dtype   partial attention output of each shard
+ *   lses    : [N, B, H]    fp32    per-shard log-sum-exp, base `base`
+ *   out     : [B, H, D]    dtype   combined output (written)
+ *   out_lse : [B, H]       fp32    global LSE (written), or NULL to skip it
+ *                                  (`return_lse` false)
+ * Per (b, h) row: l'_n = -inf if l_n is NaN or +-inf; m = max_n l'_n (0 if
+ * that is -inf); w_n = exp(l'_n - m) or 2^(l'_n - m); S = sum_n w_n;
+ * out = sum_n outputs_n * w_n / max(S, 1e-10); out_lse = ln S + m or
+ * log2 S + m. N = 1 with a finite LSE returns its input unchanged.
+ * Errors: NULL, SHAPE, DTYPE, BASE, ALIGNMENT, LAUNCH.
+ */
+int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
+                 int64_t D, int dtype, int base, void* out, float* out_lse, void* stream);
+
+/*
+ * lsec_pack_send -- `_dcp_a2a_pack_send`.
+ *   attn_out : [B, H, D]           dtype  this rank's partial attention output
+ *   attn_lse : [B, H]              fp32   its log-sum-exp
+ *   send     : [N, B, H/N, D + 2]  dtype  packed send buffer (written)
+ * Plane r holds heads [r*H/N, (r+1)*H/N): the chunk an all-to-all delivers to
+ * rank r. In each packed row, elements 0..D-1 are the output row, and elements
+ * D and D+1 hold the four bytes of the fp32 LSE in memory order (element D =
+ * bits 0..15, element D+1 = bits 16..31). Pure bit moves (NaN payloads kept).
+ * Errors: NULL, SHAPE, DIVISIBILITY (H % N != 0), DTYPE, ALIGNMENT, LAUNCH.
+ */
+int lsec_pack_send(const void* attn_out, const float* attn_lse, int64_t N, int64_t B, int64_t H,
+                   int64_t D, int dtype, void* send, void* stream);
+
+/*
+ * lsec_unpack_combine -- `_dcp_a2a_unpack_combine`.
+ *   recv    : [N, B, Hl, D + 2] dtype  packed planes; plane n came from rank n
+ *   out     : [B, Hl, D]        dtype  combined output (written)
+ *   out_lse : [B, Hl]           fp32   global LSE (written), or NULL
+ * Equivalent to lsec_unpack followed by lsec_combine with H = Hl, in one pass.
+ * Errors: NULL, SHAPE, DTYPE, BASE, ALIGNMENT, LAUNCH.
+ */
+int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,
+                        int base, void* out, float* out_lse, void* stream);
+
+/*
+ * lsec_unpack -- the layout half of the receive step.
+ *   recv    : [N, B, Hl, D + 2] dtype
+ *   outputs : [N, B, Hl, D]     dtype  (written)
+ *   lses    : [N, B, Hl]        fp32   (written; the tail bits reinterpreted)
+ * Pure bit moves; the inverse of lsec_pack_send's per-row layout.
+ * Errors: NULL, SHAPE, DTYPE, ALIGNMENT, LAUNCH.
+ */
+int lsec_unpack(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,
+                void* outputs, float* lses, void* stream);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* lsec_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int lsec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSEC_H */

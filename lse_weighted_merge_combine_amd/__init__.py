@@ -1,0 +1,260 @@
+"""LSE-weighted combine of partial attention outputs on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``liblsec.so`` (declared in
+``include/lsec.h``). Every step of the computation runs in the library's HIP
+kernels; this module only checks tensors, allocates outputs with PyTorch and
+passes raw device pointers and the current HIP stream. There is no CPU or
+PyTorch fallback: if the library is missing the import of an entry point fails.
+
+Entry points (same names as the C ABI):
+
+* ``lsec_combine(outputs, lses, ...)`` -- ``_lse_weighted_combine`` of the page
+  "vllm.v1.attention.ops.dcp_alltoall": ``[N,B,H,D]`` + ``[N,B,H]`` ->
+  ``[B,H,D]`` (+ ``[B,H]``).
+* ``lsec_pack_send(attn_out, attn_lse, N)`` -- that page's
+  ``_dcp_a2a_pack_send``: ``[B,H,D]`` + ``[B,H]`` -> ``[N,B,H/N,D+2]``.
+* ``lsec_unpack_combine(recv, ...)`` -- ``_dcp_a2a_unpack_combine``.
+* ``lsec_unpack(recv)`` -- the layout half of the receive step.
+* ``lsec_pack_dim(dtype)`` -- ``_dcp_a2a_lse_pack_dim``.
+
+``lse_weighted_combine`` keeps the argument names of the page's function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblsec.so")
+
+LSEC_OK = 0
+LSEC_ERR_NULL = 1
+LSEC_ERR_SHAPE = 2
+LSEC_ERR_DIVISIBILITY = 3
+LSEC_ERR_DTYPE = 4
+LSEC_ERR_ALIGNMENT = 5
+LSEC_ERR_BASE = 6
+LSEC_ERR_LAUNCH = 7
+LSEC_BF16 = 0
+LSEC_FP16 = 1
+LSEC_BASE_E = 0
+LSEC_BASE_2 = 1
+
+_DTYPES = {torch.bfloat16: LSEC_BF16, torch.float16: LSEC_FP16}
+_VALUE_ERRORS = (LSEC_ERR_SHAPE, LSEC_ERR_DIVISIBILITY, LSEC_ERR_DTYPE, LSEC_ERR_BASE)
+
+_lib = None
+
+
+class LsecError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblsec.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.lsec_version.restype = I
+    lib.lsec_version.argtypes = []
+    lib.lsec_pack_dim.restype = I
+    lib.lsec_pack_dim.argtypes = [I]
+    lib.lsec_status_string.restype = ctypes.c_char_p
+    lib.lsec_status_string.argtypes = [I]
+    lib.lsec_combine.restype = I
+    lib.lsec_combine.argtypes = [P, P, I64, I64, I64, I64, I, I, P, P, P]
+    lib.lsec_pack_send.restype = I
+    lib.lsec_pack_send.argtypes = [P, P, I64, I64, I64, I64, I, P, P]
+    lib.lsec_unpack_combine.restype = I
+    lib.lsec_unpack_combine.argtypes = [P, I64, I64, I64, I64, I, I, P, P, P]
+    lib.lsec_unpack.restype = I
+    lib.lsec_unpack.argtypes = [P, I64, I64, I64, I64, I, P, P, P]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().lsec_status_string(int(status)).decode()
+
+
+def _raise_on(status: int, what: str) -> None:
+    if status == LSEC_OK:
+        return
+    if status in _VALUE_ERRORS:
+        raise ValueError(f"{what}: {status_string(status)}")
+    raise LsecError(status, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}: bfloat16 or float16 only") from None
+
+
+def _check_dev(*ts: torch.Tensor) -> torch.device:
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError("tensors must live on a GPU device")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _stream(dev: torch.device, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def lsec_pack_dim(dtype: torch.dtype) -> int:
+    """Output-dtype elements per packed fp32 LSE (2 for bf16 / fp16)."""
+    code = _DTYPES.get(dtype, -1)
+    r = load_library().lsec_pack_dim(code)
+    if r < 0:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return r
+
+
+def lsec_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
+                 return_lse: bool = False, out: torch.Tensor | None = None,
+                 out_lse: torch.Tensor | None = None, stream=None):
+    """Combine partial outputs [N,B,H,D] by their LSEs [N,B,H] (fp32).
+
+    Returns the combined [B,H,D] output in the input dtype, and the [B,H] fp32
+    global LSE when ``return_lse``. ``base_e`` False means base-2 LSEs.
+    """
+    lib = load_library()
+    if outputs.dim() != 4 or lses.dim() != 3 or tuple(lses.shape) != tuple(outputs.shape[:3]):
+        raise ValueError(f"expected outputs [N,B,H,D] and lses [N,B,H], got "
+                         f"{tuple(outputs.shape)} and {tuple(lses.shape)}")
+    if lses.dtype != torch.float32:
+        raise ValueError("lses must be float32")
+    dt = _dtype_code(outputs)
+    N, B, H, D = outputs.shape
+    dev = _check_dev(outputs, lses)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=outputs.dtype, device=dev)
+    if return_lse and out_lse is None:
+        out_lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check_out(out, (B, H, D), outputs.dtype, dev)
+    if return_lse:
+        _check_out(out_lse, (B, H), torch.float32, dev)
+    st = lib.lsec_combine(_ptr(outputs), _ptr(lses), N, B, H, D, dt,
+                          LSEC_BASE_E if base_e else LSEC_BASE_2, _ptr(out),
+                          _ptr(out_lse) if return_lse else None, _stream(dev, stream))
+    _raise_on(st, "lsec_combine")
+    return (out, out_lse) if return_lse else out
+
+
+def lsec_pack_send(attn_out: torch.Tensor, attn_lse: torch.Tensor, N: int,
+                   send: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Pack [B,H,D] output + [B,H] fp32 LSE into the [N,B,H/N,D+2] send buffer."""
+    lib = load_library()
+    if attn_out.dim() != 3 or attn_lse.dim() != 2 or \
+            tuple(attn_lse.shape) != tuple(attn_out.shape[:2]):
+        raise ValueError(f"expected attn_out [B,H,D] and attn_lse [B,H], got "
+                         f"{tuple(attn_out.shape)} and {tuple(attn_lse.shape)}")
+    if attn_lse.dtype != torch.float32:
+        raise ValueError("attn_lse must be float32")
+    dt = _dtype_code(attn_out)
+    B, H, D = attn_out.shape
+    if N < 1 or H % N != 0:
+        raise ValueError(f"H={H} must be divisible by the number of ranks {N}.")
+    dev = _check_dev(attn_out, attn_lse)
+    shape = (N, B, H // N, D + lsec_pack_dim(attn_out.dtype))
+    if send is None:
+        send = torch.empty(shape, dtype=attn_out.dtype, device=dev)
+    _check_out(send, shape, attn_out.dtype, dev)
+    st = lib.lsec_pack_send(_ptr(attn_out), _ptr(attn_lse), N, B, H, D, dt, _ptr(send),
+                            _stream(dev, stream))
+    _raise_on(st, "lsec_pack_send")
+    return send
+
+
+def _recv_dims(recv: torch.Tensor):
+    if recv.dim() != 4:
+        raise ValueError(f"expected recv [N,B,Hl,D+2], got {tuple(recv.shape)}")
+    N, B, Hl, W = recv.shape
+    D = W - lsec_pack_dim(recv.dtype)
+    if D < 1:
+        raise ValueError("recv rows are too short to hold an output and an LSE")
+    return N, B, Hl, D
+
+
+def lsec_unpack_combine(recv: torch.Tensor, base_e: bool = True, return_lse: bool = False,
+                        out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None,
+                        stream=None):
+    """Combine the N packed planes of recv [N,B,Hl,D+2] -> [B,Hl,D] (+ [B,Hl])."""
+    lib = load_library()
+    dt = _dtype_code(recv)
+    N, B, Hl, D = _recv_dims(recv)
+    dev = _check_dev(recv)
+    if out is None:
+        out = torch.empty((B, Hl, D), dtype=recv.dtype, device=dev)
+    if return_lse and out_lse is None:
+        out_lse = torch.empty((B, Hl), dtype=torch.float32, device=dev)
+    _check_out(out, (B, Hl, D), recv.dtype, dev)
+    if return_lse:
+        _check_out(out_lse, (B, Hl), torch.float32, dev)
+    st = lib.lsec_unpack_combine(_ptr(recv), N, B, Hl, D, dt,
+                                 LSEC_BASE_E if base_e else LSEC_BASE_2, _ptr(out),
+                                 _ptr(out_lse) if return_lse else None, _stream(dev, stream))
+    _raise_on(st, "lsec_unpack_combine")
+    return (out, out_lse) if return_lse else out
+
+
+def lsec_unpack(recv: torch.Tensor, outputs: torch.Tensor | None = None,
+                lses: torch.Tensor | None = None, stream=None):
+    """Split recv [N,B,Hl,D+2] into outputs [N,B,Hl,D] and fp32 lses [N,B,Hl]."""
+    lib = load_library()
+    dt = _dtype_code(recv)
+    N, B, Hl, D = _recv_dims(recv)
+    dev = _check_dev(recv)
+    if outputs is None:
+        outputs = torch.empty((N, B, Hl, D), dtype=recv.dtype, device=dev)
+    if lses is None:
+        lses = torch.empty((N, B, Hl), dtype=torch.float32, device=dev)
+    _check_out(outputs, (N, B, Hl, D), recv.dtype, dev)
+    _check_out(lses, (N, B, Hl), torch.float32, dev)
+    st = lib.lsec_unpack(_ptr(recv), N, B, Hl, D, dt, _ptr(outputs), _ptr(lses),
+                         _stream(dev, stream))
+    _raise_on(st, "lsec_unpack")
+    return outputs, lses
+
+
+def lse_weighted_combine(outputs: torch.Tensor, lses: torch.Tensor, return_lse: bool = False,
+                         is_lse_base_on_e: bool = True):
+    """The page's ``_lse_weighted_combine(outputs, lses, return_lse, is_lse_base_on_e)``,
+    computed by the HIP kernel (output in the input dtype)."""
+    return lsec_combine(outputs, lses, base_e=is_lse_base_on_e, return_lse=return_lse)
+
+
+def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or \
+            not t.is_contiguous():
+        raise ValueError(f"output tensor must be contiguous {dtype} of shape {tuple(shape)} "
+                         f"on {dev}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+__all__ = [
+    "lsec_pack_dim", "lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
+    "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
+]

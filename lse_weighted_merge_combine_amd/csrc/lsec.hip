@@ -1,0 +1,571 @@
+// lsec.hip -- HIP kernels (gfx950) and the C ABI of liblsec.so.
+//
+// The operations are those of the page "vllm.v1.attention.ops.dcp_alltoall":
+// `_lse_weighted_combine` (lsec_combine), and the pack / unpack-and-combine
+// steps of `dcp_a2a_lse_reduce` (lsec_pack_send, lsec_unpack_combine,
+// lsec_unpack). The argument contract of each entry point is in lsec.h.
+//
+// Design. The combine is a streaming reduction: per (token, head) row it reads
+// N planes of D 16-bit values and writes one, so it is bound by HBM bandwidth
+// at about one FMA per byte. It runs on plain VALU (no MFMA): a group of D/8
+// consecutive lanes owns a row, each lane moving 16 bytes (8 elements) per
+// plane. Every lane loads the row's N LSE values itself (the loads are
+// broadcasts inside the group) and computes the weights in registers, so the
+// kernels need no LDS and no cross-lane traffic. All N plane loads of a lane
+// are issued before the first is consumed, which keeps N x 16 B per lane in
+// flight. Packed rows are D + 2 elements wide, so in the packed layout a row
+// start is only 4-byte aligned; gfx950 serves dwordx4 accesses at 4-byte
+// alignment, so the packed kernels read and write those rows directly.
+//
+// Build with -Xclang -target-feature -Xclang -packed-fp32-ops and without
+// fast-math (the NaN / infinity tests must survive).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsec.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kFastMaxD = 2048;  // D / 8 lanes per row must fit one block
+
+// ---------------------------------------------------------------- helpers
+
+// Unsigned 32-bit division by an invariant divisor d >= 1 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// q = (umulhi(x, m) + x) >> l with l = ceil(log2 d), m = 2^32 (2^l - d) / d + 1.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{d, uint32_t(m), l};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f) {
+    return uint32_t((uint64_t(__umulhi(x, f.m)) + x) >> f.l);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct __attribute__((aligned(4))) U32x4A4 {
+    uint32_t x, y, z, w;
+};
+
+// 16-byte load / store at a 16-byte aligned address.
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+// 16-byte load / store at a 4-byte aligned address (packed rows).
+__device__ __forceinline__ u32x4 ld16_a4(const uint16_t* p) {
+    U32x4A4 t = *reinterpret_cast<const U32x4A4*>(p);
+    u32x4 v = {t.x, t.y, t.z, t.w};
+    return v;
+}
+__device__ __forceinline__ void st16_a4(uint16_t* p, u32x4 v) {
+    U32x4A4 t = {v.x, v.y, v.z, v.w};
+    *reinterpret_cast<U32x4A4*>(p) = t;
+}
+
+// Element type: decode two packed 16-bit values, encode two floats (RNE).
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<LSEC_BF16> {
+    __device__ static __forceinline__ void dec2(uint32_t u, float& a, float& b) {
+        a = __uint_as_float(u << 16);
+        b = __uint_as_float(u & 0xffff0000u);
+    }
+    __device__ static __forceinline__ uint32_t enc2(float a, float b) {
+        bf16x2 p = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32: round to nearest even
+        return __builtin_bit_cast(uint32_t, p);
+    }
+    __device__ static __forceinline__ float dec1(uint16_t h) {
+        return __uint_as_float(uint32_t(h) << 16);
+    }
+    __device__ static __forceinline__ uint16_t enc1(float a) {
+        return __builtin_bit_cast(uint16_t, (__bf16)a);
+    }
+};
+
+template <>
+struct Elem<LSEC_FP16> {
+    __device__ static __forceinline__ void dec2(uint32_t u, float& a, float& b) {
+        f16x2 h = __builtin_bit_cast(f16x2, u);
+        a = (float)h.x;
+        b = (float)h.y;
+    }
+    __device__ static __forceinline__ uint32_t enc2(float a, float b) {
+        f16x2 p = {(_Float16)a, (_Float16)b};  // v_cvt_f16_f32: round to nearest even
+        return __builtin_bit_cast(uint32_t, p);
+    }
+    __device__ static __forceinline__ float dec1(uint16_t h) {
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+    __device__ static __forceinline__ uint16_t enc1(float a) {
+        return __builtin_bit_cast(uint16_t, (_Float16)a);
+    }
+};
+
+// NaN and +-inf shard LSEs count as -inf (exponent field all ones).
+__device__ __forceinline__ float sanitize(float l) {
+    return (__float_as_uint(l) & 0x7f800000u) == 0x7f800000u ? -__builtin_inff() : l;
+}
+
+// Weight of a shard: 2^(x * scale), x = l' - m <= 0 or -inf. scale = log2(e)
+// for base-e LSEs (e^x = 2^(x log2 e)) and 1 for base 2. v_exp_f32 maps -inf
+// to 0. A NaN weight (not reachable: x is never NaN) would become 0.
+__device__ __forceinline__ float weight(float x, float scale) {
+    float w = __builtin_amdgcn_exp2f(x * scale);
+    return w != w ? 0.0f : w;
+}
+
+// Global LSE: ln S + m = log2(S) ln 2 + m (base e), or log2(S) + m (base 2).
+// S = 0 (all shards non-finite) gives -inf.
+__device__ __forceinline__ float global_lse(float s, float m, float inv_scale) {
+    return log2f(s) * inv_scale + m;
+}
+
+// Accumulate one 16-byte chunk (8 elements) scaled by w into acc[8].
+template <int DT>
+__device__ __forceinline__ void fma8(u32x4 v, float w, float (&acc)[8]) {
+    float a, b;
+    Elem<DT>::dec2(v.x, a, b);
+    acc[0] = fmaf(a, w, acc[0]);
+    acc[1] = fmaf(b, w, acc[1]);
+    Elem<DT>::dec2(v.y, a, b);
+    acc[2] = fmaf(a, w, acc[2]);
+    acc[3] = fmaf(b, w, acc[3]);
+    Elem<DT>::dec2(v.z, a, b);
+    acc[4] = fmaf(a, w, acc[4]);
+    acc[5] = fmaf(b, w, acc[5]);
+    Elem<DT>::dec2(v.w, a, b);
+    acc[6] = fmaf(a, w, acc[6]);
+    acc[7] = fmaf(b, w, acc[7]);
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 enc8(const float (&acc)[8]) {
+    u32x4 r = {Elem<DT>::enc2(acc[0], acc[1]), Elem<DT>::enc2(acc[2], acc[3]),
+               Elem<DT>::enc2(acc[4], acc[5]), Elem<DT>::enc2(acc[6], acc[7])};
+    return r;
+}
+
+// ---------------------------------------------------------------- combine (fast path)
+//
+// Row r of plane n starts at element n * plane + r * stride of `src`.
+// Separate layout (lsec_combine): stride = D, plane = rows * D, LSE n of row r
+// at lse[n * rows + r]. Packed layout (lsec_unpack_combine): stride = D + 2,
+// plane = rows * (D + 2), LSE = the fp32 in elements D, D+1 of the row.
+// Launch: rows_per_block = kBlock / (D/8) rows per block, lane group D/8.
+template <int DT, int NT, bool PACKED>
+__global__ __launch_bounds__(kBlock) void combine_rows_kernel(
+    const uint16_t* __restrict__ src, const float* __restrict__ lse, int n_rt, uint32_t rows,
+    FastDiv g, uint32_t rows_per_block, int64_t stride, int64_t plane, int D, float scale,
+    float inv_scale, uint16_t* __restrict__ out, float* __restrict__ out_lse) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t rib = fdiv(t, g);
+    const uint32_t lane = t - rib * g.d;
+    if (rib >= rows_per_block) return;
+    const uint32_t row = blockIdx.x * rows_per_block + rib;
+    if (row >= rows) return;
+    const int N = NT > 0 ? NT : n_rt;
+    const uint16_t* rp = src + int64_t(row) * stride;
+    const uint16_t* cp = rp + lane * 8;
+
+    auto load_lse = [&](int n) -> float {
+        if (PACKED) return *reinterpret_cast<const float*>(rp + n * plane + D);
+        return lse[int64_t(n) * rows + row];
+    };
+    auto load_chunk = [&](int n) -> u32x4 {
+        if (PACKED) return ld16_a4(cp + n * plane);
+        return ld16(cp + n * plane);
+    };
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float m, s;
+    if constexpr (NT > 0) {
+        float l[NT];
+        u32x4 v[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) l[n] = load_lse(n);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) v[n] = load_chunk(n);
+        // Keep every load above this point: all N chunks stay in flight while
+        // the weights are computed.
+        __builtin_amdgcn_sched_barrier(0);
+        m = -__builtin_inff();
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            l[n] = sanitize(l[n]);
+            m = fmaxf(m, l[n]);
+        }
+        if (m == -__builtin_inff()) m = 0.0f;
+        float w[NT];
+        s = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            w[n] = weight(l[n] - m, scale);
+            s += w[n];
+        }
+        const float inv = 1.0f / fmaxf(s, 1e-10f);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) fma8<DT>(v[n], w[n] * inv, acc);
+    } else {
+        m = -__builtin_inff();
+        for (int n = 0; n < N; ++n) m = fmaxf(m, sanitize(load_lse(n)));
+        if (m == -__builtin_inff()) m = 0.0f;
+        s = 0.0f;
+        for (int n = 0; n < N; ++n) s += weight(sanitize(load_lse(n)) - m, scale);
+        const float inv = 1.0f / fmaxf(s, 1e-10f);
+        for (int n0 = 0; n0 < N; n0 += 8) {
+            u32x4 v[8];
+            float w[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (n0 + k < N) {
+                    v[k] = load_chunk(n0 + k);
+                    w[k] = weight(sanitize(load_lse(n0 + k)) - m, scale) * inv;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (n0 + k < N) fma8<DT>(v[k], w[k], acc);
+        }
+    }
+    st16(out + int64_t(row) * D + lane * 8, enc8<DT>(acc));
+    if (out_lse != nullptr && lane == 0) out_lse[row] = global_lse(s, m, inv_scale);
+}
+
+// ---------------------------------------------------------------- combine (general path)
+//
+// Any D, 2-byte aligned buffers. One thread per (row, element); each thread
+// recomputes its row's weights. Packed rows read the LSE as two 16-bit halves.
+template <int DT, bool PACKED>
+__global__ __launch_bounds__(kBlock) void combine_elems_kernel(
+    const uint16_t* __restrict__ src, const float* __restrict__ lse, int N, int64_t rows,
+    int64_t stride, int64_t plane, int64_t D, float scale, float inv_scale,
+    uint16_t* __restrict__ out, float* __restrict__ out_lse) {
+    const int64_t total = rows * D;
+    for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kBlock) {
+        const int64_t row = i / D;
+        const int64_t d = i - row * D;
+        const uint16_t* rp = src + row * stride;
+        auto load_lse = [&](int n) -> float {
+            if (PACKED) {
+                const uint16_t* q = rp + n * plane + D;
+                return __uint_as_float(uint32_t(q[0]) | (uint32_t(q[1]) << 16));
+            }
+            return lse[int64_t(n) * rows + row];
+        };
+        float m = -__builtin_inff();
+        for (int n = 0; n < N; ++n) m = fmaxf(m, sanitize(load_lse(n)));
+        if (m == -__builtin_inff()) m = 0.0f;
+        float s = 0.0f;
+        for (int n = 0; n < N; ++n) s += weight(sanitize(load_lse(n)) - m, scale);
+        const float inv = 1.0f / fmaxf(s, 1e-10f);
+        float acc = 0.0f;
+        for (int n = 0; n < N; ++n) {
+            float w = weight(sanitize(load_lse(n)) - m, scale) * inv;
+            acc = fmaf(Elem<DT>::dec1(rp[n * plane + d]), w, acc);
+        }
+        out[row * D + d] = Elem<DT>::enc1(acc);
+        if (out_lse != nullptr && d == 0) out_lse[row] = global_lse(s, m, inv_scale);
+    }
+}
+
+// ---------------------------------------------------------------- pack (fast path)
+//
+// Send row s = (r * B + b) * Hl + hl takes attention-output row
+// src = b * H + r * Hl + hl: D elements, then the fp32 LSE's 32 bits.
+__global__ __launch_bounds__(kBlock) void pack_rows_kernel(
+    const uint16_t* __restrict__ in, const float* __restrict__ lse, uint32_t send_rows,
+    FastDiv g, uint32_t rows_per_block, FastDiv hl_div, FastDiv b_div, uint32_t H, int D,
+    uint16_t* __restrict__ send) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t rib = fdiv(t, g);
+    const uint32_t lane = t - rib * g.d;
+    if (rib >= rows_per_block) return;
+    const uint32_t s = blockIdx.x * rows_per_block + rib;
+    if (s >= send_rows) return;
+    const uint32_t rb = fdiv(s, hl_div);
+    const uint32_t hl = s - rb * hl_div.d;
+    const uint32_t r = fdiv(rb, b_div);
+    const uint32_t b = rb - r * b_div.d;
+    const uint32_t src = b * H + r * hl_div.d + hl;
+    uint16_t* dp = send + int64_t(s) * (D + 2);
+    st16_a4(dp + lane * 8, ld16(in + int64_t(src) * D + lane * 8));
+    if (lane == 0) *reinterpret_cast<float*>(dp + D) = lse[src];
+}
+
+// ---------------------------------------------------------------- pack (general path)
+__global__ __launch_bounds__(kBlock) void pack_elems_kernel(
+    const uint16_t* __restrict__ in, const float* __restrict__ lse, int64_t B, int64_t H,
+    int64_t Hl, int64_t D, int64_t total, uint16_t* __restrict__ send) {
+    const int64_t W = D + 2;
+    for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kBlock) {
+        const int64_t s = i / W;
+        const int64_t d = i - s * W;
+        const int64_t rb = s / Hl;
+        const int64_t hl = s - rb * Hl;
+        const int64_t r = rb / B;
+        const int64_t b = rb - r * B;
+        const int64_t src = b * H + r * Hl + hl;
+        uint16_t v;
+        if (d < D) {
+            v = in[src * D + d];
+        } else {
+            const uint32_t bits = __float_as_uint(lse[src]);
+            v = uint16_t(d == D ? (bits & 0xffffu) : (bits >> 16));
+        }
+        send[i] = v;
+    }
+}
+
+// ---------------------------------------------------------------- unpack
+__global__ __launch_bounds__(kBlock) void unpack_rows_kernel(
+    const uint16_t* __restrict__ recv, uint32_t total_rows, FastDiv g, uint32_t rows_per_block,
+    int D, uint16_t* __restrict__ outs, float* __restrict__ lses) {
+    const uint32_t t = threadIdx.x;
+    const uint32_t rib = fdiv(t, g);
+    const uint32_t lane = t - rib * g.d;
+    if (rib >= rows_per_block) return;
+    const uint32_t q = blockIdx.x * rows_per_block + rib;
+    if (q >= total_rows) return;
+    const uint16_t* sp = recv + int64_t(q) * (D + 2);
+    st16(outs + int64_t(q) * D + lane * 8, ld16_a4(sp + lane * 8));
+    if (lane == 0) lses[q] = *reinterpret_cast<const float*>(sp + D);
+}
+
+__global__ __launch_bounds__(kBlock) void unpack_elems_kernel(
+    const uint16_t* __restrict__ recv, int64_t total_rows, int64_t D,
+    uint16_t* __restrict__ outs, float* __restrict__ lses) {
+    const int64_t W = D + 2;
+    const int64_t total = total_rows * W;
+    for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kBlock) {
+        const int64_t q = i / W;
+        const int64_t d = i - q * W;
+        if (d < D) {
+            outs[q * D + d] = recv[i];
+        } else if (d == D) {
+            lses[q] = __uint_as_float(uint32_t(recv[i]) | (uint32_t(recv[i + 1]) << 16));
+        }
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+constexpr float kLog2E = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+
+unsigned general_grid(int64_t total) {
+    int64_t blocks = (total + kBlock - 1) / kBlock;
+    const int64_t cap = int64_t(1) << 20;  // grid-stride beyond this
+    return unsigned(blocks < 1 ? 1 : (blocks > cap ? cap : blocks));
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? LSEC_OK : LSEC_ERR_LAUNCH; }
+
+bool fast_d(int64_t D) { return D % 8 == 0 && D <= kFastMaxD; }
+
+template <int DT, int NT, bool PACKED>
+void launch_combine_rows(const uint16_t* src, const float* lse, int N, uint32_t rows, int D,
+                         float scale, float inv_scale, uint16_t* out, float* out_lse,
+                         hipStream_t st) {
+    const uint32_t g = uint32_t(D / 8);
+    const uint32_t rpb = kBlock / g;
+    const unsigned blocks = (rows + rpb - 1) / rpb;
+    const int64_t stride = PACKED ? D + 2 : D;
+    combine_rows_kernel<DT, NT, PACKED><<<blocks, kBlock, 0, st>>>(
+        src, lse, N, rows, make_fastdiv(g), rpb, stride, int64_t(rows) * stride, D, scale,
+        inv_scale, out, out_lse);
+}
+
+template <int DT, bool PACKED>
+void dispatch_n(const uint16_t* src, const float* lse, int N, uint32_t rows, int D, float scale,
+                float inv_scale, uint16_t* out, float* out_lse, hipStream_t st) {
+    switch (N) {
+        case 1: launch_combine_rows<DT, 1, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
+        case 2: launch_combine_rows<DT, 2, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
+        case 4: launch_combine_rows<DT, 4, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
+        case 8: launch_combine_rows<DT, 8, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
+        case 16: launch_combine_rows<DT, 16, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
+        default: launch_combine_rows<DT, 0, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
+    }
+}
+
+template <bool PACKED>
+int run_combine(const uint16_t* src, const float* lse, int64_t N, int64_t rows, int64_t D,
+                int dtype, int base, uint16_t* out, float* out_lse, bool fast, hipStream_t st) {
+    const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
+    const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
+    (void)hipGetLastError();
+    if (fast) {
+        if (dtype == LSEC_BF16)
+            dispatch_n<LSEC_BF16, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale,
+                                          inv_scale, out, out_lse, st);
+        else
+            dispatch_n<LSEC_FP16, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale,
+                                          inv_scale, out, out_lse, st);
+    } else {
+        const int64_t stride = PACKED ? D + 2 : D;
+        const unsigned blocks = general_grid(rows * D);
+        if (dtype == LSEC_BF16)
+            combine_elems_kernel<LSEC_BF16, PACKED><<<blocks, kBlock, 0, st>>>(
+                src, lse, int(N), rows, stride, rows * stride, D, scale, inv_scale, out, out_lse);
+        else
+            combine_elems_kernel<LSEC_FP16, PACKED><<<blocks, kBlock, 0, st>>>(
+                src, lse, int(N), rows, stride, rows * stride, D, scale, inv_scale, out, out_lse);
+    }
+    return launch_status();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI
+
+extern "C" {
+
+int lsec_version(void) { return 100; }
+
+int lsec_pack_dim(int dtype) {
+    return (dtype == LSEC_BF16 || dtype == LSEC_FP16) ? 2 : -1;
+}
+
+const char* lsec_status_string(int status) {
+    switch (status) {
+        case LSEC_OK: return "ok";
+        case LSEC_ERR_NULL: return "a required pointer is NULL";
+        case LSEC_ERR_SHAPE: return "invalid shape (need N >= 1, B >= 0, H >= 1, D >= 1, sizes within int64)";
+        case LSEC_ERR_DIVISIBILITY: return "H must be divisible by N";
+        case LSEC_ERR_DTYPE: return "unsupported dtype (bf16 or fp16 only)";
+        case LSEC_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
+        case LSEC_ERR_BASE: return "base must be LSEC_BASE_E or LSEC_BASE_2";
+        case LSEC_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
+                 int64_t D, int dtype, int base, void* out, float* out_lse, void* stream) {
+    if (N < 1 || B < 0 || H < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
+    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
+    int64_t rows, rd, all;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, N, &all) ||
+        !mul_ok(all, 2, &all))
+        return LSEC_ERR_SHAPE;
+    if (rows == 0) return LSEC_OK;
+    if (!outputs || !lses || !out) return LSEC_ERR_NULL;
+    if (!aligned(outputs, 2) || !aligned(out, 2) || !aligned(lses, 4) ||
+        (out_lse && !aligned(out_lse, 4)))
+        return LSEC_ERR_ALIGNMENT;
+    const bool fast = fast_d(D) && rows < (int64_t(1) << 31) && aligned(outputs, 16) &&
+                      aligned(out, 16);
+    return run_combine<false>(static_cast<const uint16_t*>(outputs), lses, N, rows, D, dtype,
+                              base, static_cast<uint16_t*>(out), out_lse, fast,
+                              static_cast<hipStream_t>(stream));
+}
+
+int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,
+                        int base, void* out, float* out_lse, void* stream) {
+    if (N < 1 || B < 0 || Hl < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
+    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
+    int64_t rows, rw, all;
+    if (!mul_ok(B, Hl, &rows) || !mul_ok(rows, D + 2, &rw) || !mul_ok(rw, N, &all) ||
+        !mul_ok(all, 2, &all))
+        return LSEC_ERR_SHAPE;
+    if (rows == 0) return LSEC_OK;
+    if (!recv || !out) return LSEC_ERR_NULL;
+    if (!aligned(recv, 2) || !aligned(out, 2) || (out_lse && !aligned(out_lse, 4)))
+        return LSEC_ERR_ALIGNMENT;
+    const bool fast = fast_d(D) && rows < (int64_t(1) << 31) && aligned(recv, 4) &&
+                      aligned(out, 16);
+    return run_combine<true>(static_cast<const uint16_t*>(recv), nullptr, N, rows, D, dtype, base,
+                             static_cast<uint16_t*>(out), out_lse, fast,
+                             static_cast<hipStream_t>(stream));
+}
+
+int lsec_pack_send(const void* attn_out, const float* attn_lse, int64_t N, int64_t B, int64_t H,
+                   int64_t D, int dtype, void* send, void* stream) {
+    if (N < 1 || B < 0 || H < 1 || D < 1) return LSEC_ERR_SHAPE;
+    if (H % N != 0) return LSEC_ERR_DIVISIBILITY;
+    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    int64_t rows, total, bytes;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D + 2, &total) || !mul_ok(total, 2, &bytes))
+        return LSEC_ERR_SHAPE;
+    if (rows == 0) return LSEC_OK;
+    if (!attn_out || !attn_lse || !send) return LSEC_ERR_NULL;
+    if (!aligned(attn_out, 2) || !aligned(send, 2) || !aligned(attn_lse, 4))
+        return LSEC_ERR_ALIGNMENT;
+    const int64_t Hl = H / N;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const auto* in = static_cast<const uint16_t*>(attn_out);
+    auto* dst = static_cast<uint16_t*>(send);
+    (void)hipGetLastError();
+    const bool fast = fast_d(D) && rows < (int64_t(1) << 31) && aligned(attn_out, 16) &&
+                      aligned(send, 4);
+    if (fast) {
+        const uint32_t g = uint32_t(D / 8);
+        const uint32_t rpb = kBlock / g;
+        const unsigned blocks = unsigned((rows + rpb - 1) / rpb);
+        pack_rows_kernel<<<blocks, kBlock, 0, st>>>(in, attn_lse, uint32_t(rows), make_fastdiv(g),
+                                                    rpb, make_fastdiv(uint32_t(Hl)),
+                                                    make_fastdiv(uint32_t(B)), uint32_t(H),
+                                                    int(D), dst);
+    } else {
+        pack_elems_kernel<<<general_grid(total), kBlock, 0, st>>>(in, attn_lse, B, H, Hl, D,
+                                                                   total, dst);
+    }
+    return launch_status();
+}
+
+int lsec_unpack(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,
+                void* outputs, float* lses, void* stream) {
+    if (N < 1 || B < 0 || Hl < 1 || D < 1) return LSEC_ERR_SHAPE;
+    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    int64_t rows, total_rows, total, bytes;
+    if (!mul_ok(B, Hl, &rows) || !mul_ok(rows, N, &total_rows) ||
+        !mul_ok(total_rows, D + 2, &total) || !mul_ok(total, 2, &bytes))
+        return LSEC_ERR_SHAPE;
+    if (total_rows == 0) return LSEC_OK;
+    if (!recv || !outputs || !lses) return LSEC_ERR_NULL;
+    if (!aligned(recv, 2) || !aligned(outputs, 2) || !aligned(lses, 4)) return LSEC_ERR_ALIGNMENT;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const auto* src = static_cast<const uint16_t*>(recv);
+    auto* outs = static_cast<uint16_t*>(outputs);
+    (void)hipGetLastError();
+    const bool fast = fast_d(D) && total_rows < (int64_t(1) << 31) && aligned(recv, 4) &&
+                      aligned(outputs, 16);
+    if (fast) {
+        const uint32_t g = uint32_t(D / 8);
+        const uint32_t rpb = kBlock / g;
+        const unsigned blocks = unsigned((total_rows + rpb - 1) / rpb);
+        unpack_rows_kernel<<<blocks, kBlock, 0, st>>>(src, uint32_t(total_rows), make_fastdiv(g),
+                                                      rpb, int(D), outs, lses);
+    } else {
+        unpack_elems_kernel<<<general_grid(total), kBlock, 0, st>>>(src, total_rows, D, outs,
+                                                                     lses);
+    }
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function ``include/lsec.h`` declares, and
+reject bad arguments with the documented status before touching the GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsec.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import lse_weighted_merge_combine_amd as lsec
+    if not os.path.exists(lsec.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return lsec.load_library()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsec_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for n in ("lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
+              "lsec_pack_dim", "lsec_status_string", "lsec_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} declared in lsec.h but not exported"
+
+
+def test_constants_match_header(lib):
+    import lse_weighted_merge_combine_amd as lsec
+    src = open(HEADER).read()
+    for name in ("LSEC_OK", "LSEC_ERR_NULL", "LSEC_ERR_SHAPE", "LSEC_ERR_DIVISIBILITY",
+                 "LSEC_ERR_DTYPE", "LSEC_ERR_ALIGNMENT", "LSEC_ERR_BASE", "LSEC_ERR_LAUNCH",
+                 "LSEC_BF16", "LSEC_FP16", "LSEC_BASE_E", "LSEC_BASE_2"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
+        assert m and int(m.group(1)) == getattr(lsec, name), name
+
+
+def test_pack_dim_and_strings(lib):
+    assert lib.lsec_pack_dim(0) == 2 and lib.lsec_pack_dim(1) == 2 and lib.lsec_pack_dim(7) == -1
+    assert lib.lsec_version() >= 100
+    for s in range(0, 9):
+        assert lib.lsec_status_string(s)
+
+
+FAKE = 0x100000  # a 16-byte aligned non-null address; never dereferenced (calls fail validation)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((FAKE, FAKE, 0, 1, 1, 8, 0, 0, FAKE, None, None), 2),      # N < 1
+    ((FAKE, FAKE, 2, -1, 1, 8, 0, 0, FAKE, None, None), 2),     # B < 0
+    ((FAKE, FAKE, 2, 1, 0, 8, 0, 0, FAKE, None, None), 2),      # H < 1
+    ((FAKE, FAKE, 2, 1, 1, 0, 0, 0, FAKE, None, None), 2),      # D < 1
+    ((FAKE, FAKE, 2, 1 << 40, 1 << 20, 1 << 10, 0, 0, FAKE, None, None), 2),  # overflow
+    ((FAKE, FAKE, 2, 1, 1, 8, 5, 0, FAKE, None, None), 4),      # dtype
+    ((FAKE, FAKE, 2, 1, 1, 8, 0, 3, FAKE, None, None), 6),      # base
+    ((None, FAKE, 2, 1, 1, 8, 0, 0, FAKE, None, None), 1),      # NULL outputs
+    ((FAKE, None, 2, 1, 1, 8, 0, 0, FAKE, None, None), 1),      # NULL lses
+    ((FAKE, FAKE, 2, 1, 1, 8, 0, 0, None, None, None), 1),      # NULL out
+    ((FAKE + 1, FAKE, 2, 1, 1, 8, 0, 0, FAKE, None, None), 5),  # odd address
+    ((FAKE, FAKE + 2, 2, 1, 1, 8, 0, 0, FAKE, None, None), 5),  # lse not 4-aligned
+    ((FAKE, FAKE, 2, 1, 1, 8, 0, 0, FAKE, FAKE + 2, None), 5),  # out_lse not 4-aligned
+    ((None, None, 2, 0, 1, 8, 0, 0, None, None, None), 0),      # empty: nothing to do
+])
+def test_combine_validation(lib, args, want):
+    assert lib.lsec_combine(*args) == want
+
+
+def test_pack_send_validation(lib):
+    f = lib.lsec_pack_send
+    assert f(FAKE, FAKE, 3, 2, 8, 16, 0, FAKE, None) == 3   # 8 % 3 != 0
+    assert f(FAKE, FAKE, 0, 2, 8, 16, 0, FAKE, None) == 2
+    assert f(FAKE, FAKE, 2, 2, 8, 16, 9, FAKE, None) == 4
+    assert f(None, FAKE, 2, 2, 8, 16, 0, FAKE, None) == 1
+    assert f(FAKE, FAKE, 2, 2, 8, 16, 0, FAKE + 1, None) == 5
+    assert f(None, None, 2, 0, 8, 16, 0, None, None) == 0
+
+
+def test_unpack_validation(lib):
+    uc = lib.lsec_unpack_combine
+    assert uc(FAKE, 0, 2, 2, 16, 0, 0, FAKE, None, None) == 2
+    assert uc(FAKE, 2, 2, 2, 16, 2, 0, FAKE, None, None) == 4
+    assert uc(FAKE, 2, 2, 2, 16, 0, 9, FAKE, None, None) == 6
+    assert uc(None, 2, 2, 2, 16, 0, 0, FAKE, None, None) == 1
+    assert uc(FAKE, 2, 2, 2, 16, 0, 0, FAKE, FAKE + 2, None) == 5
+    u = lib.lsec_unpack
+    assert u(FAKE, 2, 2, 0, 16, 0, FAKE, FAKE, None) == 2
+    assert u(FAKE, 2, 2, 2, 16, 0, FAKE, None, None) == 1
+    assert u(FAKE, 2, 2, 2, 16, 0, FAKE, FAKE + 2, None) == 5
+    assert u(None, 2, 0, 2, 16, 0, None, None, None) == 0
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    import lse_weighted_merge_combine_amd as lsec
+    with pytest.raises(ValueError):
+        lsec.lsec_combine(torch.zeros(2, 1, 1, 8, dtype=torch.bfloat16),
+                          torch.zeros(2, 1, 1), base_e=True)  # CPU tensors
+    with pytest.raises(ValueError):
+        lsec.lsec_combine(torch.zeros(2, 1, 8, dtype=torch.bfloat16), torch.zeros(2, 1))
+    with pytest.raises(ValueError):
+        lsec.lsec_pack_dim(torch.float32)
+    with pytest.raises(ValueError):
+        lsec.lsec_pack_send(torch.zeros(1, 6, 8, dtype=torch.float16), torch.zeros(1, 6), 4)

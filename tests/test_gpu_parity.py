@@ -1,0 +1,349 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Inputs come from the seeded generator; expected values come from the oracle
+only. Combined outputs are compared within the tolerances in gpu_helpers;
+pack / unpack are compared bit for bit.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (assert_lse_close, assert_output_close, bits_of, f32_bits_of, f32_to_dev,
+                         max_abs_input, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def lsec():
+    import lse_weighted_merge_combine_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    m.load_library()
+    return m
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def test_native_library_loaded(lsec):
+    maps = open("/proc/self/maps").read()
+    assert "liblsec.so" in maps
+    assert torch.cuda.is_available()
+
+
+# ---------------------------------------------------------------- workloads at full size
+
+@pytest.mark.parametrize("name", ["small", "fp16_base2", "mla_decode"])
+@pytest.mark.parametrize("return_lse", [False, True])
+def test_workload_full(lsec, name, return_lse):
+    w = synth.WORKLOADS[name]
+    _announce(f"{name} full N={w.N} B={w.B} H={w.H} D={w.D} return_lse={return_lse}")
+    o, l = synth.combine_inputs(w)
+    res = lsec.lsec_combine(to_dev(o, w.dtype, DEV), f32_to_dev(l, DEV), base_e=not w.base2,
+                            return_lse=return_lse)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.lse_combine(o, l, w.dtype, base2=w.base2)
+    M = max_abs_input(o, w.dtype)
+    if return_lse:
+        y, L = res
+        assert_lse_close(L, L_ref, name)
+    else:
+        y = res
+    assert_output_close(y, y_ref, w.dtype, M, name)
+    if name == "small":  # the all -inf row gives 0 and -inf
+        b, h = w.allneg_row
+        assert torch.all(y[b, h] == 0)
+        if return_lse:
+            assert L[b, h].item() == float("-inf")
+
+
+def test_large_batch_full_size_sampled(lsec):
+    """N=16 B=16384 H=32 D=128 bf16, the launch the benchmark times; the oracle
+    checks sampled token ranges (rows are independent, so a slice of the
+    oracle's inputs gives exactly those rows' results)."""
+    w = synth.WORKLOADS["large_batch"]
+    _announce("large_batch full size, sampled rows")
+    o, l = synth.combine_inputs(w)
+    M = max_abs_input(o, w.dtype)
+    og, lg = to_dev(o, w.dtype, DEV), f32_to_dev(l, DEV)
+    del o, l
+    y, L = lsec.lsec_combine(og, lg, base_e=True, return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    starts = [0, w.B - 200] + sorted(rng.integers(200, w.B - 400, size=3).tolist())
+    for s in starts:
+        e = s + 200
+        os_, ls_ = synth.combine_inputs(w, b_lo=s, b_hi=e)
+        y_ref, L_ref = oracle.lse_combine(os_, ls_, w.dtype, base2=False)
+        assert_output_close(y[s:e], y_ref, w.dtype, M, f"tokens {s}:{e}")
+        assert_lse_close(L[s:e], L_ref, f"tokens {s}:{e}")
+    # every row: the global LSE is finite unless all 16 shard LSEs were non-finite
+    assert torch.isfinite(L).float().mean().item() > 0.999
+
+
+def _packed_ranks(w, b_lo=0, b_hi=None):
+    outs, lses = [], []
+    for r in range(w.N):
+        a, b = synth.rank_inputs(w, r, b_lo=b_lo, b_hi=b_hi)
+        outs.append(a)
+        lses.append(b)
+    return outs, lses
+
+
+def test_packed_workload_full(lsec):
+    """8 ranks x [2048,64,128] bf16: GPU pack on every rank (bit-exact with the
+    oracle), all-to-all stand-in, GPU unpack+combine on two receiving ranks."""
+    w = synth.WORKLOADS["packed"]
+    _announce("packed full: 8 ranks pack, exchange, unpack_combine")
+    outs, lses = _packed_ranks(w)
+    Hl = w.H // w.N
+    sends = []
+    for r in range(w.N):
+        s = lsec.lsec_pack_send(to_dev(outs[r], w.dtype, DEV), f32_to_dev(lses[r], DEV), w.N)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(s), oracle.pack_send(outs[r], lses[r], w.N)), f"rank {r}"
+        sends.append(s)
+    so, sl = np.stack(outs), np.stack(lses)
+    M = max_abs_input(so, w.dtype)
+    for p in (0, 5):
+        recv = torch.stack([sends[r][p] for r in range(w.N)]).contiguous()
+        y, L = lsec.lsec_unpack_combine(recv, base_e=True, return_lse=True)
+        uo, ul = lsec.lsec_unpack(recv)
+        torch.cuda.synchronize()
+        sl_h = slice(p * Hl, (p + 1) * Hl)
+        y_ref, L_ref = oracle.lse_combine(so[:, :, sl_h], sl[:, :, sl_h], w.dtype, base2=False)
+        assert_output_close(y, y_ref, w.dtype, M, f"recv rank {p}")
+        assert_lse_close(L, L_ref, f"recv rank {p}")
+        assert np.array_equal(bits_of(uo), np.ascontiguousarray(so[:, :, sl_h]))
+        assert np.array_equal(f32_bits_of(ul), np.ascontiguousarray(sl[:, :, sl_h]).view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype,base2", [("bf16", False), ("f16", True)])
+def test_receive_side_on_oracle_packed_buffer(lsec, dtype, base2):
+    """The receive kernels on a buffer the oracle packed and exchanged on the host."""
+    N, B, H, D = 4, 37, 12, 128
+    _announce(f"receive side on oracle buffer {dtype} N={N} B={B} H={H} D={D}")
+    outs, lses = [], []
+    for r in range(N):
+        a, b = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=300 + r,
+                                   special=((0.05, float("nan")), (0.05, float("inf")),
+                                            (0.05, float("-inf"))))
+        outs.append(a[0])
+        lses.append(b[0])
+    recvs = oracle.exchange([oracle.pack_send(outs[r], lses[r], N) for r in range(N)])
+    for p in (0, 3):
+        recv_h = recvs[p]
+        recv = to_dev(recv_h, dtype, DEV)
+        y, L = lsec.lsec_unpack_combine(recv, base_e=not base2, return_lse=True)
+        uo, ul = lsec.lsec_unpack(recv)
+        torch.cuda.synchronize()
+        y_ref, L_ref = oracle.unpack_combine(recv_h, D, dtype, base2)
+        oo, ol = oracle.unpack(recv_h, D)
+        assert_output_close(y, y_ref, dtype, max_abs_input(oo, dtype), f"rank {p}")
+        assert_lse_close(L, L_ref, f"rank {p}")
+        assert np.array_equal(bits_of(uo), oo)
+        assert np.array_equal(f32_bits_of(ul), ol.view(np.uint32))
+
+
+# ---------------------------------------------------------------- shapes and code paths
+
+SPECIALS = ((0.04, float("nan")), (0.04, float("inf")), (0.04, float("-inf")))
+
+SHAPES = [
+    # N, B, H, D, dtype, base2      (path exercised)
+    (16, 37, 5, 128, "bf16", False),  # templated N, ragged last block
+    (8, 29, 3, 512, "bf16", True),    # one wave per row
+    (4, 23, 6, 256, "f16", True),
+    (2, 31, 7, 64, "bf16", False),
+    (1, 50, 3, 512, "bf16", False),
+    (3, 11, 7, 128, "f16", True),     # runtime N
+    (5, 9, 4, 64, "bf16", True),
+    (7, 13, 3, 256, "bf16", False),
+    (32, 6, 4, 128, "bf16", False),
+    (9, 20, 2, 24, "bf16", True),     # 3 lanes per row, rows straddle waves
+    (2, 3, 3, 2048, "f16", False),    # 256 lanes per row
+    (4, 10, 3, 1000, "bf16", False),  # general path: D % 8 != 0
+    (3, 5, 2, 3, "f16", True),        # general path: tiny D
+    (2, 2, 2, 4096, "bf16", True),    # general path: D > 2048
+]
+
+
+@pytest.mark.parametrize("N,B,H,D,dtype,base2", SHAPES)
+def test_combine_shapes(lsec, N, B, H, D, dtype, base2):
+    _announce(f"combine N={N} B={B} H={H} D={D} {dtype} base2={base2}")
+    o, l = synth.custom_inputs(N, B, H, D, dtype=dtype, seed=N * 1000 + D, special=SPECIALS)
+    y, L = lsec.lsec_combine(to_dev(o, dtype, DEV), f32_to_dev(l, DEV), base_e=not base2,
+                             return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.lse_combine(o, l, dtype, base2)
+    assert_output_close(y, y_ref, dtype, max_abs_input(o, dtype))
+    assert_lse_close(L, L_ref)
+
+
+@pytest.mark.parametrize("N,B,H,D,dtype", [
+    (4, 9, 8, 128, "bf16"), (2, 7, 6, 64, "f16"), (8, 3, 16, 512, "bf16"),
+    (4, 5, 8, 6, "bf16"),    # general path: D % 8 != 0
+    (2, 5, 4, 5, "f16"),     # odd D: packed rows only 2-byte aligned
+    (3, 4, 9, 130, "bf16"),  # general path
+])
+def test_pack_unpack_shapes(lsec, N, B, H, D, dtype):
+    _announce(f"pack/unpack N={N} B={B} H={H} D={D} {dtype}")
+    o, l = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=77 + D, special=SPECIALS)
+    o, l = o[0], l[0]
+    lb = l.view(np.uint32)
+    lb[0, 0] = 0x7FC0BEEF  # NaN payload must survive
+    send = lsec.lsec_pack_send(to_dev(o, dtype, DEV), f32_to_dev(l, DEV), N)
+    torch.cuda.synchronize()
+    ref = oracle.pack_send(o, l, N)
+    assert np.array_equal(bits_of(send), ref)
+    uo, ul = lsec.lsec_unpack(to_dev(ref, dtype, DEV))
+    torch.cuda.synchronize()
+    oo, ol = oracle.unpack(ref, D)
+    assert np.array_equal(bits_of(uo), oo)
+    assert np.array_equal(f32_bits_of(ul), ol.view(np.uint32))
+    y, L = lsec.lsec_unpack_combine(to_dev(ref, dtype, DEV), base_e=True, return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.unpack_combine(ref, D, dtype, False)
+    assert_output_close(y, y_ref, dtype, max_abs_input(oo, dtype))
+    assert_lse_close(L, L_ref)
+
+
+def test_misaligned_buffers_take_general_path(lsec):
+    """Views that start 2 bytes into an allocation (only element-aligned)."""
+    N, B, H, D = 4, 6, 5, 128
+    _announce("misaligned views")
+    o, l = synth.custom_inputs(N, B, H, D, seed=5, special=SPECIALS)
+    flat = torch.empty(o.size + 1, dtype=torch.bfloat16, device=DEV)
+    og = flat[1:].view(N, B, H, D)
+    og.copy_(to_dev(o, "bf16", DEV))
+    outflat = torch.empty(B * H * D + 1, dtype=torch.bfloat16, device=DEV)
+    out = outflat[1:].view(B, H, D)
+    y = lsec.lsec_combine(og, f32_to_dev(l, DEV), out=out)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.lse_combine(o, l, "bf16")
+    assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
+    # packed: send buffer starting one element in (rows 2-byte aligned only)
+    a, b = synth.custom_inputs(1, 5, 8, 16, seed=6)
+    sflat = torch.empty(2 * 5 * 4 * 18 + 1, dtype=torch.bfloat16, device=DEV)
+    send = sflat[1:].view(2, 5, 4, 18)
+    lsec.lsec_pack_send(to_dev(a[0], "bf16", DEV), f32_to_dev(b[0], DEV), 2, send=send)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(send), oracle.pack_send(a[0], b[0], 2))
+    y2, L2 = lsec.lsec_unpack_combine(send, return_lse=True)
+    torch.cuda.synchronize()
+    y2r, L2r = oracle.unpack_combine(bits_of(send), 16, "bf16")
+    assert_output_close(y2, y2r, "bf16", max_abs_input(a[0], "bf16"))
+    assert_lse_close(L2, L2r)
+
+
+# ---------------------------------------------------------------- degenerate cases
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("base_e", [True, False])
+def test_single_shard_is_identity_bit_exact(lsec, dtype, base_e):
+    o, l = synth.custom_inputs(1, 33, 7, 128, dtype=dtype, seed=8)
+    y, L = lsec.lsec_combine(to_dev(o, dtype, DEV), f32_to_dev(l, DEV), base_e=base_e,
+                             return_lse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(y), o[0])
+    assert np.array_equal(f32_bits_of(L), l[0].view(np.uint32))
+
+
+def test_all_shards_non_finite(lsec):
+    N, B, H, D = 4, 5, 3, 128
+    o, _ = synth.custom_inputs(N, B, H, D, seed=9)
+    l = np.empty((N, B, H), dtype=np.float32)
+    l[0], l[1], l[2], l[3] = np.nan, np.inf, -np.inf, np.nan
+    for D_ in (128, 12):  # fast and general paths
+        oo = np.ascontiguousarray(o[..., :D_])
+        y, L = lsec.lsec_combine(to_dev(oo, "bf16", DEV), f32_to_dev(l, DEV), return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.all(y == 0)
+        assert torch.all(torch.isneginf(L))
+
+
+def test_nan_output_at_zero_weight_propagates(lsec):
+    """Every shard is multiplied, so a NaN output at weight 0 still gives NaN."""
+    N, B, H, D = 2, 2, 2, 128
+    o, l = synth.custom_inputs(N, B, H, D, seed=10)
+    o[0, 0, 0, 5] = 0x7FC0  # bf16 NaN
+    l[0, 0, 0] = -np.inf    # its shard has weight 0
+    y = lsec.lsec_combine(to_dev(o, "bf16", DEV), f32_to_dev(l, DEV))
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.lse_combine(o, l, "bf16")
+    assert np.isnan(y_ref[0, 0, 5])
+    assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
+
+
+def test_extreme_lse_values(lsec):
+    N, B, H, D = 4, 8, 4, 128
+    o, l = synth.custom_inputs(N, B, H, D, seed=11)
+    l[0] = 3e38
+    l[1] = -3e38
+    l[2, :4] = 1e30
+    l[3] = 0.0
+    for base_e in (True, False):
+        y, L = lsec.lsec_combine(to_dev(o, "bf16", DEV), f32_to_dev(l, DEV), base_e=base_e,
+                                 return_lse=True)
+        torch.cuda.synchronize()
+        y_ref, L_ref = oracle.lse_combine(o, l, "bf16", base2=not base_e)
+        assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
+        assert_lse_close(L, L_ref)
+
+
+def test_empty_batch(lsec):
+    og = torch.empty((4, 0, 8, 128), dtype=torch.bfloat16, device=DEV)
+    lg = torch.empty((4, 0, 8), dtype=torch.float32, device=DEV)
+    y, L = lsec.lsec_combine(og, lg, return_lse=True)
+    assert y.shape == (0, 8, 128) and L.shape == (0, 8)
+    s = lsec.lsec_pack_send(torch.empty((0, 8, 128), dtype=torch.float16, device=DEV),
+                            torch.empty((0, 8), device=DEV), 4)
+    assert s.shape == (4, 0, 2, 130)
+    y2 = lsec.lsec_unpack_combine(s)
+    assert y2.shape == (0, 2, 128)
+
+
+def test_errors_raise(lsec):
+    with pytest.raises(ValueError):
+        lsec.lsec_pack_send(torch.zeros(2, 6, 8, dtype=torch.bfloat16, device=DEV),
+                            torch.zeros(2, 6, device=DEV), 4)
+    with pytest.raises(ValueError):
+        lsec.lsec_combine(torch.zeros(2, 1, 1, 8, device=DEV), torch.zeros(2, 1, 1, device=DEV))
+    with pytest.raises(ValueError):
+        lsec.lsec_combine(torch.zeros(2, 1, 1, 8, dtype=torch.bfloat16, device=DEV),
+                          torch.zeros(2, 1, 1, dtype=torch.float64, device=DEV))
+
+
+def test_side_stream_and_preallocated_outputs(lsec):
+    N, B, H, D = 8, 64, 8, 128
+    o, l = synth.custom_inputs(N, B, H, D, seed=12, special=SPECIALS)
+    og, lg = to_dev(o, "bf16", DEV), f32_to_dev(l, DEV)
+    out = torch.full((B, H, D), 7.0, dtype=torch.bfloat16, device=DEV)
+    out_lse = torch.full((B, H), 7.0, device=DEV)
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lsec.lsec_combine(og, lg, return_lse=True, out=out, out_lse=out_lse)
+    s.synchronize()
+    y_ref, L_ref = oracle.lse_combine(o, l, "bf16")
+    assert_output_close(out, y_ref, "bf16", max_abs_input(o, "bf16"))
+    assert_lse_close(out_lse, L_ref)
+
+
+def test_page_signature_alias(lsec):
+    o, l = synth.custom_inputs(3, 4, 4, 64, seed=13)
+    y, L = lsec.lse_weighted_combine(to_dev(o, "bf16", DEV), f32_to_dev(l, DEV), return_lse=True,
+                                     is_lse_base_on_e=False)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.lse_combine(o, l, "bf16", base2=True)
+    assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
+    assert_lse_close(L, L_ref)
