@@ -103,7 +103,7 @@ def build_workload(name: str, dev):
         out = torch.empty((w.B, w.H, w.D), dtype=tdt, device=dev)
         out_lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev) if w.return_lse else None
         nbytes = combine_bytes(w.N, w.B, w.H, w.D, 2, w.return_lse)
-        kname = f"combine_rows_kernel<{w.dtype},N={w.N}>"
+        kname = f"{lsec.lsec_combine_path(w.N, w.B, w.H, w.D)} ({w.dtype}, N={w.N}, D={w.D})"
 
         def step():
             lsec.lsec_combine(og, lg, base_e=not w.base2, return_lse=w.return_lse, out=out,
@@ -136,7 +136,8 @@ def build_workload(name: str, dev):
                                      out_lse=out_lse)
 
         kernels = [("pack_rows_kernel", pack_bytes(w.N, w.B, w.H, w.D), pack),
-                   (f"combine_rows_kernel<{w.dtype},N={w.N},packed>",
+                   (f"{lsec.lsec_combine_path(w.N, w.B, Hl, w.D, packed=True)} "
+                    f"({w.dtype}, N={w.N}, D={w.D}, packed rows)",
                     unpack_combine_bytes(w.N, w.B, Hl, w.D, 2, True), unpack_combine)]
         host = None
         rows = w.B * Hl

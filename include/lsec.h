@@ -121,6 +121,18 @@ int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int6
 int lsec_unpack(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,
                 void* outputs, float* lses, void* stream);
 
+/*
+ * lsec_combine_path -- diagnostics: the name of the kernel lsec_combine
+ * (packed == 0, H = heads) or lsec_unpack_combine (packed != 0, H = heads per
+ * rank, Hl) launches for these sizes, given whether the buffers meet the fast
+ * alignment (aligned_buffers != 0: 16 bytes for outputs / out, 4 bytes for
+ * recv). Returns a static string such as "combine_tiled_kernel S=16",
+ * "combine_rows_kernel" or "combine_elems_kernel"; "none" when the sizes
+ * launch nothing or are invalid. Touches no GPU state.
+ */
+const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int packed,
+                              int aligned_buffers);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* lsec_status_string(int status);
 

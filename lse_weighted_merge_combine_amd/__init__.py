@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_unpack_combine.argtypes = [P, I64, I64, I64, I64, I, I, P, P, P]
     lib.lsec_unpack.restype = I
     lib.lsec_unpack.argtypes = [P, I64, I64, I64, I64, I, P, P, P]
+    lib.lsec_combine_path.restype = ctypes.c_char_p
+    lib.lsec_combine_path.argtypes = [I64, I64, I64, I64, I, I]
     _lib = lib
     return lib
 
@@ -240,6 +242,12 @@ def lsec_unpack(recv: torch.Tensor, outputs: torch.Tensor | None = None,
     return outputs, lses
 
 
+def lsec_combine_path(N: int, B: int, H: int, D: int, packed: bool = False,
+                      aligned: bool = True) -> str:
+    """Name of the kernel a combine of these sizes launches (diagnostics)."""
+    return load_library().lsec_combine_path(N, B, H, D, int(packed), int(aligned)).decode()
+
+
 def lse_weighted_combine(outputs: torch.Tensor, lses: torch.Tensor, return_lse: bool = False,
                          is_lse_base_on_e: bool = True):
     """The page's ``_lse_weighted_combine(outputs, lses, return_lse, is_lse_base_on_e)``,
@@ -256,5 +264,5 @@ def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
 
 __all__ = [
     "lsec_pack_dim", "lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
-    "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
+    "lsec_combine_path", "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
 ]

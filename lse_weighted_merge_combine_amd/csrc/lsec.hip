@@ -247,6 +247,138 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     if (out_lse != nullptr && lane == 0) out_lse[row] = global_lse(s, m, inv_scale);
 }
 
+// ---------------------------------------------------------------- combine (tiled path)
+//
+// For D in {128, 256, 512} and N in {2, 4, 8, 16}. A row is owned by G = D/8
+// lanes (16 bytes each). A block of 256 threads covers S slots of 256/G
+// consecutive rows, so per plane it reads one contiguous run of S*256/G rows
+// (32 KB at S = 8). The planes are walked in order, PG at a time: each lane has
+// PG*S 16-byte loads in flight and a block keeps few DRAM pages open. On
+// MI355X this streams markedly faster than issuing all N planes of one row at
+// once, which spreads every block over N distant pages.
+//
+// Weights: lane j of each 16-lane DPP row loads shard j's LSE for its row
+// (j < N; the 16-lane segments of a row group hold identical copies). Max and
+// sum are 16-lane DPP reductions; during the sweep the weight of plane n comes
+// from lane n of the segment (a lane shuffle, or readlane when one wave is one
+// row). The global LSE is written before the sweep so nothing but the weights
+// stays live through it.
+//
+// Addresses: plane n starts at n * plane_bytes (uniform, scalar registers);
+// a lane's chunk sits at a 32-bit byte offset inside the plane. The host
+// checks plane_bytes < 2^32. Rows past the end of the last block are clamped
+// to the last row for loading and are not stored.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
+// Reductions over the 16 lanes of each DPP row (every lane gets the result).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
+    v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
+    v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm:[2,3,0,1]
+    v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm:[1,0,3,2]
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0x128>(v);
+    v += dpp_mov<0x124>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0xB1>(v);
+    return v;
+}
+
+// Value held by lane n of this lane's 16-lane segment (n uniform).
+template <int G>
+__device__ __forceinline__ float lane_value(float v, int n) {
+    if constexpr (G == 64)
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), n));
+    else
+        return __shfl(v, n, 16);
+}
+
+__device__ __forceinline__ u32x4 ld16_nt_at(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16_a4_at(const char* p) {
+    return ld16_a4(reinterpret_cast<const uint16_t*>(p));
+}
+
+template <int S, int NT>
+constexpr int tiled_pg() {
+    return (S >= 4 ? 1 : (8 / S < NT ? 8 / S : NT));
+}
+
+template <int DT, int NT, int G, int S, bool PACKED>
+__global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
+    const uint16_t* src, const float* __restrict__ lse, uint32_t rows, uint32_t stride,
+    uint64_t plane_bytes, float scale, float inv_scale, uint16_t* __restrict__ out,
+    float* __restrict__ out_lse) {
+    constexpr int RPS = kBlock / G;  // rows per slot
+    constexpr int D = G * 8;
+    constexpr int PG = tiled_pg<S, NT>();
+    static_assert(NT % PG == 0, "plane groups must tile N");
+    const uint32_t t = threadIdx.x;
+    const uint32_t rib = t / G;
+    const uint32_t lane = t % G;
+    const uint32_t j = t & 15u;
+    const uint32_t row0 = blockIdx.x * (RPS * S);
+    const char* base = reinterpret_cast<const char*>(src);
+
+    uint32_t row[S], off[S];
+    float lw[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        row[s] = row0 + s * RPS + rib;
+        const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
+        off[s] = (rc * stride + lane * 8) * 2;
+        float l = -__builtin_inff();
+        if (j < NT) {
+            if (PACKED)
+                l = *reinterpret_cast<const float*>(base + j * plane_bytes + (rc * stride + D) * 2);
+            else
+                l = lse[j * rows + rc];
+        }
+        lw[s] = l;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float l = j < NT ? sanitize(lw[s]) : -__builtin_inff();
+        float m = row16_max(l);
+        if (m == -__builtin_inff()) m = 0.0f;
+        const float w = j < NT ? weight(l - m, scale) : 0.0f;
+        const float sum = row16_sum(w);
+        lw[s] = w * (1.0f / fmaxf(sum, 1e-10f));
+        if (out_lse != nullptr && lane == 0 && row[s] < rows) out_lse[row[s]] = global_lse(sum, m, inv_scale);
+    }
+
+    float acc[S][8];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[s][k] = 0.0f;
+#pragma unroll 1
+    for (int n0 = 0; n0 < NT; n0 += PG) {
+        u32x4 v[PG][S];
+#pragma unroll
+        for (int p = 0; p < PG; ++p) {
+            const char* pb = base + uint64_t(n0 + p) * plane_bytes;
+#pragma unroll
+            for (int s = 0; s < S; ++s) v[p][s] = PACKED ? ld16_a4_at(pb + off[s]) : ld16_nt_at(pb + off[s]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all PG*S loads issued before the first is used
+#pragma unroll
+        for (int p = 0; p < PG; ++p)
+#pragma unroll
+            for (int s = 0; s < S; ++s) fma8<DT>(v[p][s], lane_value<G>(lw[s], n0 + p), acc[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        if (row[s] < rows) st16(out + uint64_t(row[s]) * D + lane * 8, enc8<DT>(acc[s]));
+}
+
 // ---------------------------------------------------------------- combine (general path)
 //
 // Any D, 2-byte aligned buffers. One thread per (row, element); each thread
@@ -411,13 +543,97 @@ void dispatch_n(const uint16_t* src, const float* lse, int N, uint32_t rows, int
     }
 }
 
+// Tiled path: the largest S in {16, 8, 4, 2, 1} that still gives every CU at
+// least 8 blocks (small inputs fall back to S = 1 with more planes in flight).
+// Measured on MI355X: S = 16 (64 KB runs per plane, one wave per SIMD) is the
+// fastest for 128-wide rows at 2 GB per call; S = 4..8 for 512-wide rows.
+constexpr unsigned kTiledMinBlocks = 2048;
+
+template <int DT, int NT, int G, bool PACKED>
+void launch_tiled_s(int S, const uint16_t* src, const float* lse, uint32_t rows, uint32_t stride,
+                    uint64_t plane_bytes, float scale, float inv_scale, uint16_t* out,
+                    float* out_lse, hipStream_t st) {
+    constexpr uint32_t RPS = kBlock / G;
+    const unsigned blocks = (rows + RPS * S - 1) / (RPS * S);
+#define LSEC_TILED(SV)                                                                         \
+    combine_tiled_kernel<DT, NT, G, SV, PACKED><<<blocks, kBlock, 0, st>>>(                    \
+        src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse)
+    switch (S) {
+        case 16: LSEC_TILED(16); break;
+        case 8: LSEC_TILED(8); break;
+        case 4: LSEC_TILED(4); break;
+        case 2: LSEC_TILED(2); break;
+        default: LSEC_TILED(1); break;
+    }
+#undef LSEC_TILED
+}
+
+template <int DT, int G, bool PACKED>
+void launch_tiled_n(int N, int S, const uint16_t* src, const float* lse, uint32_t rows,
+                    uint32_t stride, uint64_t plane_bytes, float scale, float inv_scale,
+                    uint16_t* out, float* out_lse, hipStream_t st) {
+    switch (N) {
+        case 2: launch_tiled_s<DT, 2, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+        case 4: launch_tiled_s<DT, 4, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+        case 8: launch_tiled_s<DT, 8, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+        default: launch_tiled_s<DT, 16, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+    }
+}
+
+template <int DT, bool PACKED>
+void launch_tiled(int N, int S, uint32_t rows, int D, const uint16_t* src, const float* lse,
+                  float scale, float inv_scale, uint16_t* out, float* out_lse, hipStream_t st) {
+    const uint32_t stride = uint32_t(PACKED ? D + 2 : D);
+    const uint64_t plane_bytes = uint64_t(rows) * stride * 2;
+    switch (D) {
+        case 128: launch_tiled_n<DT, 16, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+        case 256: launch_tiled_n<DT, 32, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+        default: launch_tiled_n<DT, 64, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+    }
+}
+
+// Which combine kernel serves a call. `fast` = D % 8 == 0, D <= 2048,
+// rows < 2^31 and the buffers meet the 16-byte (separate) or 4-byte (packed)
+// alignment; otherwise the element-wise kernel runs.
+enum { kPathTiled = 0, kPathRows = 1, kPathElems = 2 };
+struct CombinePlan {
+    int kind;
+    int S;  // row slots per lane (tiled path)
+};
+
+CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, bool packed, bool fast) {
+    if (!fast) return {kPathElems, 0};
+    const bool tiled_shape = (D == 128 || D == 256 || D == 512) &&
+                             (N == 2 || N == 4 || N == 8 || N == 16);
+    if (tiled_shape) {
+        const uint64_t plane_bytes = uint64_t(rows) * uint64_t(packed ? D + 2 : D) * 2;
+        const bool fits32 = plane_bytes < (uint64_t(1) << 32) &&
+                            (packed || uint64_t(N) * uint64_t(rows) < (uint64_t(1) << 32));
+        if (fits32) {
+            const uint64_t rps = kBlock / uint64_t(D / 8);
+            int S = 16;
+            while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < kTiledMinBlocks) S /= 2;
+            return {kPathTiled, S};
+        }
+    }
+    return {kPathRows, 0};
+}
+
 template <bool PACKED>
 int run_combine(const uint16_t* src, const float* lse, int64_t N, int64_t rows, int64_t D,
                 int dtype, int base, uint16_t* out, float* out_lse, bool fast, hipStream_t st) {
     const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
     const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
+    const CombinePlan plan = plan_combine(N, rows, D, PACKED, fast);
     (void)hipGetLastError();
-    if (fast) {
+    if (plan.kind == kPathTiled) {
+        if (dtype == LSEC_BF16)
+            launch_tiled<LSEC_BF16, PACKED>(int(N), plan.S, uint32_t(rows), int(D), src, lse,
+                                            scale, inv_scale, out, out_lse, st);
+        else
+            launch_tiled<LSEC_FP16, PACKED>(int(N), plan.S, uint32_t(rows), int(D), src, lse,
+                                            scale, inv_scale, out, out_lse, st);
+    } else if (plan.kind == kPathRows) {
         if (dtype == LSEC_BF16)
             dispatch_n<LSEC_BF16, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale,
                                           inv_scale, out, out_lse, st);
@@ -460,6 +676,23 @@ const char* lsec_status_string(int status) {
         case LSEC_ERR_BASE: return "base must be LSEC_BASE_E or LSEC_BASE_2";
         case LSEC_ERR_LAUNCH: return "kernel launch failed";
         default: return "unknown status";
+    }
+}
+
+const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int packed,
+                              int aligned_buffers) {
+    int64_t rows;
+    if (N < 1 || B < 1 || H < 1 || D < 1 || !mul_ok(B, H, &rows)) return "none";
+    const bool fast = aligned_buffers && fast_d(D) && rows < (int64_t(1) << 31);
+    const CombinePlan plan = plan_combine(N, rows, D, packed != 0, fast);
+    if (plan.kind == kPathElems) return "combine_elems_kernel";
+    if (plan.kind == kPathRows) return "combine_rows_kernel";
+    switch (plan.S) {
+        case 16: return "combine_tiled_kernel S=16";
+        case 8: return "combine_tiled_kernel S=8";
+        case 4: return "combine_tiled_kernel S=4";
+        case 2: return "combine_tiled_kernel S=2";
+        default: return "combine_tiled_kernel S=1";
     }
 }
 

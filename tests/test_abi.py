@@ -116,3 +116,20 @@ def test_python_binding_rejects_bad_tensors():
         lsec.lsec_pack_dim(torch.float32)
     with pytest.raises(ValueError):
         lsec.lsec_pack_send(torch.zeros(1, 6, 8, dtype=torch.float16), torch.zeros(1, 6), 4)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((16, 16384, 32, 128, 0, 1), "combine_tiled_kernel S=16"),
+    ((8, 4096, 16, 512, 0, 1), "combine_tiled_kernel S=8"),
+    ((4, 256, 32, 128, 0, 1), "combine_tiled_kernel S=1"),
+    ((8, 2048, 8, 128, 1, 1), "combine_tiled_kernel S=1"),
+    ((16, 16384, 32, 128, 0, 0), "combine_elems_kernel"),   # buffers not 16-byte aligned
+    ((1, 50, 3, 512, 0, 1), "combine_rows_kernel"),          # N = 1
+    ((32, 6, 4, 128, 0, 1), "combine_rows_kernel"),          # N outside {2, 4, 8, 16}
+    ((4, 10, 3, 64, 0, 1), "combine_rows_kernel"),           # D outside {128, 256, 512}
+    ((3, 5, 2, 3, 0, 1), "combine_elems_kernel"),            # D % 8 != 0
+    ((2, 2, 2, 4096, 0, 1), "combine_elems_kernel"),         # D > 2048
+    ((4, 0, 8, 128, 0, 1), "none"),
+])
+def test_combine_path(lib, args, want):
+    assert lib.lsec_combine_path(*args).decode() == want

@@ -189,6 +189,60 @@ def test_combine_shapes(lsec, N, B, H, D, dtype, base2):
     assert_lse_close(L, L_ref)
 
 
+# Large enough for the tiled kernel to pick 16, 8, 4, 2 and 1 row slots per
+# lane (the largest count that still gives 2048 blocks), each with a ragged
+# last block (rows not a multiple of the block's rows).
+TILED = [
+    # N, B, H, D, dtype, base2, slots   (rows)
+    (2, 16389, 32, 128, "bf16", False, 16),  # 524448 rows
+    (2, 8197, 32, 256, "f16", True, 16),     # 262304 rows, two rows per wave
+    (2, 2081, 63, 512, "bf16", True, 16),    # 131103 rows, one wave per row
+    (2, 9001, 33, 128, "bf16", True, 8),     # 297033 rows
+    (2, 8193, 17, 256, "bf16", False, 8),    # 139281 rows
+    (4, 4099, 32, 128, "bf16", False, 4),    # 131168 rows
+    (2, 2051, 17, 512, "f16", False, 4),     # 34867 rows
+    (8, 3125, 31, 128, "bf16", False, 2),    # 96875 rows
+    (8, 1250, 31, 128, "f16", True, 1),      # 38750 rows
+    (2, 1000, 3, 128, "bf16", True, 1),      # 3000 rows
+]
+
+
+@pytest.mark.parametrize("N,B,H,D,dtype,base2,slots", TILED)
+def test_tiled_slots_ragged(lsec, N, B, H, D, dtype, base2, slots):
+    _announce(f"tiled combine N={N} B={B} H={H} D={D} {dtype} base2={base2} S={slots}")
+    assert lsec.lsec_combine_path(N, B, H, D) == f"combine_tiled_kernel S={slots}"
+    o, l = synth.custom_inputs(N, B, H, D, dtype=dtype, seed=B + D, special=SPECIALS)
+    y, L = lsec.lsec_combine(to_dev(o, dtype, DEV), f32_to_dev(l, DEV), base_e=not base2,
+                             return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.lse_combine(o, l, dtype, base2)
+    assert_output_close(y, y_ref, dtype, max_abs_input(o, dtype))
+    assert_lse_close(L, L_ref)
+
+
+@pytest.mark.parametrize("N,B,H,D,dtype,slots", [
+    (4, 8193, 16, 128, "bf16", 1),   # 32772 rows of the packed layout, ragged
+    (8, 4099, 64, 128, "bf16", 1),   # 32792 rows
+    (2, 4097, 32, 512, "f16", 8),    # 65552 rows
+    (2, 16389, 64, 128, "bf16", 16),  # 524448 rows
+])
+def test_tiled_unpack_combine_ragged(lsec, N, B, H, D, dtype, slots):
+    _announce(f"tiled unpack_combine N={N} B={B} H={H} D={D} {dtype} S={slots}")
+    assert lsec.lsec_combine_path(N, B, H // N, D, packed=True) == f"combine_tiled_kernel S={slots}"
+    outs, lses = [], []
+    for r in range(N):
+        a, b = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=500 + r, special=SPECIALS)
+        outs.append(a[0])
+        lses.append(b[0])
+    recv_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N) for r in range(N)])[1]
+    y, L = lsec.lsec_unpack_combine(to_dev(recv_h, dtype, DEV), base_e=True, return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.unpack_combine(recv_h, D, dtype, False)
+    oo, _ = oracle.unpack(recv_h, D)
+    assert_output_close(y, y_ref, dtype, max_abs_input(oo, dtype))
+    assert_lse_close(L, L_ref)
+
+
 @pytest.mark.parametrize("N,B,H,D,dtype", [
     (4, 9, 8, 128, "bf16"), (2, 7, 6, 64, "f16"), (8, 3, 16, 512, "bf16"),
     (4, 5, 8, 6, "bf16"),    # general path: D % 8 != 0
