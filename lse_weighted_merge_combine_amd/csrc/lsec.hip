@@ -306,6 +306,21 @@ __device__ __forceinline__ u32x4 ld16_a4_at(const char* p) {
     return ld16_a4(reinterpret_cast<const uint16_t*>(p));
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i mod 8). Remap so that each XCD takes chunks of kXcdChunk consecutive
+// tiles: logical tile = (chunk * 8 + xcd) * kXcdChunk + index within chunk.
+// The remap is a permutation of [0, nblocks): the grid's tail that does not
+// fill a whole round of 8 chunks keeps the identity. Measured on MI355X: 4-8 %
+// more bandwidth for the streaming combine than plain round-robin order.
+constexpr uint32_t kXcdChunk = 16;
+
+__device__ __forceinline__ uint32_t xcd_chunked_block(uint32_t bid, uint32_t nblocks) {
+    const uint32_t full = nblocks / (8 * kXcdChunk) * (8 * kXcdChunk);
+    if (bid >= full) return bid;
+    const uint32_t xcd = bid % 8, i = bid / 8;
+    return ((i / kXcdChunk) * 8 + xcd) * kXcdChunk + i % kXcdChunk;
+}
+
 template <int S, int NT>
 constexpr int tiled_pg() {
     return (S >= 4 ? 1 : (8 / S < NT ? 8 / S : NT));
@@ -324,7 +339,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     const uint32_t rib = t / G;
     const uint32_t lane = t % G;
     const uint32_t j = t & 15u;
-    const uint32_t row0 = blockIdx.x * (RPS * S);
+    const uint32_t row0 = xcd_chunked_block(blockIdx.x, gridDim.x) * (RPS * S);
     const char* base = reinterpret_cast<const char*>(src);
 
     uint32_t row[S], off[S];
@@ -543,11 +558,15 @@ void dispatch_n(const uint16_t* src, const float* lse, int N, uint32_t rows, int
     }
 }
 
-// Tiled path: the largest S in {16, 8, 4, 2, 1} that still gives every CU at
-// least 8 blocks (small inputs fall back to S = 1 with more planes in flight).
-// Measured on MI355X: S = 16 (64 KB runs per plane, one wave per SIMD) is the
-// fastest for 128-wide rows at 2 GB per call; S = 4..8 for 512-wide rows.
-constexpr unsigned kTiledMinBlocks = 2048;
+// Tiled path: the largest S in {16, 8, 4, 2, 1} that still gives at least
+// kTiledMinBlocks blocks (small inputs fall back to S = 1 with more planes in
+// flight). With N = 16 a block walks enough planes to amortise its prologue
+// (LSE loads, reductions) over 1024 blocks; with fewer planes it needs more,
+// smaller blocks. Measured on MI355X (bf16): N=16 D=128 rows 2^19 -> S = 16;
+// N=16 D=512 rows 2^16 -> S = 16; N=8 D=512 rows 2^16 -> S = 8;
+// N=8 D=256 rows 2^17 -> S = 8; N=8 D=128 rows 2^17 -> S = 4.
+constexpr uint64_t kTiledMinBlocks = 2048;
+constexpr uint64_t kTiledMinBlocksN16 = 1024;
 
 template <int DT, int NT, int G, bool PACKED>
 void launch_tiled_s(int S, const uint16_t* src, const float* lse, uint32_t rows, uint32_t stride,
@@ -611,8 +630,9 @@ CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, bool packed, bool f
                             (packed || uint64_t(N) * uint64_t(rows) < (uint64_t(1) << 32));
         if (fits32) {
             const uint64_t rps = kBlock / uint64_t(D / 8);
+            const uint64_t min_blocks = N >= 16 ? kTiledMinBlocksN16 : kTiledMinBlocks;
             int S = 16;
-            while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < kTiledMinBlocks) S /= 2;
+            while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < min_blocks) S /= 2;
             return {kPathTiled, S};
         }
     }

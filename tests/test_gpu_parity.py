@@ -220,6 +220,28 @@ def test_tiled_slots_ragged(lsec, N, B, H, D, dtype, base2, slots):
     assert_lse_close(L, L_ref)
 
 
+def test_tiled_n16_relaxed_block_count_sampled(lsec):
+    """N=16 takes 16 slots down to 1024 blocks: 67551 rows of D=512 (1056
+    blocks, ragged last block); the oracle checks token ranges at both ends
+    and in the middle."""
+    N, B, H, D = 16, 2047, 33, 512
+    _announce(f"tiled combine N={N} B={B} H={H} D={D} bf16, sampled")
+    assert lsec.lsec_combine_path(N, B, H, D) == "combine_tiled_kernel S=16"
+    w = synth.Workload("n16_d512", 90, "combine", N, B, H, D, "bf16", ("normal", 0.0, 1.0),
+                       ("uniform", -10.0, 30.0), special=SPECIALS, base2=True)
+    o, l = synth.combine_inputs(w)
+    M = max_abs_input(o, "bf16")
+    y, L = lsec.lsec_combine(to_dev(o, "bf16", DEV), f32_to_dev(l, DEV), base_e=False,
+                             return_lse=True)
+    torch.cuda.synchronize()
+    del o, l
+    for s, e in ((0, 64), (1000, 1064), (B - 64, B)):
+        os_, ls_ = synth.combine_inputs(w, b_lo=s, b_hi=e)
+        y_ref, L_ref = oracle.lse_combine(os_, ls_, "bf16", base2=True)
+        assert_output_close(y[s:e], y_ref, "bf16", M, f"tokens {s}:{e}")
+        assert_lse_close(L[s:e], L_ref, f"tokens {s}:{e}")
+
+
 @pytest.mark.parametrize("N,B,H,D,dtype,slots", [
     (4, 8193, 16, 128, "bf16", 1),   # 32772 rows of the packed layout, ragged
     (8, 4099, 64, 128, "bf16", 1),   # 32792 rows
