@@ -54,10 +54,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-struct __attribute__((aligned(4))) U32x4A4 {
-    uint32_t x, y, z, w;
-};
+// The same four dwords at 4-byte alignment (packed rows start every D + 2
+// elements, i.e. on 4-byte boundaries).
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
+// Every input byte is read once and every output byte written once, so all
+// streaming accesses are non-temporal (the `nt` cache policy); on MI355X plain
+// loads cost 12-15 % at 2 GB per call and up to 40 % on small cold calls.
 // 16-byte load / store at a 16-byte aligned address.
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -65,16 +68,22 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
-// 16-byte load / store at a 4-byte aligned address (packed rows).
+// 16-byte load / store at a 4-byte aligned address (packed rows): gfx950
+// serves dwordx4 at dword alignment. Packed rows (D + 2 elements) are written
+// in pieces that straddle cache lines, so those stores keep the default
+// policy: L2 assembles whole lines before they go to HBM (non-temporal stores
+// here measured about 10 % slower).
 __device__ __forceinline__ u32x4 ld16_a4(const uint16_t* p) {
-    U32x4A4 t = *reinterpret_cast<const U32x4A4*>(p);
-    u32x4 v = {t.x, t.y, t.z, t.w};
-    return v;
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(p));
 }
 __device__ __forceinline__ void st16_a4(uint16_t* p, u32x4 v) {
-    U32x4A4 t = {v.x, v.y, v.z, v.w};
-    *reinterpret_cast<U32x4A4*>(p) = t;
+    *reinterpret_cast<u32x4_a4*>(p) = static_cast<u32x4_a4>(v);
 }
+// The fp32 LSE in the tail of a packed row (same cache lines as the row).
+__device__ __forceinline__ float ld_tail(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
+}
+__device__ __forceinline__ void st_tail(void* p, float v) { *reinterpret_cast<float*>(p) = v; }
 
 // Element type: decode two packed 16-bit values, encode two floats (RNE).
 template <int DT>
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     const uint16_t* cp = rp + lane * 8;
 
     auto load_lse = [&](int n) -> float {
-        if (PACKED) return *reinterpret_cast<const float*>(rp + n * plane + D);
+        if (PACKED) return ld_tail(rp + n * plane + D);
         return lse[int64_t(n) * rows + row];
     };
     auto load_chunk = [&](int n) -> u32x4 {
@@ -349,15 +358,34 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
         row[s] = row0 + s * RPS + rib;
         const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
         off[s] = (rc * stride + lane * 8) * 2;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
         float l = -__builtin_inff();
         if (j < NT) {
             if (PACKED)
-                l = *reinterpret_cast<const float*>(base + j * plane_bytes + (rc * stride + D) * 2);
+                l = ld_tail(base + j * plane_bytes + (rc * stride + D) * 2);
             else
                 l = lse[j * rows + rc];
         }
         lw[s] = l;
     }
+    // The first plane group's loads go out right behind the LSE loads, so the
+    // LSE round trip overlaps the data instead of preceding it (small,
+    // latency-bound calls pay for exactly that) and the reductions below run
+    // while the data is in flight.
+    u32x4 v[PG][S];
+    auto load_group = [&](int n0) {
+#pragma unroll
+        for (int p = 0; p < PG; ++p) {
+            const char* pb = base + uint64_t(n0 + p) * plane_bytes;
+#pragma unroll
+            for (int s = 0; s < S; ++s) v[p][s] = PACKED ? ld16_a4_at(pb + off[s]) : ld16_nt_at(pb + off[s]);
+        }
+    };
+    load_group(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const float l = j < NT ? sanitize(lw[s]) : -__builtin_inff();
@@ -376,13 +404,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
         for (int k = 0; k < 8; ++k) acc[s][k] = 0.0f;
 #pragma unroll 1
     for (int n0 = 0; n0 < NT; n0 += PG) {
-        u32x4 v[PG][S];
-#pragma unroll
-        for (int p = 0; p < PG; ++p) {
-            const char* pb = base + uint64_t(n0 + p) * plane_bytes;
-#pragma unroll
-            for (int s = 0; s < S; ++s) v[p][s] = PACKED ? ld16_a4_at(pb + off[s]) : ld16_nt_at(pb + off[s]);
-        }
+        if (n0 > 0) load_group(n0);
         __builtin_amdgcn_sched_barrier(0);  // all PG*S loads issued before the first is used
 #pragma unroll
         for (int p = 0; p < PG; ++p)
@@ -453,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_kernel(
     const uint32_t src = b * H + r * hl_div.d + hl;
     uint16_t* dp = send + int64_t(s) * (D + 2);
     st16_a4(dp + lane * 8, ld16(in + int64_t(src) * D + lane * 8));
-    if (lane == 0) *reinterpret_cast<float*>(dp + D) = lse[src];
+    if (lane == 0) st_tail(dp + D, lse[src]);
 }
 
 // ---------------------------------------------------------------- pack (general path)
@@ -493,7 +515,7 @@ __global__ __launch_bounds__(kBlock) void unpack_rows_kernel(
     if (q >= total_rows) return;
     const uint16_t* sp = recv + int64_t(q) * (D + 2);
     st16(outs + int64_t(q) * D + lane * 8, ld16_a4(sp + lane * 8));
-    if (lane == 0) lses[q] = *reinterpret_cast<const float*>(sp + D);
+    if (lane == 0) lses[q] = ld_tail(sp + D);
 }
 
 __global__ __launch_bounds__(kBlock) void unpack_elems_kernel(
