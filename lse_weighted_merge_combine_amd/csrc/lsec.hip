@@ -458,6 +458,10 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
 //
 // Send row s = (r * B + b) * Hl + hl takes attention-output row
 // src = b * H + r * Hl + hl: D elements, then the fp32 LSE's 32 bits.
+// A lane group of D/8 lanes owns a send row; each group handles kPackRows
+// send rows (spaced one block-width apart) with all their loads in flight.
+constexpr int kPackRows = 4;
+
 __global__ __launch_bounds__(kBlock) void pack_rows_kernel(
     const uint16_t* __restrict__ in, const float* __restrict__ lse, uint32_t send_rows,
     FastDiv g, uint32_t rows_per_block, FastDiv hl_div, FastDiv b_div, uint32_t H, int D,
@@ -466,16 +470,30 @@ __global__ __launch_bounds__(kBlock) void pack_rows_kernel(
     const uint32_t rib = fdiv(t, g);
     const uint32_t lane = t - rib * g.d;
     if (rib >= rows_per_block) return;
-    const uint32_t s = blockIdx.x * rows_per_block + rib;
-    if (s >= send_rows) return;
-    const uint32_t rb = fdiv(s, hl_div);
-    const uint32_t hl = s - rb * hl_div.d;
-    const uint32_t r = fdiv(rb, b_div);
-    const uint32_t b = rb - r * b_div.d;
-    const uint32_t src = b * H + r * hl_div.d + hl;
-    uint16_t* dp = send + int64_t(s) * (D + 2);
-    st16_a4(dp + lane * 8, ld16(in + int64_t(src) * D + lane * 8));
-    if (lane == 0) st_tail(dp + D, lse[src]);
+    u32x4 v[kPackRows];
+    float lv[kPackRows];
+    uint32_t sr[kPackRows];
+#pragma unroll
+    for (int k = 0; k < kPackRows; ++k) {
+        const uint32_t q = (blockIdx.x * kPackRows + k) * rows_per_block + rib;
+        sr[k] = q;
+        const uint32_t s = q < send_rows ? q : send_rows - 1;  // clamp: load a valid row, store nothing
+        const uint32_t rb = fdiv(s, hl_div);
+        const uint32_t hl = s - rb * hl_div.d;
+        const uint32_t r = fdiv(rb, b_div);
+        const uint32_t b = rb - r * b_div.d;
+        const uint32_t src = b * H + r * hl_div.d + hl;
+        v[k] = ld16(in + int64_t(src) * D + lane * 8);
+        lv[k] = lse[src];
+    }
+#pragma unroll
+    for (int k = 0; k < kPackRows; ++k) {
+        if (sr[k] < send_rows) {
+            uint16_t* dp = send + int64_t(sr[k]) * (D + 2);
+            st16_a4(dp + lane * 8, v[k]);
+            if (lane == 0) st_tail(dp + D, lv[k]);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- pack (general path)
@@ -801,7 +819,7 @@ int lsec_pack_send(const void* attn_out, const float* attn_lse, int64_t N, int64
     if (fast) {
         const uint32_t g = uint32_t(D / 8);
         const uint32_t rpb = kBlock / g;
-        const unsigned blocks = unsigned((rows + rpb - 1) / rpb);
+        const unsigned blocks = unsigned((rows + rpb * kPackRows - 1) / (rpb * kPackRows));
         pack_rows_kernel<<<blocks, kBlock, 0, st>>>(in, attn_lse, uint32_t(rows), make_fastdiv(g),
                                                     rpb, make_fastdiv(uint32_t(Hl)),
                                                     make_fastdiv(uint32_t(B)), uint32_t(H),
