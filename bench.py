@@ -13,6 +13,8 @@ already resident in HBM:
 * ``packed``: one rank's lsec_pack_send ([2048, 64, 128] -> [8, 2048, 8, 130])
   followed by lsec_unpack_combine of an 8-rank receive buffer (the exchange
   in between is not part of a single GPU's work).
+* ``merge_heads``: lsec_merge of received planes [8, 8, 2048, 128] bf16 into
+  token-major [2048, 8, 128] (the head-scattered exchange of the Ascend merge).
 
 Workloads under 1 GiB are timed cold: a 1 GiB buffer is rewritten before each
 step, outside the timed events. Kernel time comes from HIP events recorded on
@@ -95,7 +97,22 @@ def build_workload(name: str, dev):
     info = {"workload": name, "desc": w.desc, "N": w.N, "B": w.B, "H": w.H, "D": w.D,
             "io_dtype": w.dtype, "lse_base": "2" if w.base2 else "e",
             "return_lse": w.return_lse, "parallelism": "none (one GPU)"}
-    if w.kind == "combine":
+    if w.kind == "merge":
+        o, l = synth.combine_inputs(w)
+        og, lg = dev_bits(o), torch.from_numpy(l).to(dev)
+        out = torch.empty((w.H, w.B, w.D), dtype=tdt, device=dev)   # token-major [C, A, D]
+        nbytes = combine_bytes(w.N, w.B, w.H, w.D, 2, False)
+        kname = f"{lsec.lsec_combine_path(w.N, w.B, w.H, w.D)} ({w.dtype}, N={w.N}, D={w.D}, " \
+                f"token-major store)"
+
+        def step():
+            lsec.lsec_merge(og, lg, 2, base_e=True, return_lse=False, out=out)
+
+        kernels = [(kname, nbytes, step)]
+        host = (o, l)
+        rows = w.B * w.H
+        info["token_dim"] = 2
+    elif w.kind == "combine":
         t0 = time.time()
         o, l = synth.combine_inputs(w)
         log(f"[bench] generated {name} inputs in {time.time() - t0:.1f}s")
@@ -235,7 +252,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large_batch",
-                    choices=["large_batch", "mla_decode", "fp16_base2", "packed", "small"])
+                    choices=["large_batch", "mla_decode", "fp16_base2", "packed", "small",
+                             "merge_heads"])
     ap.add_argument("--flush-mib", type=int, default=-1,
                     help="cache flush before each step (default: 1024 MiB if the step's "
                          "working set is under 1 GiB, else none)")

@@ -1,7 +1,8 @@
 /*
  * lsec.h -- C ABI of the LSE-weighted combine library (liblsec.so), gfx950.
  *
- * The operations are those of the page "vllm.v1.attention.ops.dcp_alltoall":
+ * The operations are those of the page "vllm.v1.attention.ops.dcp_alltoall"
+ * (lsec_merge: of the page "vllm_ascend/attention/context_parallel/sfa_cp.py"):
  *  - lsec_combine        : `_lse_weighted_combine` (merge N partial attention
  *                          outputs by their log-sum-exp weights);
  *  - lsec_pack_send      : `_dcp_a2a_pack_send` inside `dcp_a2a_lse_reduce`
@@ -52,7 +53,8 @@ enum {
     LSEC_ERR_DTYPE = 4,        /* dtype is neither LSEC_BF16 nor LSEC_FP16 */
     LSEC_ERR_ALIGNMENT = 5,    /* a pointer is not aligned to its element size */
     LSEC_ERR_BASE = 6,         /* base is neither LSEC_BASE_E nor LSEC_BASE_2 */
-    LSEC_ERR_LAUNCH = 7        /* the HIP runtime rejected the kernel launch */
+    LSEC_ERR_LAUNCH = 7,       /* the HIP runtime rejected the kernel launch */
+    LSEC_ERR_TOKEN_DIM = 8     /* token_dim is neither 1 nor 2 (lsec_merge) */
 };
 
 /* Element types of the attention outputs. */
@@ -84,6 +86,25 @@ int lsec_pack_dim(int dtype);
  */
 int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
                  int64_t D, int dtype, int base, void* out, float* out_lse, void* stream);
+
+/*
+ * lsec_merge -- the merge of page "vllm_ascend/attention/context_parallel/
+ * sfa_cp.py", `_merge_dcp_outputs_with_torch`: the combine of lsec_combine over
+ * received planes whose token index is the first or the second of the two row
+ * dimensions, written token-major (the merge's trailing `movedim`).
+ *   outputs : [N, A, C, D] dtype   plane n = what rank n sent
+ *   lses    : [N, A, C]    fp32
+ *   token_dim == 1 (tokens are A, e.g. token-sharded exchange):
+ *       out [A, C, D], out_lse [A, C]     -- identical to lsec_combine(B=A, H=C)
+ *   token_dim == 2 (tokens are C, e.g. head-sharded exchange [N, Hl, T, D]):
+ *       out [C, A, D], out_lse [C, A]     -- row (a, c) is stored at (c, a)
+ * The page's merge is base e and returns no LSE; `base` and `out_lse` extend
+ * it exactly as in lsec_combine (out_lse may be NULL).
+ * Errors: TOKEN_DIM, NULL, SHAPE, DTYPE, BASE, ALIGNMENT, LAUNCH.
+ */
+int lsec_merge(const void* outputs, const float* lses, int64_t N, int64_t A, int64_t C,
+               int64_t D, int token_dim, int dtype, int base, void* out, float* out_lse,
+               void* stream);
 
 /*
  * lsec_pack_send -- `_dcp_a2a_pack_send`.

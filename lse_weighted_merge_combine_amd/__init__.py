@@ -17,7 +17,12 @@ Entry points (same names as the C ABI):
 * ``lsec_unpack(recv)`` -- the layout half of the receive step.
 * ``lsec_pack_dim(dtype)`` -- ``_dcp_a2a_lse_pack_dim``.
 
-``lse_weighted_combine`` keeps the argument names of the page's function.
+* ``lsec_merge(outputs, lses, token_dim)`` -- ``_merge_dcp_outputs_with_torch``
+  of the page "vllm_ascend/attention/context_parallel/sfa_cp.py": the same
+  combine over received planes, stored token-major.
+
+``lse_weighted_combine`` and ``merge_dcp_outputs`` keep the argument names of
+the pages' functions.
 """
 from __future__ import annotations
 
@@ -37,6 +42,7 @@ LSEC_ERR_DTYPE = 4
 LSEC_ERR_ALIGNMENT = 5
 LSEC_ERR_BASE = 6
 LSEC_ERR_LAUNCH = 7
+LSEC_ERR_TOKEN_DIM = 8
 LSEC_BF16 = 0
 LSEC_FP16 = 1
 LSEC_BASE_E = 0
@@ -79,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_unpack_combine.argtypes = [P, I64, I64, I64, I64, I, I, P, P, P]
     lib.lsec_unpack.restype = I
     lib.lsec_unpack.argtypes = [P, I64, I64, I64, I64, I, P, P, P]
+    lib.lsec_merge.restype = I
+    lib.lsec_merge.argtypes = [P, P, I64, I64, I64, I64, I, I, I, P, P, P]
     lib.lsec_combine_path.restype = ctypes.c_char_p
     lib.lsec_combine_path.argtypes = [I64, I64, I64, I64, I, I]
     _lib = lib
@@ -164,6 +172,46 @@ def lsec_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
                           _ptr(out_lse) if return_lse else None, _stream(dev, stream))
     _raise_on(st, "lsec_combine")
     return (out, out_lse) if return_lse else out
+
+
+def lsec_merge(outputs: torch.Tensor, lses: torch.Tensor, token_dim: int, base_e: bool = True,
+               return_lse: bool = False, out: torch.Tensor | None = None,
+               out_lse: torch.Tensor | None = None, stream=None):
+    """Token-major merge of received planes outputs [N,A,C,D] + lses [N,A,C].
+
+    token_dim 1: tokens are A -> [A,C,D] (+ [A,C]); token_dim 2: tokens are C
+    -> [C,A,D] (+ [C,A]), i.e. row (a, c) is stored at (c, a).
+    """
+    lib = load_library()
+    if outputs.dim() != 4 or lses.dim() != 3 or tuple(lses.shape) != tuple(outputs.shape[:3]):
+        raise RuntimeError("merge expects matching rank/token/head dimensions, got "
+                           f"{tuple(outputs.shape)} and {tuple(lses.shape)}")
+    if token_dim not in (1, 2):
+        raise RuntimeError(f"merge token_dim must be 1 or 2, got {token_dim}")
+    if lses.dtype != torch.float32:
+        raise ValueError("lses must be float32")
+    dt = _dtype_code(outputs)
+    N, A, C, D = outputs.shape
+    dev = _check_dev(outputs, lses)
+    rows = (A, C) if token_dim == 1 else (C, A)
+    if out is None:
+        out = torch.empty(rows + (D,), dtype=outputs.dtype, device=dev)
+    if return_lse and out_lse is None:
+        out_lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    _check_out(out, rows + (D,), outputs.dtype, dev)
+    if return_lse:
+        _check_out(out_lse, rows, torch.float32, dev)
+    st = lib.lsec_merge(_ptr(outputs), _ptr(lses), N, A, C, D, int(token_dim), dt,
+                        LSEC_BASE_E if base_e else LSEC_BASE_2, _ptr(out),
+                        _ptr(out_lse) if return_lse else None, _stream(dev, stream))
+    _raise_on(st, "lsec_merge")
+    return (out, out_lse) if return_lse else out
+
+
+def merge_dcp_outputs(output_recv: torch.Tensor, lse_recv: torch.Tensor, token_dim: int):
+    """The Ascend page's ``_merge_dcp_outputs_with_torch(output_recv, lse_recv,
+    token_dim)`` (base e, no LSE), computed by the HIP kernel in the input dtype."""
+    return lsec_merge(output_recv, lse_recv, token_dim, base_e=True, return_lse=False)
 
 
 def lsec_pack_send(attn_out: torch.Tensor, attn_lse: torch.Tensor, N: int,
@@ -264,5 +312,5 @@ def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
 
 __all__ = [
     "lsec_pack_dim", "lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
-    "lsec_combine_path", "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
+    "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
 ]

@@ -50,6 +50,20 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f) {
     return uint32_t((uint64_t(__umulhi(x, f.m)) + x) >> f.l);
 }
 
+// Output row order. Identity (a == 0), or the token-major transpose of the
+// Ascend SFA merge with its token in the second input dimension: input row
+// r = (x, t) of an [A, C] grid (x < A, t < C) is stored at output row t * A + x.
+struct OutMap {
+    uint32_t a;  // A, or 0 for the identity
+    FastDiv c;   // divides by C
+};
+
+__device__ __forceinline__ uint32_t out_row(uint32_t r, OutMap om) {
+    if (om.a == 0) return r;
+    const uint32_t x = fdiv(r, om.c);
+    return (r - x * om.c.d) * om.a + x;
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -181,7 +195,7 @@ template <int DT, int NT, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     const uint16_t* __restrict__ src, const float* __restrict__ lse, int n_rt, uint32_t rows,
     FastDiv g, uint32_t rows_per_block, int64_t stride, int64_t plane, int D, float scale,
-    float inv_scale, uint16_t* __restrict__ out, float* __restrict__ out_lse) {
+    float inv_scale, uint16_t* __restrict__ out, float* __restrict__ out_lse, OutMap om) {
     const uint32_t t = threadIdx.x;
     const uint32_t rib = fdiv(t, g);
     const uint32_t lane = t - rib * g.d;
@@ -252,8 +266,9 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
                 if (n0 + k < N) fma8<DT>(v[k], w[k], acc);
         }
     }
-    st16(out + int64_t(row) * D + lane * 8, enc8<DT>(acc));
-    if (out_lse != nullptr && lane == 0) out_lse[row] = global_lse(s, m, inv_scale);
+    const uint32_t orow = out_row(row, om);
+    st16(out + int64_t(orow) * D + lane * 8, enc8<DT>(acc));
+    if (out_lse != nullptr && lane == 0) out_lse[orow] = global_lse(s, m, inv_scale);
 }
 
 // ---------------------------------------------------------------- combine (tiled path)
@@ -339,7 +354,7 @@ template <int DT, int NT, int G, int S, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     const uint16_t* src, const float* __restrict__ lse, uint32_t rows, uint32_t stride,
     uint64_t plane_bytes, float scale, float inv_scale, uint16_t* __restrict__ out,
-    float* __restrict__ out_lse) {
+    float* __restrict__ out_lse, OutMap om) {
     constexpr int RPS = kBlock / G;  // rows per slot
     constexpr int D = G * 8;
     constexpr int PG = tiled_pg<S, NT>();
@@ -394,7 +409,8 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
         const float w = j < NT ? weight(l - m, scale) : 0.0f;
         const float sum = row16_sum(w);
         lw[s] = w * (1.0f / fmaxf(sum, 1e-10f));
-        if (out_lse != nullptr && lane == 0 && row[s] < rows) out_lse[row[s]] = global_lse(sum, m, inv_scale);
+        if (out_lse != nullptr && lane == 0 && row[s] < rows)
+            out_lse[out_row(row[s], om)] = global_lse(sum, m, inv_scale);
     }
 
     float acc[S][8];
@@ -413,7 +429,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     }
 #pragma unroll
     for (int s = 0; s < S; ++s)
-        if (row[s] < rows) st16(out + uint64_t(row[s]) * D + lane * 8, enc8<DT>(acc[s]));
+        if (row[s] < rows) st16(out + uint64_t(out_row(row[s], om)) * D + lane * 8, enc8<DT>(acc[s]));
 }
 
 // ---------------------------------------------------------------- combine (general path)
@@ -424,7 +440,7 @@ template <int DT, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
     const uint16_t* __restrict__ src, const float* __restrict__ lse, int N, int64_t rows,
     int64_t stride, int64_t plane, int64_t D, float scale, float inv_scale,
-    uint16_t* __restrict__ out, float* __restrict__ out_lse) {
+    uint16_t* __restrict__ out, float* __restrict__ out_lse, int64_t map_a, int64_t map_c) {
     const int64_t total = rows * D;
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
          i += int64_t(gridDim.x) * kBlock) {
@@ -449,8 +465,9 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
             float w = weight(sanitize(load_lse(n)) - m, scale) * inv;
             acc = fmaf(Elem<DT>::dec1(rp[n * plane + d]), w, acc);
         }
-        out[row * D + d] = Elem<DT>::enc1(acc);
-        if (out_lse != nullptr && d == 0) out_lse[row] = global_lse(s, m, inv_scale);
+        const int64_t orow = map_a == 0 ? row : (row % map_c) * map_a + row / map_c;
+        out[orow * D + d] = Elem<DT>::enc1(acc);
+        if (out_lse != nullptr && d == 0) out_lse[orow] = global_lse(s, m, inv_scale);
     }
 }
 
@@ -575,26 +592,26 @@ bool fast_d(int64_t D) { return D % 8 == 0 && D <= kFastMaxD; }
 template <int DT, int NT, bool PACKED>
 void launch_combine_rows(const uint16_t* src, const float* lse, int N, uint32_t rows, int D,
                          float scale, float inv_scale, uint16_t* out, float* out_lse,
-                         hipStream_t st) {
+                         OutMap om, hipStream_t st) {
     const uint32_t g = uint32_t(D / 8);
     const uint32_t rpb = kBlock / g;
     const unsigned blocks = (rows + rpb - 1) / rpb;
     const int64_t stride = PACKED ? D + 2 : D;
     combine_rows_kernel<DT, NT, PACKED><<<blocks, kBlock, 0, st>>>(
         src, lse, N, rows, make_fastdiv(g), rpb, stride, int64_t(rows) * stride, D, scale,
-        inv_scale, out, out_lse);
+        inv_scale, out, out_lse, om);
 }
 
 template <int DT, bool PACKED>
 void dispatch_n(const uint16_t* src, const float* lse, int N, uint32_t rows, int D, float scale,
-                float inv_scale, uint16_t* out, float* out_lse, hipStream_t st) {
+                float inv_scale, uint16_t* out, float* out_lse, OutMap om, hipStream_t st) {
     switch (N) {
-        case 1: launch_combine_rows<DT, 1, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
-        case 2: launch_combine_rows<DT, 2, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
-        case 4: launch_combine_rows<DT, 4, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
-        case 8: launch_combine_rows<DT, 8, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
-        case 16: launch_combine_rows<DT, 16, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
-        default: launch_combine_rows<DT, 0, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, st); break;
+        case 1: launch_combine_rows<DT, 1, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
+        case 2: launch_combine_rows<DT, 2, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
+        case 4: launch_combine_rows<DT, 4, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
+        case 8: launch_combine_rows<DT, 8, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
+        case 16: launch_combine_rows<DT, 16, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
+        default: launch_combine_rows<DT, 0, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
     }
 }
 
@@ -611,12 +628,12 @@ constexpr uint64_t kTiledMinBlocksN16 = 1024;
 template <int DT, int NT, int G, bool PACKED>
 void launch_tiled_s(int S, const uint16_t* src, const float* lse, uint32_t rows, uint32_t stride,
                     uint64_t plane_bytes, float scale, float inv_scale, uint16_t* out,
-                    float* out_lse, hipStream_t st) {
+                    float* out_lse, OutMap om, hipStream_t st) {
     constexpr uint32_t RPS = kBlock / G;
     const unsigned blocks = (rows + RPS * S - 1) / (RPS * S);
 #define LSEC_TILED(SV)                                                                         \
     combine_tiled_kernel<DT, NT, G, SV, PACKED><<<blocks, kBlock, 0, st>>>(                    \
-        src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse)
+        src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om)
     switch (S) {
         case 16: LSEC_TILED(16); break;
         case 8: LSEC_TILED(8); break;
@@ -630,24 +647,25 @@ void launch_tiled_s(int S, const uint16_t* src, const float* lse, uint32_t rows,
 template <int DT, int G, bool PACKED>
 void launch_tiled_n(int N, int S, const uint16_t* src, const float* lse, uint32_t rows,
                     uint32_t stride, uint64_t plane_bytes, float scale, float inv_scale,
-                    uint16_t* out, float* out_lse, hipStream_t st) {
+                    uint16_t* out, float* out_lse, OutMap om, hipStream_t st) {
     switch (N) {
-        case 2: launch_tiled_s<DT, 2, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
-        case 4: launch_tiled_s<DT, 4, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
-        case 8: launch_tiled_s<DT, 8, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
-        default: launch_tiled_s<DT, 16, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+        case 2: launch_tiled_s<DT, 2, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
+        case 4: launch_tiled_s<DT, 4, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
+        case 8: launch_tiled_s<DT, 8, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
+        default: launch_tiled_s<DT, 16, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
     }
 }
 
 template <int DT, bool PACKED>
 void launch_tiled(int N, int S, uint32_t rows, int D, const uint16_t* src, const float* lse,
-                  float scale, float inv_scale, uint16_t* out, float* out_lse, hipStream_t st) {
+                  float scale, float inv_scale, uint16_t* out, float* out_lse, OutMap om,
+                  hipStream_t st) {
     const uint32_t stride = uint32_t(PACKED ? D + 2 : D);
     const uint64_t plane_bytes = uint64_t(rows) * stride * 2;
     switch (D) {
-        case 128: launch_tiled_n<DT, 16, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
-        case 256: launch_tiled_n<DT, 32, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
-        default: launch_tiled_n<DT, 64, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, st); break;
+        case 128: launch_tiled_n<DT, 16, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
+        case 256: launch_tiled_n<DT, 32, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
+        default: launch_tiled_n<DT, 64, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
     }
 }
 
@@ -681,7 +699,9 @@ CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, bool packed, bool f
 
 template <bool PACKED>
 int run_combine(const uint16_t* src, const float* lse, int64_t N, int64_t rows, int64_t D,
-                int dtype, int base, uint16_t* out, float* out_lse, bool fast, hipStream_t st) {
+                int dtype, int base, uint16_t* out, float* out_lse, bool fast, hipStream_t st,
+                int64_t map_a = 0, int64_t map_c = 1) {
+    const OutMap om{uint32_t(map_a), make_fastdiv(uint32_t(map_c))};
     const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
     const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
     const CombinePlan plan = plan_combine(N, rows, D, PACKED, fast);
@@ -689,26 +709,28 @@ int run_combine(const uint16_t* src, const float* lse, int64_t N, int64_t rows, 
     if (plan.kind == kPathTiled) {
         if (dtype == LSEC_BF16)
             launch_tiled<LSEC_BF16, PACKED>(int(N), plan.S, uint32_t(rows), int(D), src, lse,
-                                            scale, inv_scale, out, out_lse, st);
+                                            scale, inv_scale, out, out_lse, om, st);
         else
             launch_tiled<LSEC_FP16, PACKED>(int(N), plan.S, uint32_t(rows), int(D), src, lse,
-                                            scale, inv_scale, out, out_lse, st);
+                                            scale, inv_scale, out, out_lse, om, st);
     } else if (plan.kind == kPathRows) {
         if (dtype == LSEC_BF16)
             dispatch_n<LSEC_BF16, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale,
-                                          inv_scale, out, out_lse, st);
+                                          inv_scale, out, out_lse, om, st);
         else
             dispatch_n<LSEC_FP16, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale,
-                                          inv_scale, out, out_lse, st);
+                                          inv_scale, out, out_lse, om, st);
     } else {
         const int64_t stride = PACKED ? D + 2 : D;
         const unsigned blocks = general_grid(rows * D);
         if (dtype == LSEC_BF16)
             combine_elems_kernel<LSEC_BF16, PACKED><<<blocks, kBlock, 0, st>>>(
-                src, lse, int(N), rows, stride, rows * stride, D, scale, inv_scale, out, out_lse);
+                src, lse, int(N), rows, stride, rows * stride, D, scale, inv_scale, out, out_lse,
+                map_a, map_c);
         else
             combine_elems_kernel<LSEC_FP16, PACKED><<<blocks, kBlock, 0, st>>>(
-                src, lse, int(N), rows, stride, rows * stride, D, scale, inv_scale, out, out_lse);
+                src, lse, int(N), rows, stride, rows * stride, D, scale, inv_scale, out, out_lse,
+                map_a, map_c);
     }
     return launch_status();
 }
@@ -735,6 +757,7 @@ const char* lsec_status_string(int status) {
         case LSEC_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
         case LSEC_ERR_BASE: return "base must be LSEC_BASE_E or LSEC_BASE_2";
         case LSEC_ERR_LAUNCH: return "kernel launch failed";
+        case LSEC_ERR_TOKEN_DIM: return "token_dim must be 1 or 2";
         default: return "unknown status";
     }
 }
@@ -756,8 +779,15 @@ const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int pa
     }
 }
 
-int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
-                 int64_t D, int dtype, int base, void* out, float* out_lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by lsec_combine and lsec_merge: rows (b, h) of a [B, H] grid, stored
+// in input order or, when `transposed`, at row h * B + b.
+int combine_entry(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
+                  int64_t D, int dtype, int base, void* out, float* out_lse, void* stream,
+                  bool transposed) {
     if (N < 1 || B < 0 || H < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
     if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
     if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
@@ -774,7 +804,25 @@ int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, i
                       aligned(out, 16);
     return run_combine<false>(static_cast<const uint16_t*>(outputs), lses, N, rows, D, dtype,
                               base, static_cast<uint16_t*>(out), out_lse, fast,
-                              static_cast<hipStream_t>(stream));
+                              static_cast<hipStream_t>(stream), transposed ? B : 0,
+                              transposed ? H : 1);
+}
+
+}  // namespace
+
+extern "C" {
+
+int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
+                 int64_t D, int dtype, int base, void* out, float* out_lse, void* stream) {
+    return combine_entry(outputs, lses, N, B, H, D, dtype, base, out, out_lse, stream, false);
+}
+
+int lsec_merge(const void* outputs, const float* lses, int64_t N, int64_t A, int64_t C,
+               int64_t D, int token_dim, int dtype, int base, void* out, float* out_lse,
+               void* stream) {
+    if (token_dim != 1 && token_dim != 2) return LSEC_ERR_TOKEN_DIM;
+    return combine_entry(outputs, lses, N, A, C, D, dtype, base, out, out_lse, stream,
+                         token_dim == 2);
 }
 
 int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,

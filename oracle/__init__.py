@@ -10,6 +10,9 @@ only marshals numpy arrays through ctypes. Each function follows the page
 ``_lse_weighted_combine``; ``pack_send``, ``unpack`` and ``unpack_combine`` are
 the steps of its ``dcp_a2a_lse_reduce`` (``_dcp_a2a_pack_send``, the
 all-to-all's chunk-r-to-rank-r placement, ``_dcp_a2a_unpack_combine``).
+``merge`` is ``_merge_dcp_outputs_with_torch`` of the page
+"vllm_ascend/attention/context_parallel/sfa_cp.py" (the same combine, stored
+token-major).
 
 Parity status: every function here is pinned by the CPU tests (closed forms,
 brute-force sharded attention, library log-sum-exp / softmax, the second
@@ -63,6 +66,8 @@ def _load():
         lib.oracle_combine_f64.argtypes = [_P, _P, _I, _I, _I, ctypes.c_int, _P, _P]
         lib.oracle_lse_combine.argtypes = [_P, ctypes.c_int, _P, _I, _I, _I, _I, ctypes.c_int,
                                            _P, _P]
+        lib.oracle_merge.argtypes = [_P, ctypes.c_int, _P, _I, _I, _I, _I, ctypes.c_int,
+                                     ctypes.c_int, _P, _P]
         lib.oracle_pack_dim.argtypes = [ctypes.c_int]
         lib.oracle_pack_send.argtypes = [_P, _P, _I, _I, _I, _I, _P]
         lib.oracle_unpack.argtypes = [_P, _I, _I, _I, _I, _P, _P]
@@ -115,6 +120,25 @@ def lse_combine(outputs: np.ndarray, lses: np.ndarray, dtype: str, base2: bool =
     L = np.empty((B, H), dtype=np.float64)
     _check(_load().oracle_lse_combine(o.ctypes.data, _DT[dtype], l.ctypes.data, N, B, H, D,
                                       int(base2), y.ctypes.data, L.ctypes.data), "lse_combine")
+    return y, L
+
+
+def merge(outputs: np.ndarray, lses: np.ndarray, dtype: str, token_dim: int,
+          base2: bool = False):
+    """Token-major merge (Ascend SFA page, `_merge_dcp_outputs_with_torch`):
+    outputs [N,A,C,D] bits, lses [N,A,C] -> y [A,C,D] (token_dim 1) or
+    [C,A,D] (token_dim 2) in fp64, and L laid out the same way."""
+    o = _c(outputs, np.uint16)
+    l = _c(lses, np.float32)
+    N, A, C, D = o.shape
+    if l.shape != (N, A, C):
+        raise ValueError("lses shape must be outputs.shape[:3]")
+    shape = (A, C) if token_dim == 1 else (C, A)
+    y = np.empty(shape + (D,), dtype=np.float64)
+    L = np.empty(shape, dtype=np.float64)
+    _check(_load().oracle_merge(o.ctypes.data, _DT[dtype], l.ctypes.data, N, A, C, D,
+                                int(token_dim), int(base2), y.ctypes.data, L.ctypes.data),
+           "merge")
     return y, L
 
 

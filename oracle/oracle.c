@@ -141,6 +141,39 @@ int oracle_lse_combine(const uint16_t* outputs, int dtype, const float* lses, in
     return 0;
 }
 
+/* ---- the token-major merge ----
+ *
+ * Follows `_merge_dcp_outputs_with_torch` on the page
+ * "vllm_ascend/attention/context_parallel/sfa_cp.py": the received planes
+ * outputs [N][A][C][D] and lses [N][A][C] are combined per (a, c) row, and the
+ * result is laid out token-major (its closing `movedim`): token_dim 1 keeps
+ * y [A][C][D]; token_dim 2 stores row (a, c) at (c, a), y [C][A][D]. L is laid
+ * out the same way ([A][C] or [C][A]). The combine itself is the one above.
+ */
+int oracle_merge(const uint16_t* outputs, int dtype, const float* lses, int64_t N, int64_t A,
+                 int64_t C, int64_t D, int token_dim, int base2, double* y, double* L) {
+    if (N < 1 || A < 0 || C < 1 || D < 1 || (token_dim != 1 && token_dim != 2) ||
+        (dtype != ORACLE_BF16 && dtype != ORACLE_F16))
+        return -1;
+    const int64_t R = A * C;
+    double* ob = (double*)malloc(sizeof(double) * (size_t)(N * D + N));
+    if (!ob) return -2;
+    double* lb = ob + N * D;
+    for (int64_t a = 0; a < A; ++a)
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t r = a * C + c;                           /* input row */
+            const int64_t o = token_dim == 1 ? r : c * A + a;      /* output row */
+            for (int64_t n = 0; n < N; ++n) {
+                lb[n] = (double)lses[n * R + r];
+                for (int64_t d = 0; d < D; ++d)
+                    ob[n * D + d] = load_elem(&outputs[(n * R + r) * D + d], dtype);
+            }
+            oracle_combine_f64(ob, lb, N, 1, D, base2, &y[o * D], L ? &L[o] : 0);
+        }
+    free(ob);
+    return 0;
+}
+
 /* ---- pack / unpack (pure byte moves) ----
  *
  * pack:   out [B][H][D] (16-bit elements), lse [B][H] fp32

@@ -9,7 +9,7 @@ tensor is a pure function of ``(seed, workload id, tensor id, sub-stream, i)``,
 so any slice of a tensor can be generated on its own and equals the same slice
 of the whole tensor.
 
-The workloads are the five shapes the combine is specified and measured on:
+The workloads are the shapes the combine is specified and measured on:
 
 ==============  ======  ======  ====  ====  =====  ===========  =============  =====================
 name            N       B       H     D     dtype  outputs      LSE            special LSE entries
@@ -19,10 +19,13 @@ fp16_base2      4       256     32    128   fp16   N(0,1)       U[0,20] 2      2
 packed          8       2048    64    128   bf16   N(0,1)       U[-5,15] e     none (per-rank [B,H,D])
 mla_decode      8       4096    16    512   bf16   N(0,0.5)     N(10,3) 2      1% -inf
 large_batch     16      16384   32    128   bf16   N(0,1)       U[-10,30] e    0.5% split NaN/+inf/-inf
+merge_heads     8       8       2048  128   bf16   N(0,1)       U[-5,15] e     none (B = heads, H = tokens)
 ==============  ======  ======  ====  ====  =====  ===========  =============  =====================
 
 For ``packed`` the shape is one rank's ``[B, H, D]`` attention output plus its
 ``[B, H]`` LSE; rank ``r`` of ``N`` draws its own tensors (sub-stream ``r``).
+``merge_heads`` is the received planes ``[N, A=8 heads, C=2048 tokens, D=128]``
+of a head-scattered exchange (base e, no LSE), merged token-major.
 """
 from __future__ import annotations
 
@@ -121,7 +124,7 @@ def f32_to_f16(x: float) -> int:
 class Workload:
     name: str
     wid: int
-    kind: str  # "combine" or "packed"
+    kind: str  # "combine", "packed" or "merge"
     N: int
     B: int
     H: int
@@ -157,6 +160,10 @@ WORKLOADS = {
                  ("normal", 10.0, 3.0), special=((0.01, float("-inf")),), base2=True,
                  return_lse=False,
                  desc="N=8 B=4096 H=16 D=512 bf16, LSE base 2 N(10,3), 1% -inf"),
+        Workload("merge_heads", 6, "merge", 8, 8, 2048, 128, "bf16", ("normal", 0.0, 1.0),
+                 ("uniform", -5.0, 15.0), base2=False, return_lse=False,
+                 desc="received planes [8, 8 heads, 2048 tokens, 128] bf16 + [8, 8, 2048] -> "
+                      "token-major [2048, 8, 128] (head-scattered exchange, token_dim 2)"),
         Workload("large_batch", 5, "combine", 16, 16384, 32, 128, "bf16", ("normal", 0.0, 1.0),
                  ("uniform", -10.0, 30.0),
                  special=((0.005 / 3, float("nan")), (0.005 / 3, float("inf")),
@@ -197,7 +204,7 @@ def combine_inputs(w: Workload | str, seed: int = 0, b_lo: int = 0, b_hi: int | 
     slice of the whole.
     """
     w = WORKLOADS[w] if isinstance(w, str) else w
-    if w.kind != "combine":
+    if w.kind == "packed":
         raise ValueError(f"{w.name} is a packed workload; use rank_inputs()")
     b_hi = w.B if b_hi is None else b_hi
     if not (0 <= b_lo <= b_hi <= w.B):

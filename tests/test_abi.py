@@ -30,8 +30,8 @@ def _declared():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for n in ("lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
-              "lsec_pack_dim", "lsec_status_string", "lsec_version"):
+    for n in ("lsec_combine", "lsec_merge", "lsec_pack_send", "lsec_unpack_combine",
+              "lsec_unpack", "lsec_pack_dim", "lsec_status_string", "lsec_version"):
         assert n in names
 
 
@@ -45,6 +45,7 @@ def test_constants_match_header(lib):
     src = open(HEADER).read()
     for name in ("LSEC_OK", "LSEC_ERR_NULL", "LSEC_ERR_SHAPE", "LSEC_ERR_DIVISIBILITY",
                  "LSEC_ERR_DTYPE", "LSEC_ERR_ALIGNMENT", "LSEC_ERR_BASE", "LSEC_ERR_LAUNCH",
+                 "LSEC_ERR_TOKEN_DIM",
                  "LSEC_BF16", "LSEC_FP16", "LSEC_BASE_E", "LSEC_BASE_2"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == getattr(lsec, name), name
@@ -53,7 +54,7 @@ def test_constants_match_header(lib):
 def test_pack_dim_and_strings(lib):
     assert lib.lsec_pack_dim(0) == 2 and lib.lsec_pack_dim(1) == 2 and lib.lsec_pack_dim(7) == -1
     assert lib.lsec_version() >= 100
-    for s in range(0, 9):
+    for s in range(0, 10):
         assert lib.lsec_status_string(s)
 
 
@@ -133,3 +134,20 @@ def test_python_binding_rejects_bad_tensors():
 ])
 def test_combine_path(lib, args, want):
     assert lib.lsec_combine_path(*args).decode() == want
+
+
+def test_merge_validation(lib):
+    m = lib.lsec_merge
+    assert m(FAKE, FAKE, 2, 3, 4, 8, 0, 0, 0, FAKE, None, None) == 8   # token_dim 0
+    assert m(FAKE, FAKE, 2, 3, 4, 8, 3, 0, 0, FAKE, None, None) == 8   # token_dim 3
+    assert m(FAKE, FAKE, 0, 3, 4, 8, 2, 0, 0, FAKE, None, None) == 2   # N < 1
+    assert m(FAKE, FAKE, 2, 3, 4, 8, 2, 7, 0, FAKE, None, None) == 4   # dtype
+    assert m(None, FAKE, 2, 3, 4, 8, 2, 0, 0, FAKE, None, None) == 1   # NULL outputs
+    assert m(FAKE, FAKE, 2, 3, 4, 8, 2, 0, 0, FAKE + 1, None, None) == 5  # out alignment
+    assert m(None, None, 2, 0, 4, 8, 2, 0, 0, None, None, None) == 0   # empty
+    import torch
+    import lse_weighted_merge_combine_amd as lsec
+    with pytest.raises(RuntimeError):
+        lsec.lsec_merge(torch.zeros(2, 3, 4, 8, dtype=torch.bfloat16), torch.zeros(2, 3, 4), 3)
+    with pytest.raises(RuntimeError):
+        lsec.lsec_merge(torch.zeros(2, 3, 4, 8, dtype=torch.bfloat16), torch.zeros(2, 3, 5), 2)

@@ -321,6 +321,53 @@ def test_misaligned_buffers_take_general_path(lsec):
     assert_lse_close(L2, L2r)
 
 
+# ---------------------------------------------------------------- token-major merge
+
+MERGE = [
+    # N, A, C, D, dtype, token_dim, base2
+    (8, 8, 2048, 128, "bf16", 2, False),   # head-scattered exchange [N, Hl, T, D] -> [T, Hl, D]
+    (4, 512, 64, 128, "bf16", 1, False),   # token-scattered [N, T/N, H, D] -> [T/N, H, D]
+    (16, 4, 8197, 128, "bf16", 2, True),   # tiled 8 slots, ragged, transposed store
+    (4, 16, 1031, 512, "f16", 2, False),   # one wave per row
+    (3, 5, 77, 64, "bf16", 2, True),       # row kernel (N = 3)
+    (2, 7, 13, 12, "f16", 2, False),       # element kernel (D % 8 != 0)
+]
+
+
+@pytest.mark.parametrize("N,A,C,D,dtype,token_dim,base2", MERGE)
+def test_merge_token_major(lsec, N, A, C, D, dtype, token_dim, base2):
+    _announce(f"merge N={N} A={A} C={C} D={D} {dtype} token_dim={token_dim} base2={base2}")
+    o, l = synth.custom_inputs(N, A, C, D, dtype=dtype, seed=A * 31 + C, special=SPECIALS)
+    y, L = lsec.lsec_merge(to_dev(o, dtype, DEV), f32_to_dev(l, DEV), token_dim,
+                           base_e=not base2, return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.merge(o, l, dtype, token_dim, base2)
+    assert tuple(y.shape) == y_ref.shape
+    assert_output_close(y, y_ref, dtype, max_abs_input(o, dtype))
+    assert_lse_close(L, L_ref)
+
+
+def test_merge_heads_workload_full(lsec):
+    """The merge_heads workload the benchmark times: [8, 8, 2048, 128] bf16 planes
+    merged token-major into [2048, 8, 128] (head-scattered exchange)."""
+    w = synth.WORKLOADS["merge_heads"]
+    _announce("merge_heads full")
+    o, l = synth.combine_inputs(w)
+    y = lsec.lsec_merge(to_dev(o, w.dtype, DEV), f32_to_dev(l, DEV), 2, base_e=True)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.merge(o, l, w.dtype, 2, False)
+    assert tuple(y.shape) == (w.H, w.B, w.D)
+    assert_output_close(y, y_ref, w.dtype, max_abs_input(o, w.dtype))
+
+
+def test_merge_page_alias(lsec):
+    o, l = synth.custom_inputs(4, 4, 33, 128, seed=14, special=SPECIALS)
+    y = lsec.merge_dcp_outputs(to_dev(o, "bf16", DEV), f32_to_dev(l, DEV), 2)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.merge(o, l, "bf16", 2)
+    assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
+
+
 # ---------------------------------------------------------------- degenerate cases
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

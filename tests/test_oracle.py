@@ -294,3 +294,34 @@ def test_bad_arguments(oracle_mod):
         oracle_mod.pack_send(o, l, 4)  # H = 6 not divisible by 4
     with pytest.raises(ValueError):
         oracle_mod.unpack(np.zeros((2, 1, 1, 5), dtype=np.uint16), 4)
+
+
+# ---------------------------------------------------------------- token-major merge
+
+def _page2_merge_layout(o, lse, token_dim):
+    """`_merge_dcp_outputs_with_torch` written with torch library calls: mask
+    non-finite LSEs to -inf, softmax over shards, NaN -> 0, weighted sum over
+    dim 0, then move dimension token_dim - 1 to the front."""
+    lt = torch.from_numpy(lse)
+    lt = lt.masked_fill(~torch.isfinite(lt), float("-inf"))
+    w = torch.nan_to_num(torch.softmax(lt, dim=0), nan=0.0)
+    out = (torch.from_numpy(o) * w.unsqueeze(-1)).sum(dim=0)
+    return out.movedim(token_dim - 1, 0).contiguous().numpy()
+
+
+@pytest.mark.parametrize("token_dim", [1, 2])
+def test_merge_matches_page2_layout(oracle_mod, synth_mod, token_dim):
+    N, A, C, D = 4, 3, 5, 8
+    o, l = synth_mod.custom_inputs(N, A, C, D, seed=60 + token_dim,
+                                   special=((0.1, float("nan")), (0.1, float("inf")),
+                                            (0.1, float("-inf"))))
+    l[:, 1, 2] = -np.inf   # an all -inf row
+    y, L = oracle_mod.merge(o, l, "bf16", token_dim)
+    want = _page2_merge_layout(oracle_mod.bits_to_f64(o, "bf16"), l.astype(np.float64), token_dim)
+    assert y.shape == want.shape
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-13)
+    # the LSE follows the same layout and equals the plain combine's
+    _, Lc = oracle_mod.lse_combine(o, l, "bf16")
+    assert np.array_equal(L, Lc if token_dim == 1 else Lc.T)
+    with pytest.raises(ValueError):
+        oracle_mod.merge(o, l, "bf16", 3)
