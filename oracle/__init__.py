@@ -12,7 +12,11 @@ the steps of its ``dcp_a2a_lse_reduce`` (``_dcp_a2a_pack_send``, the
 all-to-all's chunk-r-to-rank-r placement, ``_dcp_a2a_unpack_combine``).
 ``merge`` is ``_merge_dcp_outputs_with_torch`` of the page
 "vllm_ascend/attention/context_parallel/sfa_cp.py" (the same combine, stored
-token-major).
+token-major). ``correct_partial`` is the local step of the LSE all-gather +
+output reduce-scatter strategies that the page "vllm.v1.attention.ops.dcp"
+names (``cp_lse_ag_out_rs`` / ``cp_lse_ag_out_ar``; a reading, since their
+bodies are not shown): pinned by "the corrected partials of all ranks sum to
+the combine".
 
 Parity status: every function here is pinned by the CPU tests (closed forms,
 brute-force sharded attention, library log-sum-exp / softmax, the second
@@ -68,6 +72,8 @@ def _load():
                                            _P, _P]
         lib.oracle_merge.argtypes = [_P, ctypes.c_int, _P, _I, _I, _I, _I, ctypes.c_int,
                                      ctypes.c_int, _P, _P]
+        lib.oracle_correct_partial.argtypes = [_P, _I, _I, _P, ctypes.c_int, _I, _I, _I,
+                                               ctypes.c_int, _P, _P]
         lib.oracle_pack_dim.argtypes = [ctypes.c_int]
         lib.oracle_pack_send.argtypes = [_P, _P, _I, _I, _I, _I, _P]
         lib.oracle_unpack.argtypes = [_P, _I, _I, _I, _I, _P, _P]
@@ -139,6 +145,26 @@ def merge(outputs: np.ndarray, lses: np.ndarray, dtype: str, token_dim: int,
     _check(_load().oracle_merge(o.ctypes.data, _DT[dtype], l.ctypes.data, N, A, C, D,
                                 int(token_dim), int(base2), y.ctypes.data, L.ctypes.data),
            "merge")
+    return y, L
+
+
+def correct_partial(lses: np.ndarray, rank: int, partial: np.ndarray, dtype: str,
+                    base2: bool = False):
+    """Local step of an LSE all-gather + output reduce-scatter (reading of the
+    strategy names on the page "vllm.v1.attention.ops.dcp"): lses [N,B,H] of
+    all shards, rank r's partial [B,H,D] bits -> (partial * normalised weight
+    of shard r [B,H,D] f64, global LSE [B,H] f64)."""
+    l = _c(lses, np.float32)
+    p = _c(partial, np.uint16)
+    N, B, H = l.shape
+    if p.shape[:2] != (B, H):
+        raise ValueError("partial must be [B,H,D] with lses [N,B,H]")
+    D = p.shape[2]
+    y = np.empty((B, H, D), dtype=np.float64)
+    L = np.empty((B, H), dtype=np.float64)
+    _check(_load().oracle_correct_partial(l.ctypes.data, N, rank, p.ctypes.data, _DT[dtype], B, H,
+                                          D, int(base2), y.ctypes.data, L.ctypes.data),
+           "correct_partial")
     return y, L
 
 

@@ -141,6 +141,54 @@ int oracle_lse_combine(const uint16_t* outputs, int dtype, const float* lses, in
     return 0;
 }
 
+/* ---- the local step of an LSE all-gather + output reduce-scatter ----
+ *
+ * The page "vllm.v1.attention.ops.dcp" names the strategies
+ * `cp_lse_ag_out_rs` and `cp_lse_ag_out_ar` without showing them. Reading:
+ * every rank holds the gathered LSEs of all N shards and its own partial
+ * output o_r; it scales o_r by shard r's normalised weight from
+ * `_lse_weighted_combine` (steps sanitise, max, weights, NaN guard, clamped
+ * normalisation), and the collective then sums the scaled partials over the
+ * ranks, which gives the combine. L is the global LSE of the same function.
+ *   lses [N][B][H] fp32; partial [B][H][D] bf16/fp16 bits of rank `rank`
+ *   y [B][H][D] fp64 = partial * w_rank / max(S, 1e-10);  L [B][H] or NULL.
+ */
+int oracle_correct_partial(const float* lses, int64_t N, int64_t rank, const uint16_t* partial,
+                           int dtype, int64_t B, int64_t H, int64_t D, int base2, double* y,
+                           double* L) {
+    if (N < 1 || rank < 0 || rank >= N || B < 0 || H < 1 || D < 1 ||
+        (dtype != ORACLE_BF16 && dtype != ORACLE_F16))
+        return -1;
+    const int64_t R = B * H;
+    double* l = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!l) return -2;
+    for (int64_t r = 0; r < R; ++r) {
+        /* NaN and +-inf shard LSEs become -inf. */
+        for (int64_t n = 0; n < N; ++n) {
+            double v = (double)lses[n * R + r];
+            l[n] = (isnan(v) || isinf(v)) ? -INFINITY : v;
+        }
+        /* max over shards; an all -inf max is replaced by 0. */
+        double m = -INFINITY;
+        for (int64_t n = 0; n < N; ++n)
+            if (l[n] > m) m = l[n];
+        if (m == -INFINITY) m = 0.0;
+        /* weights; a NaN weight becomes 0; the sum in shard order. */
+        double s = 0.0, wr = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double w = base2 ? pow(2.0, l[n] - m) : exp(l[n] - m);
+            if (isnan(w)) w = 0.0;
+            s += w;
+            if (n == rank) wr = w;
+        }
+        const double wn = wr / (s < 1e-10 ? 1e-10 : s);
+        for (int64_t d = 0; d < D; ++d) y[r * D + d] = load_elem(&partial[r * D + d], dtype) * wn;
+        if (L) L[r] = (base2 ? log2(s) : log(s)) + m;
+    }
+    free(l);
+    return 0;
+}
+
 /* ---- the token-major merge ----
  *
  * Follows `_merge_dcp_outputs_with_torch` on the page

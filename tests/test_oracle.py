@@ -325,3 +325,38 @@ def test_merge_matches_page2_layout(oracle_mod, synth_mod, token_dim):
     assert np.array_equal(L, Lc if token_dim == 1 else Lc.T)
     with pytest.raises(ValueError):
         oracle_mod.merge(o, l, "bf16", 3)
+
+
+# ---------------------------------------------------------------- all-gather + reduce-scatter local step
+
+@pytest.mark.parametrize("base2", [False, True])
+def test_corrected_partials_sum_to_the_combine(oracle_mod, synth_mod, base2):
+    """The reduce-scatter / all-reduce sums every rank's corrected partial; the
+    sum must be the combine of all ranks' partials (and L its global LSE)."""
+    N, B, H, D = 5, 6, 4, 16
+    o, l = synth_mod.custom_inputs(N, B, H, D, seed=71,
+                                   special=((0.1, float("nan")), (0.1, float("inf")),
+                                            (0.1, float("-inf"))))
+    l[:, 0, 0] = -np.inf  # all -inf row: every corrected partial is 0
+    y_ref, L_ref = oracle_mod.lse_combine(o, l, "bf16", base2)
+    total = np.zeros_like(y_ref)
+    for r in range(N):
+        y, L = oracle_mod.correct_partial(l, r, o[r], "bf16", base2)
+        assert np.array_equal(L, L_ref)
+        total += y
+    np.testing.assert_allclose(total, y_ref, rtol=1e-12, atol=1e-13)
+    assert np.all(total[0, 0] == 0)
+
+
+def test_corrected_partial_closed_form(oracle_mod):
+    """Two shards, base e, lse = [0, ln 3]: normalised weights [1/4, 3/4]."""
+    l = np.array([0.0, math.log(3.0)], dtype=np.float32).reshape(2, 1, 1)
+    o = np.array([[0x4080, 0xBF80], [0x4100, 0x4040]], dtype=np.uint16)  # [4, -1], [8, 3] in bf16
+    w3 = float(np.float32(math.log(3.0)))  # the fp32 LSE actually stored
+    w = np.array([1.0, math.exp(w3)]) / (1.0 + math.exp(w3))
+    for r, want in ((0, np.array([4.0, -1.0]) * w[0]), (1, np.array([8.0, 3.0]) * w[1])):
+        y, L = oracle_mod.correct_partial(l, r, o[r].reshape(1, 1, 2), "bf16")
+        np.testing.assert_allclose(y.ravel(), want, rtol=1e-15)
+        assert abs(L[0, 0] - math.log(1.0 + math.exp(w3))) < 1e-15
+    with pytest.raises(ValueError):
+        oracle_mod.correct_partial(l, 2, o[0].reshape(1, 1, 2), "bf16")
