@@ -15,6 +15,9 @@ already resident in HBM:
   in between is not part of a single GPU's work).
 * ``merge_heads``: lsec_merge of received planes [8, 8, 2048, 128] bf16 into
   token-major [2048, 8, 128] (the head-scattered exchange of the Ascend merge).
+* ``ag_correct``: lsec_correct_partial of rank 3's [4096, 16, 512] bf16 partial
+  with the gathered LSEs [8, 4096, 16] (the local step of an all-gather +
+  reduce-scatter combine).
 
 Workloads under 1 GiB are timed cold: a 1 GiB buffer is rewritten before each
 step, outside the timed events. Kernel time comes from HIP events recorded on
@@ -97,7 +100,24 @@ def build_workload(name: str, dev):
     info = {"workload": name, "desc": w.desc, "N": w.N, "B": w.B, "H": w.H, "D": w.D,
             "io_dtype": w.dtype, "lse_base": "2" if w.base2 else "e",
             "return_lse": w.return_lse, "parallelism": "none (one GPU)"}
-    if w.kind == "merge":
+    if w.kind == "correct":
+        rank = 3
+        o, l = synth.combine_inputs(w)
+        part = dev_bits(o[rank])
+        lg = torch.from_numpy(l).to(dev)
+        del o
+        out = torch.empty((w.B, w.H, w.D), dtype=tdt, device=dev)
+        rows = w.B * w.H
+        nbytes = w.N * rows * 4 + 2 * rows * w.D * 2
+        kname = f"correct_tiled_kernel ({w.dtype}, N={w.N}, D={w.D}, rank {rank})"
+
+        def step():
+            lsec.lsec_correct_partial(lg, rank, part, base_e=not w.base2, out=out)
+
+        kernels = [(kname, nbytes, step)]
+        host = None
+        info["rank"] = rank
+    elif w.kind == "merge":
         o, l = synth.combine_inputs(w)
         og, lg = dev_bits(o), torch.from_numpy(l).to(dev)
         out = torch.empty((w.H, w.B, w.D), dtype=tdt, device=dev)   # token-major [C, A, D]
@@ -253,7 +273,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large_batch",
                     choices=["large_batch", "mla_decode", "fp16_base2", "packed", "small",
-                             "merge_heads"])
+                             "merge_heads", "ag_correct"])
     ap.add_argument("--flush-mib", type=int, default=-1,
                     help="cache flush before each step (default: 1024 MiB if the step's "
                          "working set is under 1 GiB, else none)")

@@ -54,7 +54,8 @@ enum {
     LSEC_ERR_ALIGNMENT = 5,    /* a pointer is not aligned to its element size */
     LSEC_ERR_BASE = 6,         /* base is neither LSEC_BASE_E nor LSEC_BASE_2 */
     LSEC_ERR_LAUNCH = 7,       /* the HIP runtime rejected the kernel launch */
-    LSEC_ERR_TOKEN_DIM = 8     /* token_dim is neither 1 nor 2 (lsec_merge) */
+    LSEC_ERR_TOKEN_DIM = 8,    /* token_dim is neither 1 nor 2 (lsec_merge) */
+    LSEC_ERR_RANK = 9          /* rank outside [0, N) (lsec_correct_partial) */
 };
 
 /* Element types of the attention outputs. */
@@ -105,6 +106,24 @@ int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, i
 int lsec_merge(const void* outputs, const float* lses, int64_t N, int64_t A, int64_t C,
                int64_t D, int token_dim, int dtype, int base, void* out, float* out_lse,
                void* stream);
+
+/*
+ * lsec_correct_partial -- the local step of the LSE all-gather + output
+ * reduce-scatter / all-reduce strategies that the page
+ * "vllm.v1.attention.ops.dcp" selects in `MLADCPManager` (`cp_lse_ag_out_rs`,
+ * `cp_lse_ag_out_ar`; only their names are shown, so this is a reading):
+ *   lses    : [N, B, H]  fp32   every shard's LSE (after the all-gather)
+ *   rank    : r in [0, N)       this rank's shard
+ *   partial : [B, H, D]  dtype  this rank's partial output
+ *   out     : [B, H, D]  dtype  partial * w_r / max(S, 1e-10) (written)
+ *   out_lse : [B, H]     fp32   global LSE (written), or NULL
+ * with w_r and S exactly as in lsec_combine, so the sum of `out` over the N
+ * ranks (what the reduce-scatter / all-reduce computes) is the combine.
+ * Errors: RANK, NULL, SHAPE, DTYPE, BASE, ALIGNMENT, LAUNCH.
+ */
+int lsec_correct_partial(const float* lses, int64_t N, int64_t rank, const void* partial,
+                         int64_t B, int64_t H, int64_t D, int dtype, int base, void* out,
+                         float* out_lse, void* stream);
 
 /*
  * lsec_pack_send -- `_dcp_a2a_pack_send`.

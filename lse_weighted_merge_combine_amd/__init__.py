@@ -21,6 +21,10 @@ Entry points (same names as the C ABI):
   of the page "vllm_ascend/attention/context_parallel/sfa_cp.py": the same
   combine over received planes, stored token-major.
 
+* ``lsec_correct_partial(lses, rank, partial)`` -- the local step of the LSE
+  all-gather + output reduce-scatter strategies named on the page
+  "vllm.v1.attention.ops.dcp" (``cp_lse_ag_out_rs`` / ``cp_lse_ag_out_ar``).
+
 ``lse_weighted_combine`` and ``merge_dcp_outputs`` keep the argument names of
 the pages' functions.
 """
@@ -43,13 +47,15 @@ LSEC_ERR_ALIGNMENT = 5
 LSEC_ERR_BASE = 6
 LSEC_ERR_LAUNCH = 7
 LSEC_ERR_TOKEN_DIM = 8
+LSEC_ERR_RANK = 9
 LSEC_BF16 = 0
 LSEC_FP16 = 1
 LSEC_BASE_E = 0
 LSEC_BASE_2 = 1
 
 _DTYPES = {torch.bfloat16: LSEC_BF16, torch.float16: LSEC_FP16}
-_VALUE_ERRORS = (LSEC_ERR_SHAPE, LSEC_ERR_DIVISIBILITY, LSEC_ERR_DTYPE, LSEC_ERR_BASE)
+_VALUE_ERRORS = (LSEC_ERR_SHAPE, LSEC_ERR_DIVISIBILITY, LSEC_ERR_DTYPE, LSEC_ERR_BASE,
+                 LSEC_ERR_RANK)
 
 _lib = None
 
@@ -87,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_unpack.argtypes = [P, I64, I64, I64, I64, I, P, P, P]
     lib.lsec_merge.restype = I
     lib.lsec_merge.argtypes = [P, P, I64, I64, I64, I64, I, I, I, P, P, P]
+    lib.lsec_correct_partial.restype = I
+    lib.lsec_correct_partial.argtypes = [P, I64, I64, P, I64, I64, I64, I, I, P, P, P]
     lib.lsec_combine_path.restype = ctypes.c_char_p
     lib.lsec_combine_path.argtypes = [I64, I64, I64, I64, I, I]
     _lib = lib
@@ -208,6 +216,37 @@ def lsec_merge(outputs: torch.Tensor, lses: torch.Tensor, token_dim: int, base_e
     return (out, out_lse) if return_lse else out
 
 
+def lsec_correct_partial(lses: torch.Tensor, rank: int, partial: torch.Tensor,
+                         base_e: bool = True, return_lse: bool = False,
+                         out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None,
+                         stream=None):
+    """Scale rank ``rank``'s partial output [B,H,D] by its normalised LSE weight
+    among the gathered LSEs [N,B,H] (fp32); summing the results over the N
+    ranks (a reduce-scatter or all-reduce) gives the combine."""
+    lib = load_library()
+    if lses.dim() != 3 or partial.dim() != 3 or tuple(partial.shape[:2]) != tuple(lses.shape[1:]):
+        raise ValueError(f"expected lses [N,B,H] and partial [B,H,D], got {tuple(lses.shape)} "
+                         f"and {tuple(partial.shape)}")
+    if lses.dtype != torch.float32:
+        raise ValueError("lses must be float32")
+    dt = _dtype_code(partial)
+    N, B, H = lses.shape
+    D = partial.shape[2]
+    dev = _check_dev(lses, partial)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=partial.dtype, device=dev)
+    if return_lse and out_lse is None:
+        out_lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check_out(out, (B, H, D), partial.dtype, dev)
+    if return_lse:
+        _check_out(out_lse, (B, H), torch.float32, dev)
+    st = lib.lsec_correct_partial(_ptr(lses), N, int(rank), _ptr(partial), B, H, D, dt,
+                                  LSEC_BASE_E if base_e else LSEC_BASE_2, _ptr(out),
+                                  _ptr(out_lse) if return_lse else None, _stream(dev, stream))
+    _raise_on(st, "lsec_correct_partial")
+    return (out, out_lse) if return_lse else out
+
+
 def merge_dcp_outputs(output_recv: torch.Tensor, lse_recv: torch.Tensor, token_dim: int):
     """The Ascend page's ``_merge_dcp_outputs_with_torch(output_recv, lse_recv,
     token_dim)`` (base e, no LSE), computed by the HIP kernel in the input dtype."""
@@ -312,5 +351,6 @@ def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
 
 __all__ = [
     "lsec_pack_dim", "lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
-    "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
+    "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
+    "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
 ]

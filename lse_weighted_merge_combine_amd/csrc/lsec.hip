@@ -471,6 +471,85 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
     }
 }
 
+// ---------------------------------------------------------------- correct a partial
+//
+// Local step of an LSE all-gather + output reduce-scatter (or all-reduce):
+// with every shard's LSE gathered, rank r scales its own partial output by
+// shard r's normalised weight; summing the scaled partials over the ranks
+// gives the combine. Per row: the same sanitise / max / weight / clamped
+// normalisation as the combine, then one plane read and one written.
+// Tiled path for D in {128, 256, 512} and N <= 16: G = D/8 lanes per row, S
+// row slots per lane, lane j of each 16-lane DPP row loads shard j's LSE.
+template <int DT, int G, int S>
+__global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
+    const float* __restrict__ lse, int N, int rank, const uint16_t* __restrict__ part,
+    uint32_t rows, float scale, float inv_scale, uint16_t* __restrict__ out,
+    float* __restrict__ out_lse) {
+    constexpr int RPS = kBlock / G;
+    constexpr int D = G * 8;
+    const uint32_t t = threadIdx.x;
+    const uint32_t rib = t / G;
+    const uint32_t lane = t % G;
+    const uint32_t j = t & 15u;
+    const uint32_t row0 = xcd_chunked_block(blockIdx.x, gridDim.x) * (RPS * S);
+    uint32_t row[S];
+    float lw[S];
+    u32x4 v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        row[s] = row0 + s * RPS + rib;
+        const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
+        lw[s] = int(j) < N ? lse[j * rows + rc] : -__builtin_inff();
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
+        v[s] = ld16(part + uint64_t(rc) * D + lane * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float l = int(j) < N ? sanitize(lw[s]) : -__builtin_inff();
+        float m = row16_max(l);
+        if (m == -__builtin_inff()) m = 0.0f;
+        const float w = int(j) < N ? weight(l - m, scale) : 0.0f;
+        const float sum = row16_sum(w);
+        const float wr = lane_value<G>(w * (1.0f / fmaxf(sum, 1e-10f)), rank);
+        if (row[s] < rows) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            fma8<DT>(v[s], wr, acc);
+            st16(out + uint64_t(row[s]) * D + lane * 8, enc8<DT>(acc));
+            if (out_lse != nullptr && lane == 0) out_lse[row[s]] = global_lse(sum, m, inv_scale);
+        }
+    }
+}
+
+// General path: any N, any D, 2-byte alignment; one thread per element.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void correct_elems_kernel(
+    const float* __restrict__ lse, int N, int rank, const uint16_t* __restrict__ part, int64_t rows,
+    int64_t D, float scale, float inv_scale, uint16_t* __restrict__ out,
+    float* __restrict__ out_lse) {
+    const int64_t total = rows * D;
+    for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * kBlock) {
+        const int64_t row = i / D;
+        const int64_t d = i - row * D;
+        float m = -__builtin_inff();
+        for (int n = 0; n < N; ++n) m = fmaxf(m, sanitize(lse[int64_t(n) * rows + row]));
+        if (m == -__builtin_inff()) m = 0.0f;
+        float s = 0.0f, wr = 0.0f;
+        for (int n = 0; n < N; ++n) {
+            const float w = weight(sanitize(lse[int64_t(n) * rows + row]) - m, scale);
+            s += w;
+            if (n == rank) wr = w;
+        }
+        wr *= 1.0f / fmaxf(s, 1e-10f);
+        out[i] = Elem<DT>::enc1(fmaf(Elem<DT>::dec1(part[i]), wr, 0.0f));
+        if (out_lse != nullptr && d == 0) out_lse[row] = global_lse(s, m, inv_scale);
+    }
+}
+
 // ---------------------------------------------------------------- pack (fast path)
 //
 // Send row s = (r * B + b) * Hl + hl takes attention-output row
@@ -735,6 +814,43 @@ int run_combine(const uint16_t* src, const float* lse, int64_t N, int64_t rows, 
     return launch_status();
 }
 
+template <int DT, int G>
+void launch_correct_s(int S, const float* lse, int N, int rank, const uint16_t* part, uint32_t rows,
+                      float scale, float inv_scale, uint16_t* out, float* out_lse,
+                      hipStream_t st) {
+    constexpr uint32_t RPS = kBlock / G;
+    const unsigned blocks = (rows + RPS * S - 1) / (RPS * S);
+#define LSEC_CORRECT(SV)                                                                        \
+    correct_tiled_kernel<DT, G, SV><<<blocks, kBlock, 0, st>>>(lse, N, rank, part, rows, scale, \
+                                                               inv_scale, out, out_lse)
+    switch (S) {
+        case 8: LSEC_CORRECT(8); break;
+        case 4: LSEC_CORRECT(4); break;
+        case 2: LSEC_CORRECT(2); break;
+        default: LSEC_CORRECT(1); break;
+    }
+#undef LSEC_CORRECT
+}
+
+template <int DT>
+void launch_correct(bool tiled, const float* lse, int64_t N, int64_t rank, const uint16_t* part,
+                    int64_t rows, int64_t D, float scale, float inv_scale, uint16_t* out,
+                    float* out_lse, hipStream_t st) {
+    if (!tiled) {
+        correct_elems_kernel<DT><<<general_grid(rows * D), kBlock, 0, st>>>(
+            lse, int(N), int(rank), part, rows, D, scale, inv_scale, out, out_lse);
+        return;
+    }
+    const uint64_t rps = kBlock / uint64_t(D / 8);
+    int S = 8;
+    while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < kTiledMinBlocks) S /= 2;
+    switch (D) {
+        case 128: launch_correct_s<DT, 16>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_lse, st); break;
+        case 256: launch_correct_s<DT, 32>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_lse, st); break;
+        default: launch_correct_s<DT, 64>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_lse, st); break;
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -758,6 +874,7 @@ const char* lsec_status_string(int status) {
         case LSEC_ERR_BASE: return "base must be LSEC_BASE_E or LSEC_BASE_2";
         case LSEC_ERR_LAUNCH: return "kernel launch failed";
         case LSEC_ERR_TOKEN_DIM: return "token_dim must be 1 or 2";
+        case LSEC_ERR_RANK: return "rank must be in [0, N)";
         default: return "unknown status";
     }
 }
@@ -843,6 +960,38 @@ int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int6
     return run_combine<true>(static_cast<const uint16_t*>(recv), nullptr, N, rows, D, dtype, base,
                              static_cast<uint16_t*>(out), out_lse, fast,
                              static_cast<hipStream_t>(stream));
+}
+
+int lsec_correct_partial(const float* lses, int64_t N, int64_t rank, const void* partial,
+                         int64_t B, int64_t H, int64_t D, int dtype, int base, void* out,
+                         float* out_lse, void* stream) {
+    if (N < 1 || B < 0 || H < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
+    if (rank < 0 || rank >= N) return LSEC_ERR_RANK;
+    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
+    int64_t rows, rd, nl;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, 2, &rd) ||
+        !mul_ok(rows, N, &nl) || !mul_ok(nl, 4, &nl))
+        return LSEC_ERR_SHAPE;
+    if (rows == 0) return LSEC_OK;
+    if (!lses || !partial || !out) return LSEC_ERR_NULL;
+    if (!aligned(partial, 2) || !aligned(out, 2) || !aligned(lses, 4) ||
+        (out_lse && !aligned(out_lse, 4)))
+        return LSEC_ERR_ALIGNMENT;
+    const bool tiled = (D == 128 || D == 256 || D == 512) && N <= 16 &&
+                       rows < (int64_t(1) << 31) && uint64_t(N) * uint64_t(rows) < (uint64_t(1) << 32) &&
+                       aligned(partial, 16) && aligned(out, 16);
+    const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
+    const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (dtype == LSEC_BF16)
+        launch_correct<LSEC_BF16>(tiled, lses, N, rank, static_cast<const uint16_t*>(partial), rows,
+                                  D, scale, inv_scale, static_cast<uint16_t*>(out), out_lse, st);
+    else
+        launch_correct<LSEC_FP16>(tiled, lses, N, rank, static_cast<const uint16_t*>(partial), rows,
+                                  D, scale, inv_scale, static_cast<uint16_t*>(out), out_lse, st);
+    return launch_status();
 }
 
 int lsec_pack_send(const void* attn_out, const float* attn_lse, int64_t N, int64_t B, int64_t H,

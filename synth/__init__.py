@@ -20,6 +20,7 @@ packed          8       2048    64    128   bf16   N(0,1)       U[-5,15] e     n
 mla_decode      8       4096    16    512   bf16   N(0,0.5)     N(10,3) 2      1% -inf
 large_batch     16      16384   32    128   bf16   N(0,1)       U[-10,30] e    0.5% split NaN/+inf/-inf
 merge_heads     8       8       2048  128   bf16   N(0,1)       U[-5,15] e     none (B = heads, H = tokens)
+ag_correct      8       4096    16    512   bf16   N(0,0.5)     N(10,3) 2      1% -inf (rank 3's plane used)
 ==============  ======  ======  ====  ====  =====  ===========  =============  =====================
 
 For ``packed`` the shape is one rank's ``[B, H, D]`` attention output plus its
@@ -124,7 +125,7 @@ def f32_to_f16(x: float) -> int:
 class Workload:
     name: str
     wid: int
-    kind: str  # "combine", "packed" or "merge"
+    kind: str  # "combine", "packed", "merge" or "correct"
     N: int
     B: int
     H: int
@@ -164,6 +165,11 @@ WORKLOADS = {
                  ("uniform", -5.0, 15.0), base2=False, return_lse=False,
                  desc="received planes [8, 8 heads, 2048 tokens, 128] bf16 + [8, 8, 2048] -> "
                       "token-major [2048, 8, 128] (head-scattered exchange, token_dim 2)"),
+        Workload("ag_correct", 7, "correct", 8, 4096, 16, 512, "bf16", ("normal", 0.0, 0.5),
+                 ("normal", 10.0, 3.0), special=((0.01, float("-inf")),), base2=True,
+                 return_lse=False,
+                 desc="gathered LSEs [8,4096,16] base 2 + rank 3's partial [4096,16,512] bf16 -> "
+                      "its share of the combine (all-gather + reduce-scatter local step)"),
         Workload("large_batch", 5, "combine", 16, 16384, 32, 128, "bf16", ("normal", 0.0, 1.0),
                  ("uniform", -10.0, 30.0),
                  special=((0.005 / 3, float("nan")), (0.005 / 3, float("inf")),
@@ -206,6 +212,7 @@ def combine_inputs(w: Workload | str, seed: int = 0, b_lo: int = 0, b_hi: int | 
     w = WORKLOADS[w] if isinstance(w, str) else w
     if w.kind == "packed":
         raise ValueError(f"{w.name} is a packed workload; use rank_inputs()")
+    # "correct" workloads draw all N shards; the caller uses one rank's plane
     b_hi = w.B if b_hi is None else b_hi
     if not (0 <= b_lo <= b_hi <= w.B):
         raise ValueError("token range out of bounds")

@@ -45,7 +45,7 @@ def test_constants_match_header(lib):
     src = open(HEADER).read()
     for name in ("LSEC_OK", "LSEC_ERR_NULL", "LSEC_ERR_SHAPE", "LSEC_ERR_DIVISIBILITY",
                  "LSEC_ERR_DTYPE", "LSEC_ERR_ALIGNMENT", "LSEC_ERR_BASE", "LSEC_ERR_LAUNCH",
-                 "LSEC_ERR_TOKEN_DIM",
+                 "LSEC_ERR_TOKEN_DIM", "LSEC_ERR_RANK",
                  "LSEC_BF16", "LSEC_FP16", "LSEC_BASE_E", "LSEC_BASE_2"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == getattr(lsec, name), name
@@ -54,7 +54,7 @@ def test_constants_match_header(lib):
 def test_pack_dim_and_strings(lib):
     assert lib.lsec_pack_dim(0) == 2 and lib.lsec_pack_dim(1) == 2 and lib.lsec_pack_dim(7) == -1
     assert lib.lsec_version() >= 100
-    for s in range(0, 10):
+    for s in range(0, 11):
         assert lib.lsec_status_string(s)
 
 
@@ -151,3 +151,15 @@ def test_merge_validation(lib):
         lsec.lsec_merge(torch.zeros(2, 3, 4, 8, dtype=torch.bfloat16), torch.zeros(2, 3, 4), 3)
     with pytest.raises(RuntimeError):
         lsec.lsec_merge(torch.zeros(2, 3, 4, 8, dtype=torch.bfloat16), torch.zeros(2, 3, 5), 2)
+
+
+def test_correct_partial_validation(lib):
+    c = lib.lsec_correct_partial
+    assert c(FAKE, 4, 4, FAKE, 2, 3, 8, 0, 0, FAKE, None, None) == 9    # rank == N
+    assert c(FAKE, 4, -1, FAKE, 2, 3, 8, 0, 0, FAKE, None, None) == 9   # rank < 0
+    assert c(FAKE, 0, 0, FAKE, 2, 3, 8, 0, 0, FAKE, None, None) == 2    # N < 1
+    assert c(FAKE, 4, 1, FAKE, 2, 3, 8, 3, 0, FAKE, None, None) == 4    # dtype
+    assert c(FAKE, 4, 1, FAKE, 2, 3, 8, 0, 5, FAKE, None, None) == 6    # base
+    assert c(None, 4, 1, FAKE, 2, 3, 8, 0, 0, FAKE, None, None) == 1    # NULL lses
+    assert c(FAKE, 4, 1, FAKE + 1, 2, 3, 8, 0, 0, FAKE, None, None) == 5  # odd partial
+    assert c(None, 4, 1, None, 0, 3, 8, 0, 0, None, None, None) == 0    # empty

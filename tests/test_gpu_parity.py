@@ -368,6 +368,48 @@ def test_merge_page_alias(lsec):
     assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
 
 
+# ---------------------------------------------------------------- all-gather + reduce-scatter local step
+
+CORRECT = [
+    # N, B, H, D, dtype, base2      (path)
+    (8, 4096, 16, 512, "bf16", True),   # tiled, one wave per row, 8 slots
+    (16, 1000, 32, 128, "bf16", False),  # tiled, ragged
+    (2, 777, 5, 256, "f16", True),      # tiled, two rows per wave
+    (4, 33, 3, 64, "bf16", False),      # element kernel (D outside {128, 256, 512})
+    (20, 9, 4, 128, "bf16", True),      # element kernel (N > 16)
+]
+
+
+@pytest.mark.parametrize("N,B,H,D,dtype,base2", CORRECT)
+def test_correct_partial(lsec, N, B, H, D, dtype, base2):
+    _announce(f"correct_partial N={N} B={B} H={H} D={D} {dtype} base2={base2}")
+    o, l = synth.custom_inputs(N, B, H, D, dtype=dtype, seed=N * 7 + D, special=SPECIALS)
+    lg = f32_to_dev(l, DEV)
+    M = max_abs_input(o, dtype)
+    total = torch.zeros((B, H, D), dtype=torch.float64, device=DEV)
+    for r in sorted({0, N // 2, N - 1}):
+        y, L = lsec.lsec_correct_partial(lg, r, to_dev(o[r], dtype, DEV), base_e=not base2,
+                                         return_lse=True)
+        torch.cuda.synchronize()
+        y_ref, L_ref = oracle.correct_partial(l, r, o[r], dtype, base2)
+        assert_output_close(y, y_ref, dtype, max_abs_input(o[r], dtype), f"rank {r}")
+        assert_lse_close(L, L_ref, f"rank {r}")
+    for r in range(N):
+        total += lsec.lsec_correct_partial(lg, r, to_dev(o[r], dtype, DEV),
+                                           base_e=not base2).double()
+    torch.cuda.synchronize()
+    # the ranks' corrected partials sum to the combine (each term rounded once)
+    y_all, _ = oracle.lse_combine(o, l, dtype, base2)
+    err = float((total.cpu().numpy() - y_all)[np.isfinite(y_all)].__abs__().max())
+    assert err <= 2 * (8e-3 if dtype == "bf16" else 1e-3) * M + 1e-6
+
+
+def test_correct_partial_rank_error(lsec):
+    with pytest.raises(ValueError):
+        lsec.lsec_correct_partial(torch.zeros(4, 2, 3, device=DEV), 4,
+                                  torch.zeros(2, 3, 8, dtype=torch.bfloat16, device=DEV))
+
+
 # ---------------------------------------------------------------- degenerate cases
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
