@@ -18,12 +18,17 @@ names (``cp_lse_ag_out_rs`` / ``cp_lse_ag_out_ar``; a reading, since their
 bodies are not shown): pinned by "the corrected partials of all ranks sum to
 the combine".
 
+Element dtypes: "bf16" and "f16" arrays hold 16-bit patterns (uint16);
+"f32" arrays are float32 values or their uint32 patterns. A packed row holds D
+elements and then P = 4 / element size elements carrying the fp32 LSE (P = 2
+for 16-bit elements, 1 for fp32).
+
 Parity status: every function here is pinned by the CPU tests (closed forms,
 brute-force sharded attention, library log-sum-exp / softmax, the second
 formulation of the merge on the Ascend SFA context-parallel page, the simulated
 all-to-all). One reading is not pinned against any source: the order of the
-LSE's bytes inside the two tail elements of a packed row (memory order is
-taken); the round trip through pack and unpack is.
+LSE's bytes inside the two tail elements of a 16-bit packed row (memory order
+is taken); the round trip through pack and unpack is.
 """
 from __future__ import annotations
 
@@ -37,8 +42,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liblsec_oracle.so")
 
-BF16, F16 = 0, 1
-_DT = {"bf16": BF16, "f16": F16}
+BF16, F16, F32 = 0, 1, 2
+_DT = {"bf16": BF16, "f16": F16, "f32": F32}
+_EB = {"bf16": 2, "f16": 2, "f32": 4}
 
 
 def build() -> str:
@@ -65,6 +71,8 @@ def _load():
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f32_to_f64.restype = ctypes.c_double
+        lib.oracle_f32_to_f64.argtypes = [ctypes.c_uint32]
         lib.oracle_bits_to_f64.argtypes = [_P, ctypes.c_int, _I, _P]
         lib.oracle_combine_f64.restype = None
         lib.oracle_combine_f64.argtypes = [_P, _P, _I, _I, _I, ctypes.c_int, _P, _P]
@@ -75,8 +83,8 @@ def _load():
         lib.oracle_correct_partial.argtypes = [_P, _I, _I, _P, ctypes.c_int, _I, _I, _I,
                                                ctypes.c_int, _P, _P]
         lib.oracle_pack_dim.argtypes = [ctypes.c_int]
-        lib.oracle_pack_send.argtypes = [_P, _P, _I, _I, _I, _I, _P]
-        lib.oracle_unpack.argtypes = [_P, _I, _I, _I, _I, _P, _P]
+        lib.oracle_pack_send.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P]
+        lib.oracle_unpack.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P]
         lib.oracle_unpack_combine.argtypes = [_P, ctypes.c_int, _I, _I, _I, _I, ctypes.c_int,
                                               _P, _P]
         _lib = lib
@@ -87,14 +95,29 @@ def _c(a: np.ndarray, dtype) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=dtype)
 
 
+def _bits(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Contiguous storage patterns of an element array: uint16 for bf16 / f16,
+    uint32 for f32 (float32 values are reinterpreted, not converted)."""
+    if dtype not in _DT:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    a = np.ascontiguousarray(a)
+    if dtype == "f32":
+        if a.dtype == np.float32:
+            return a.view(np.uint32)
+        if a.dtype != np.uint32:
+            raise ValueError("f32 elements must be float32 values or uint32 patterns")
+        return a
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
 def _check(rc: int, what: str) -> None:
     if rc != 0:
         raise ValueError(f"oracle {what}: bad arguments (rc={rc})")
 
 
 def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """bf16 / fp16 bit patterns -> exact fp64 values."""
-    b = _c(bits, np.uint16)
+    """bf16 / fp16 / fp32 elements -> exact fp64 values."""
+    b = _bits(bits, dtype)
     out = np.empty(b.shape, dtype=np.float64)
     _check(_load().oracle_bits_to_f64(b.ctypes.data, _DT[dtype], b.size, out.ctypes.data),
            "bits_to_f64")
@@ -116,8 +139,8 @@ def combine_f64(o: np.ndarray, lse: np.ndarray, base2: bool = False):
 
 
 def lse_combine(outputs: np.ndarray, lses: np.ndarray, dtype: str, base2: bool = False):
-    """outputs [N,B,H,D] bf16/fp16 bits, lses [N,B,H] fp32 -> (y [B,H,D] f64, L [B,H] f64)."""
-    o = _c(outputs, np.uint16)
+    """outputs [N,B,H,D] elements, lses [N,B,H] fp32 -> (y [B,H,D] f64, L [B,H] f64)."""
+    o = _bits(outputs, dtype)
     l = _c(lses, np.float32)
     N, B, H, D = o.shape
     if l.shape != (N, B, H):
@@ -134,7 +157,7 @@ def merge(outputs: np.ndarray, lses: np.ndarray, dtype: str, token_dim: int,
     """Token-major merge (Ascend SFA page, `_merge_dcp_outputs_with_torch`):
     outputs [N,A,C,D] bits, lses [N,A,C] -> y [A,C,D] (token_dim 1) or
     [C,A,D] (token_dim 2) in fp64, and L laid out the same way."""
-    o = _c(outputs, np.uint16)
+    o = _bits(outputs, dtype)
     l = _c(lses, np.float32)
     N, A, C, D = o.shape
     if l.shape != (N, A, C):
@@ -152,10 +175,10 @@ def correct_partial(lses: np.ndarray, rank: int, partial: np.ndarray, dtype: str
                     base2: bool = False):
     """Local step of an LSE all-gather + output reduce-scatter (reading of the
     strategy names on the page "vllm.v1.attention.ops.dcp"): lses [N,B,H] of
-    all shards, rank r's partial [B,H,D] bits -> (partial * normalised weight
-    of shard r [B,H,D] f64, global LSE [B,H] f64)."""
+    all shards, rank r's partial [B,H,D] elements -> (partial * normalised
+    weight of shard r [B,H,D] f64, global LSE [B,H] f64)."""
     l = _c(lses, np.float32)
-    p = _c(partial, np.uint16)
+    p = _bits(partial, dtype)
     N, B, H = l.shape
     if p.shape[:2] != (B, H):
         raise ValueError("partial must be [B,H,D] with lses [N,B,H]")
@@ -172,38 +195,41 @@ def pack_dim(elem_bytes: int) -> int:
     return int(_load().oracle_pack_dim(elem_bytes))
 
 
-def pack_send(out: np.ndarray, lse: np.ndarray, N: int) -> np.ndarray:
-    """out [B,H,D] 16-bit bits, lse [B,H] fp32 -> send [N,B,H/N,D+2] 16-bit bits."""
-    o = _c(out, np.uint16)
+def pack_send(out: np.ndarray, lse: np.ndarray, N: int, dtype: str = "bf16") -> np.ndarray:
+    """out [B,H,D] elements, lse [B,H] fp32 -> send [N,B,H/N,D+P] patterns
+    (uint16 with P = 2 for bf16 / f16, uint32 with P = 1 for f32)."""
+    o = _bits(out, dtype)
     l = _c(lse, np.float32)
     B, H, D = o.shape
     if l.shape != (B, H) or N < 1 or H % N:
         raise ValueError("bad pack_send arguments")
-    send = np.empty((N, B, H // N, D + 2), dtype=np.uint16)
-    _check(_load().oracle_pack_send(o.ctypes.data, l.ctypes.data, N, B, H, D, send.ctypes.data),
-           "pack_send")
+    E = _EB[dtype]
+    send = np.empty((N, B, H // N, D + 4 // E), dtype=o.dtype)
+    _check(_load().oracle_pack_send(o.ctypes.data, l.ctypes.data, N, B, H, D, E,
+                                    send.ctypes.data), "pack_send")
     return send
 
 
-def unpack(recv: np.ndarray, D: int):
-    """recv [N,B,Hl,D+2] -> (outputs [N,B,Hl,D] bits, lses [N,B,Hl] fp32)."""
-    r = _c(recv, np.uint16)
+def unpack(recv: np.ndarray, D: int, dtype: str = "bf16"):
+    """recv [N,B,Hl,D+P] -> (outputs [N,B,Hl,D] patterns, lses [N,B,Hl] fp32)."""
+    r = _bits(recv, dtype)
     N, B, Hl, W = r.shape
-    if W != D + 2:
-        raise ValueError("recv last dim must be D + 2")
-    outs = np.empty((N, B, Hl, D), dtype=np.uint16)
+    E = _EB[dtype]
+    if W != D + 4 // E:
+        raise ValueError("recv last dim must be D + P")
+    outs = np.empty((N, B, Hl, D), dtype=r.dtype)
     lses = np.empty((N, B, Hl), dtype=np.float32)
-    _check(_load().oracle_unpack(r.ctypes.data, N, B, Hl, D, outs.ctypes.data, lses.ctypes.data),
-           "unpack")
+    _check(_load().oracle_unpack(r.ctypes.data, N, B, Hl, D, E, outs.ctypes.data,
+                                 lses.ctypes.data), "unpack")
     return outs, lses
 
 
 def unpack_combine(recv: np.ndarray, D: int, dtype: str, base2: bool = False):
-    """recv [N,B,Hl,D+2] -> (y [B,Hl,D] f64, L [B,Hl] f64)."""
-    r = _c(recv, np.uint16)
+    """recv [N,B,Hl,D+P] -> (y [B,Hl,D] f64, L [B,Hl] f64)."""
+    r = _bits(recv, dtype)
     N, B, Hl, W = r.shape
-    if W != D + 2:
-        raise ValueError("recv last dim must be D + 2")
+    if W != D + 4 // _EB[dtype]:
+        raise ValueError("recv last dim must be D + P")
     y = np.empty((B, Hl, D), dtype=np.float64)
     L = np.empty((B, Hl), dtype=np.float64)
     _check(_load().oracle_unpack_combine(r.ctypes.data, _DT[dtype], N, B, Hl, D, int(base2),

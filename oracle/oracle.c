@@ -17,14 +17,16 @@
  *    `_dcp_a2a_unpack_combine`.
  *
  * Readings where the pages leave a step open:
- *  - P (`_dcp_a2a_lse_pack_dim`) is the number of 16-bit output elements that
- *    hold one fp32 LSE: 4 / sizeof(dtype) = 2 for bf16 and fp16.
+ *  - P (`_dcp_a2a_lse_pack_dim`) is the number of output elements that hold
+ *    one fp32 LSE: 4 / sizeof(dtype) = 2 for bf16 and fp16, 1 for fp32.
  *  - The fp32 LSE occupies the P tail elements in memory order (its four
  *    bytes copied verbatim, little-endian on every target here).
  *  - Plane r of the send buffer holds heads [r*Hl, (r+1)*Hl) in order.
  *  - Arithmetic is fp64 throughout; inputs are converted exactly (every bf16,
  *    fp16 and fp32 value is a double). The combined output is returned
- *    unrounded, in fp64.
+ *    unrounded, in fp64; the caller's result dtype (the input dtype, or the
+ *    fp32 that the page's CPU function promotes bf16 / fp16 products to) only
+ *    changes the tolerance of a comparison, not the oracle.
  *
  * Build: gcc -O2 -std=c11 (no fast-math: the NaN / inf tests must survive).
  */
@@ -33,7 +35,12 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_BF16 = 0, ORACLE_F16 = 1 };
+enum { ORACLE_BF16 = 0, ORACLE_F16 = 1, ORACLE_F32 = 2 };
+
+/* Bytes per stored element of a dtype, or 0 for an unknown dtype. */
+static int64_t elem_bytes(int dtype) {
+    return dtype == ORACLE_BF16 || dtype == ORACLE_F16 ? 2 : dtype == ORACLE_F32 ? 4 : 0;
+}
 
 /* ---- exact storage-to-fp64 conversions ---- */
 
@@ -57,14 +64,29 @@ double oracle_f16_to_f64(uint16_t h) {
     return sign ? -v : v;
 }
 
-static double load_elem(const uint16_t* p, int dtype) {
-    return dtype == ORACLE_BF16 ? oracle_bf16_to_f64(*p) : oracle_f16_to_f64(*p);
+/* IEEE binary32: the bits reinterpreted as a float, then widened (exact). */
+double oracle_f32_to_f64(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Element i of an array of stored elements of the given dtype, as fp64. */
+static double load_elem(const void* base, int64_t i, int dtype) {
+    if (dtype == ORACLE_F32) {
+        uint32_t u;
+        memcpy(&u, (const char*)base + 4 * i, 4);
+        return oracle_f32_to_f64(u);
+    }
+    uint16_t h;
+    memcpy(&h, (const char*)base + 2 * i, 2);
+    return dtype == ORACLE_BF16 ? oracle_bf16_to_f64(h) : oracle_f16_to_f64(h);
 }
 
 /* Array form of the conversions above. Returns 0, or -1 on a bad dtype. */
-int oracle_bits_to_f64(const uint16_t* bits, int dtype, int64_t n, double* out) {
-    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16) return -1;
-    for (int64_t i = 0; i < n; ++i) out[i] = load_elem(&bits[i], dtype);
+int oracle_bits_to_f64(const void* bits, int dtype, int64_t n, double* out) {
+    if (!elem_bytes(dtype)) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = load_elem(bits, i, dtype);
     return 0;
 }
 
@@ -116,15 +138,14 @@ void oracle_combine_f64(const double* o, const double* lse, int64_t N, int64_t R
 
 /* ---- the combine on storage-typed inputs ----
  *
- * outputs : [N][B][H][D] bf16 or fp16 bits;  lses : [N][B][H] fp32
+ * outputs : [N][B][H][D] bf16, fp16 or fp32 bits;  lses : [N][B][H] fp32
  * y : [B][H][D] fp64;  L : [B][H] fp64 or NULL.
  * Converts each row's inputs exactly to fp64, then runs oracle_combine_f64 on
  * that row. Returns 0, or -1 on a bad argument.
  */
-int oracle_lse_combine(const uint16_t* outputs, int dtype, const float* lses, int64_t N,
+int oracle_lse_combine(const void* outputs, int dtype, const float* lses, int64_t N,
                        int64_t B, int64_t H, int64_t D, int base2, double* y, double* L) {
-    if (N < 1 || B < 0 || H < 1 || D < 1 || (dtype != ORACLE_BF16 && dtype != ORACLE_F16))
-        return -1;
+    if (N < 1 || B < 0 || H < 1 || D < 1 || !elem_bytes(dtype)) return -1;
     int64_t R = B * H;
     double* ob = (double*)malloc(sizeof(double) * (size_t)(N * D + N));
     if (!ob) return -2;
@@ -133,7 +154,7 @@ int oracle_lse_combine(const uint16_t* outputs, int dtype, const float* lses, in
         for (int64_t n = 0; n < N; ++n) {
             lb[n] = (double)lses[n * R + r];
             for (int64_t d = 0; d < D; ++d)
-                ob[n * D + d] = load_elem(&outputs[(n * R + r) * D + d], dtype);
+                ob[n * D + d] = load_elem(outputs, (n * R + r) * D + d, dtype);
         }
         oracle_combine_f64(ob, lb, N, 1, D, base2, &y[r * D], L ? &L[r] : 0);
     }
@@ -150,14 +171,13 @@ int oracle_lse_combine(const uint16_t* outputs, int dtype, const float* lses, in
  * `_lse_weighted_combine` (steps sanitise, max, weights, NaN guard, clamped
  * normalisation), and the collective then sums the scaled partials over the
  * ranks, which gives the combine. L is the global LSE of the same function.
- *   lses [N][B][H] fp32; partial [B][H][D] bf16/fp16 bits of rank `rank`
+ *   lses [N][B][H] fp32; partial [B][H][D] bf16/fp16/fp32 bits of rank `rank`
  *   y [B][H][D] fp64 = partial * w_rank / max(S, 1e-10);  L [B][H] or NULL.
  */
-int oracle_correct_partial(const float* lses, int64_t N, int64_t rank, const uint16_t* partial,
+int oracle_correct_partial(const float* lses, int64_t N, int64_t rank, const void* partial,
                            int dtype, int64_t B, int64_t H, int64_t D, int base2, double* y,
                            double* L) {
-    if (N < 1 || rank < 0 || rank >= N || B < 0 || H < 1 || D < 1 ||
-        (dtype != ORACLE_BF16 && dtype != ORACLE_F16))
+    if (N < 1 || rank < 0 || rank >= N || B < 0 || H < 1 || D < 1 || !elem_bytes(dtype))
         return -1;
     const int64_t R = B * H;
     double* l = (double*)malloc(sizeof(double) * (size_t)N);
@@ -182,7 +202,7 @@ int oracle_correct_partial(const float* lses, int64_t N, int64_t rank, const uin
             if (n == rank) wr = w;
         }
         const double wn = wr / (s < 1e-10 ? 1e-10 : s);
-        for (int64_t d = 0; d < D; ++d) y[r * D + d] = load_elem(&partial[r * D + d], dtype) * wn;
+        for (int64_t d = 0; d < D; ++d) y[r * D + d] = load_elem(partial, r * D + d, dtype) * wn;
         if (L) L[r] = (base2 ? log2(s) : log(s)) + m;
     }
     free(l);
@@ -198,10 +218,10 @@ int oracle_correct_partial(const float* lses, int64_t N, int64_t rank, const uin
  * y [A][C][D]; token_dim 2 stores row (a, c) at (c, a), y [C][A][D]. L is laid
  * out the same way ([A][C] or [C][A]). The combine itself is the one above.
  */
-int oracle_merge(const uint16_t* outputs, int dtype, const float* lses, int64_t N, int64_t A,
+int oracle_merge(const void* outputs, int dtype, const float* lses, int64_t N, int64_t A,
                  int64_t C, int64_t D, int token_dim, int base2, double* y, double* L) {
     if (N < 1 || A < 0 || C < 1 || D < 1 || (token_dim != 1 && token_dim != 2) ||
-        (dtype != ORACLE_BF16 && dtype != ORACLE_F16))
+        !elem_bytes(dtype))
         return -1;
     const int64_t R = A * C;
     double* ob = (double*)malloc(sizeof(double) * (size_t)(N * D + N));
@@ -214,7 +234,7 @@ int oracle_merge(const uint16_t* outputs, int dtype, const float* lses, int64_t 
             for (int64_t n = 0; n < N; ++n) {
                 lb[n] = (double)lses[n * R + r];
                 for (int64_t d = 0; d < D; ++d)
-                    ob[n * D + d] = load_elem(&outputs[(n * R + r) * D + d], dtype);
+                    ob[n * D + d] = load_elem(outputs, (n * R + r) * D + d, dtype);
             }
             oracle_combine_f64(ob, lb, N, 1, D, base2, &y[o * D], L ? &L[o] : 0);
         }
@@ -224,59 +244,66 @@ int oracle_merge(const uint16_t* outputs, int dtype, const float* lses, int64_t 
 
 /* ---- pack / unpack (pure byte moves) ----
  *
- * pack:   out [B][H][D] (16-bit elements), lse [B][H] fp32
- *      -> send [N][B][Hl][D+2], Hl = H / N:
+ * Elements are E = 2 (bf16, fp16) or 4 (fp32) bytes wide; P = 4 / E.
+ * pack:   out [B][H][D] elements, lse [B][H] fp32
+ *      -> send [N][B][Hl][D+P] elements, Hl = H / N:
  *         send[r][b][h][0:D]   = out[b][r*Hl + h][0:D]
- *         send[r][b][h][D:D+2] = the 4 bytes of lse[b][r*Hl + h]
- * unpack: recv [N][B][Hl][D+2] -> outputs [N][B][Hl][D], lses [N][B][Hl]
+ *         send[r][b][h][D:D+P] = the 4 bytes of lse[b][r*Hl + h]
+ * unpack: recv [N][B][Hl][D+P] -> outputs [N][B][Hl][D], lses [N][B][Hl]
  *         (plane n of recv is what source rank n sent).
  */
 int oracle_pack_dim(int elem_bytes) { return elem_bytes > 0 && elem_bytes <= 4 ? 4 / elem_bytes : -1; }
 
-int oracle_pack_send(const uint16_t* out, const float* lse, int64_t N, int64_t B, int64_t H,
-                     int64_t D, uint16_t* send) {
-    if (N < 1 || B < 0 || H < 1 || D < 1 || H % N != 0) return -1;
-    const int64_t P = 2, Hl = H / N, W = D + P;
+int oracle_pack_send(const void* out, const float* lse, int64_t N, int64_t B, int64_t H,
+                     int64_t D, int64_t E, void* send) {
+    if (N < 1 || B < 0 || H < 1 || D < 1 || H % N != 0 || (E != 2 && E != 4)) return -1;
+    const int64_t P = 4 / E, Hl = H / N, W = D + P;
+    const char* o = (const char*)out;
+    char* s = (char*)send;
     for (int64_t r = 0; r < N; ++r)
         for (int64_t b = 0; b < B; ++b)
             for (int64_t h = 0; h < Hl; ++h) {
-                int64_t src = b * H + r * Hl + h;
-                uint16_t* dst = &send[((r * B + b) * Hl + h) * W];
-                for (int64_t d = 0; d < D; ++d) dst[d] = out[src * D + d];
-                memcpy(&dst[D], &lse[src], 4);
+                const int64_t src = b * H + r * Hl + h;
+                char* dst = s + ((r * B + b) * Hl + h) * W * E;
+                for (int64_t d = 0; d < D; ++d) memcpy(dst + d * E, o + (src * D + d) * E, (size_t)E);
+                memcpy(dst + D * E, &lse[src], 4);
             }
     return 0;
 }
 
-int oracle_unpack(const uint16_t* recv, int64_t N, int64_t B, int64_t Hl, int64_t D,
-                  uint16_t* outputs, float* lses) {
-    if (N < 1 || B < 0 || Hl < 1 || D < 1) return -1;
-    const int64_t P = 2, W = D + P, R = B * Hl;
+int oracle_unpack(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int64_t E,
+                  void* outputs, float* lses) {
+    if (N < 1 || B < 0 || Hl < 1 || D < 1 || (E != 2 && E != 4)) return -1;
+    const int64_t P = 4 / E, W = D + P, R = B * Hl;
+    const char* rv = (const char*)recv;
+    char* os = (char*)outputs;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t r = 0; r < R; ++r) {
-            const uint16_t* src = &recv[(n * R + r) * W];
-            for (int64_t d = 0; d < D; ++d) outputs[(n * R + r) * D + d] = src[d];
-            memcpy(&lses[n * R + r], &src[D], 4);
+            const char* src = rv + (n * R + r) * W * E;
+            for (int64_t d = 0; d < D; ++d)
+                memcpy(os + ((n * R + r) * D + d) * E, src + d * E, (size_t)E);
+            memcpy(&lses[n * R + r], src + D * E, 4);
         }
     return 0;
 }
 
-/* unpack, then combine: recv [N][B][Hl][D+2] -> y [B][Hl][D] fp64, L [B][Hl]. */
-int oracle_unpack_combine(const uint16_t* recv, int dtype, int64_t N, int64_t B, int64_t Hl,
+/* unpack, then combine: recv [N][B][Hl][D+P] -> y [B][Hl][D] fp64, L [B][Hl]. */
+int oracle_unpack_combine(const void* recv, int dtype, int64_t N, int64_t B, int64_t Hl,
                           int64_t D, int base2, double* y, double* L) {
-    if (N < 1 || B < 0 || Hl < 1 || D < 1 || (dtype != ORACLE_BF16 && dtype != ORACLE_F16))
-        return -1;
-    const int64_t P = 2, W = D + P, R = B * Hl;
+    const int64_t E = elem_bytes(dtype);
+    if (N < 1 || B < 0 || Hl < 1 || D < 1 || !E) return -1;
+    const int64_t P = 4 / E, W = D + P, R = B * Hl;
+    const char* rv = (const char*)recv;
     double* ob = (double*)malloc(sizeof(double) * (size_t)(N * D + N));
     if (!ob) return -2;
     double* lb = ob + N * D;
     for (int64_t r = 0; r < R; ++r) {
         for (int64_t n = 0; n < N; ++n) {
-            const uint16_t* src = &recv[(n * R + r) * W];
+            const char* src = rv + (n * R + r) * W * E;
             float lf;
-            memcpy(&lf, &src[D], 4);
+            memcpy(&lf, src + D * E, 4);
             lb[n] = (double)lf;
-            for (int64_t d = 0; d < D; ++d) ob[n * D + d] = load_elem(&src[d], dtype);
+            for (int64_t d = 0; d < D; ++d) ob[n * D + d] = load_elem(src, d, dtype);
         }
         oracle_combine_f64(ob, lb, N, 1, D, base2, &y[r * D], L ? &L[r] : 0);
     }

@@ -54,6 +54,25 @@ def test_f16_decoding_all_patterns(oracle_mod):
     assert got[0x3C00] == 1.0 and got[0x0001] == 2.0 ** -24 and got[0x7BFF] == 65504.0
 
 
+def test_f32_decoding(oracle_mod):
+    rng = np.random.default_rng(17)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0, 0x80000000, 0x00000001, 0x007FFFFF, 0x00800000, 0x3F800000,
+                        0x7F7FFFFF, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC12345],
+                       dtype=np.uint32)
+    bits = np.concatenate([special, bits])
+    got = oracle_mod.bits_to_f64(bits, "f32")
+    with np.errstate(invalid="ignore"):
+        want = bits.view(np.float32).astype(np.float64)  # numpy's binary32 decoder
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    m = ~np.isnan(want)
+    assert np.array_equal(got[m], want[m])
+    assert got[2] == 2.0 ** -149 and got[5] == 1.0 and got[7] == math.inf
+    # float32 values and their patterns are the same input
+    vals = bits[m].view(np.float32)
+    assert np.array_equal(oracle_mod.bits_to_f64(vals, "f32"), want[m])
+
+
 # ---------------------------------------------------------------- closed forms
 
 def _golden_cases():
@@ -142,6 +161,40 @@ def test_brute_force_sharded_attention(oracle_mod, how, base2, N):
     np.testing.assert_allclose(Lg, full_l * scale, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("N", [2, 5])
+def test_brute_force_fp32_storage(oracle_mod, N):
+    """Sharded attention whose partial outputs and LSEs are stored in fp32 (the
+    fp32-output case of the packed exchange): the storage entry point must
+    reproduce unsharded attention up to the fp32 rounding of its inputs.
+
+    Bound: each partial is off by at most 2^-24 |o| <= 2^-24 M (M = max |v|);
+    each stored LSE by 2^-24 |l|, which moves a normalised weight by at most
+    2 * 2^-24 * max|l| relative; so |y - y*| <= (1 + 4 max|l|) 2^-24 M.
+    """
+    rng = np.random.default_rng(90 + N)
+    B, H, dk, D, L = 2, 3, 8, 6, 41
+    q = rng.normal(size=(B, H, dk))
+    k = rng.normal(size=(L, H, dk)) * 2.0
+    v = rng.normal(size=(L, H, D)) * 3.0
+    sets = np.array_split(rng.permutation(L), N)
+    o = np.zeros((N, B, H, D), dtype=np.float32)
+    lse = np.zeros((N, B, H), dtype=np.float32)
+    full = np.zeros((B, H, D))
+    for b in range(B):
+        for h in range(H):
+            full[b, h] = _attention(q[b, h], k[:, h], v[:, h])[0]
+            for n, sset in enumerate(sets):
+                on, ln = _attention(q[b, h], k[sset, h], v[sset, h])
+                o[n, b, h], lse[n, b, h] = on, ln
+    y, _ = oracle_mod.lse_combine(o, lse, "f32")
+    M = np.abs(v).max()
+    bound = (1 + 4 * np.abs(lse).max()) * 2.0 ** -24 * M
+    assert np.abs(y - full).max() <= bound
+    # the same inputs as raw patterns
+    y2, _ = oracle_mod.lse_combine(o.view(np.uint32), lse, "f32")
+    assert np.array_equal(y, y2)
+
+
 # ---------------------------------------------------------------- library routines
 
 @pytest.mark.parametrize("base2", [False, True])
@@ -219,8 +272,8 @@ def test_invariants(oracle_mod):
 
 
 def test_storage_entry_matches_f64_entry(oracle_mod, synth_mod):
-    """The bf16/fp16 entry point equals the fp64 entry point on decoded inputs."""
-    for dt in ("bf16", "f16"):
+    """The storage-typed entry point equals the fp64 entry point on decoded inputs."""
+    for dt in ("bf16", "f16", "f32"):
         o, l = synth_mod.custom_inputs(3, 5, 4, 16, dtype=dt, seed=2,
                                        special=((0.1, float("nan")), (0.1, float("inf"))))
         y, L = oracle_mod.lse_combine(o, l, dt, base2=(dt == "f16"))
@@ -263,7 +316,30 @@ def test_pack_layout_and_round_trip(oracle_mod, synth_mod):
         assert np.array_equal(lses[r].view(np.uint32), lse_bits[:, r * Hl:(r + 1) * Hl])
 
 
-@pytest.mark.parametrize("dt,base2", [("bf16", False), ("f16", True)])
+def test_pack_layout_f32(oracle_mod, synth_mod):
+    """fp32 elements: P = 1, the tail element is the LSE's own pattern."""
+    N, B, H, D = 2, 3, 6, 5
+    o, _ = synth_mod.custom_inputs(1, B, H, D, dtype="f32", seed=19)
+    o = o[0]
+    assert o.dtype == np.float32
+    rng = np.random.default_rng(4)
+    lse = rng.uniform(-5, 15, size=(B, H)).astype(np.float32)
+    lse.view(np.uint32)[1, 2] = 0x7FC00ABC  # NaN payload moves as bits
+    send = oracle_mod.pack_send(o, lse, N, dtype="f32")
+    Hl = H // N
+    assert send.shape == (N, B, Hl, D + 1) and send.dtype == np.uint32
+    for r in range(N):
+        assert np.array_equal(send[r, :, :, :D], o[:, r * Hl:(r + 1) * Hl].view(np.uint32))
+        assert np.array_equal(send[r, :, :, D], lse.view(np.uint32)[:, r * Hl:(r + 1) * Hl])
+    outs, lses = oracle_mod.unpack(send, D, dtype="f32")
+    for r in range(N):
+        assert np.array_equal(outs[r], o[:, r * Hl:(r + 1) * Hl].view(np.uint32))
+        assert np.array_equal(lses[r].view(np.uint32), lse.view(np.uint32)[:, r * Hl:(r + 1) * Hl])
+    with pytest.raises(ValueError):
+        oracle_mod.unpack(send, D + 1, dtype="f32")
+
+
+@pytest.mark.parametrize("dt,base2", [("bf16", False), ("f16", True), ("f32", False)])
 def test_simulated_all_to_all(oracle_mod, synth_mod, dt, base2):
     """pack on N ranks -> all-to-all -> unpack_combine on rank p equals the
     combine over the N ranks' outputs for rank p's head slice."""
@@ -275,7 +351,7 @@ def test_simulated_all_to_all(oracle_mod, synth_mod, dt, base2):
                                        special=((0.1, float("nan")), (0.05, float("-inf"))))
         outs.append(o[0])
         lses.append(l[0])
-    sends = [oracle_mod.pack_send(outs[r], lses[r], N) for r in range(N)]
+    sends = [oracle_mod.pack_send(outs[r], lses[r], N, dtype=dt) for r in range(N)]
     recvs = oracle_mod.exchange(sends)
     stacked_o = np.stack(outs)   # [N, B, H, D]: rank r's partial output
     stacked_l = np.stack(lses)
@@ -310,38 +386,39 @@ def _page2_merge_layout(o, lse, token_dim):
 
 
 @pytest.mark.parametrize("token_dim", [1, 2])
-def test_merge_matches_page2_layout(oracle_mod, synth_mod, token_dim):
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_merge_matches_page2_layout(oracle_mod, synth_mod, token_dim, dt):
     N, A, C, D = 4, 3, 5, 8
-    o, l = synth_mod.custom_inputs(N, A, C, D, seed=60 + token_dim,
+    o, l = synth_mod.custom_inputs(N, A, C, D, dtype=dt, seed=60 + token_dim,
                                    special=((0.1, float("nan")), (0.1, float("inf")),
                                             (0.1, float("-inf"))))
     l[:, 1, 2] = -np.inf   # an all -inf row
-    y, L = oracle_mod.merge(o, l, "bf16", token_dim)
-    want = _page2_merge_layout(oracle_mod.bits_to_f64(o, "bf16"), l.astype(np.float64), token_dim)
+    y, L = oracle_mod.merge(o, l, dt, token_dim)
+    want = _page2_merge_layout(oracle_mod.bits_to_f64(o, dt), l.astype(np.float64), token_dim)
     assert y.shape == want.shape
     np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-13)
     # the LSE follows the same layout and equals the plain combine's
-    _, Lc = oracle_mod.lse_combine(o, l, "bf16")
+    _, Lc = oracle_mod.lse_combine(o, l, dt)
     assert np.array_equal(L, Lc if token_dim == 1 else Lc.T)
     with pytest.raises(ValueError):
-        oracle_mod.merge(o, l, "bf16", 3)
+        oracle_mod.merge(o, l, dt, 3)
 
 
 # ---------------------------------------------------------------- all-gather + reduce-scatter local step
 
-@pytest.mark.parametrize("base2", [False, True])
-def test_corrected_partials_sum_to_the_combine(oracle_mod, synth_mod, base2):
+@pytest.mark.parametrize("base2,dt", [(False, "bf16"), (True, "bf16"), (False, "f32")])
+def test_corrected_partials_sum_to_the_combine(oracle_mod, synth_mod, base2, dt):
     """The reduce-scatter / all-reduce sums every rank's corrected partial; the
     sum must be the combine of all ranks' partials (and L its global LSE)."""
     N, B, H, D = 5, 6, 4, 16
-    o, l = synth_mod.custom_inputs(N, B, H, D, seed=71,
+    o, l = synth_mod.custom_inputs(N, B, H, D, dtype=dt, seed=71,
                                    special=((0.1, float("nan")), (0.1, float("inf")),
                                             (0.1, float("-inf"))))
     l[:, 0, 0] = -np.inf  # all -inf row: every corrected partial is 0
-    y_ref, L_ref = oracle_mod.lse_combine(o, l, "bf16", base2)
+    y_ref, L_ref = oracle_mod.lse_combine(o, l, dt, base2)
     total = np.zeros_like(y_ref)
     for r in range(N):
-        y, L = oracle_mod.correct_partial(l, r, o[r], "bf16", base2)
+        y, L = oracle_mod.correct_partial(l, r, o[r], dt, base2)
         assert np.array_equal(L, L_ref)
         total += y
     np.testing.assert_allclose(total, y_ref, rtol=1e-12, atol=1e-13)
