@@ -18,6 +18,13 @@ already resident in HBM:
 * ``ag_correct``: lsec_correct_partial of rank 3's [4096, 16, 512] bf16 partial
   with the gathered LSEs [8, 4096, 16] (the local step of an all-gather +
   reduce-scatter combine).
+* ``mla_decode_f32``: lsec_combine of fp32 partials [8, 4096, 16, 512], base 2.
+* ``packed_f32``: the ``packed`` pair on fp32 outputs (packed rows of D + 1
+  fp32 elements, the LSE in the last).
+
+``--out-f32`` asks the combine workloads for an fp32 result from 16-bit
+partials (the promoted dtype of the page's CPU combine) instead of a result in
+the input dtype.
 
 Workloads under 1 GiB are timed cold: a 1 GiB buffer is rewritten before each
 step, outside the timed events. Kernel time comes from HIP events recorded on
@@ -48,16 +55,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def combine_bytes(N, B, H, D, s=2, return_lse=False):
-    return N * B * H * (D * s + 4) + B * H * D * s + (B * H * 4 if return_lse else 0)
+# Algorithmic HBM bytes per launch: every input byte read once, every output
+# byte written once. s / os = element bytes of the partials / of the result;
+# a packed row is D * s + 4 bytes (the LSE takes 4 / s elements).
+def combine_bytes(N, B, H, D, s=2, return_lse=False, os_=None):
+    os_ = s if os_ is None else os_
+    return N * B * H * (D * s + 4) + B * H * D * os_ + (B * H * 4 if return_lse else 0)
 
 
-def unpack_combine_bytes(N, B, Hl, D, s=2, return_lse=False):
-    return N * B * Hl * (D + 2) * s + B * Hl * D * s + (B * Hl * 4 if return_lse else 0)
+def unpack_combine_bytes(N, B, Hl, D, s=2, return_lse=False, os_=None):
+    os_ = s if os_ is None else os_
+    return N * B * Hl * (D * s + 4) + B * Hl * D * os_ + (B * Hl * 4 if return_lse else 0)
 
 
 def pack_bytes(N, B, H, D, s=2):
-    return B * H * (D * s + 4) + B * H * (D + 2) * s
+    return B * H * (D * s + 4) + B * H * (D * s + 4)
 
 
 def source_sha() -> str:
@@ -83,7 +95,7 @@ def load_traffic(workload: str, kernel: str):
 
 # ---------------------------------------------------------------- workloads
 
-def build_workload(name: str, dev):
+def build_workload(name: str, dev, out_f32: bool = False):
     """Inputs on the device, preallocated outputs and the step's kernels."""
     import numpy as np
     import torch
@@ -92,14 +104,24 @@ def build_workload(name: str, dev):
     import synth
 
     w = synth.WORKLOADS[name]
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    s = 4 if w.dtype == "f32" else 2
+    if out_f32 and w.kind != "combine":
+        raise SystemExit("--out-f32 applies to the combine workloads only")
+    odt = torch.float32 if out_f32 else tdt
+    os_ = 4 if odt == torch.float32 else 2
 
     def dev_bits(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+        a = np.ascontiguousarray(a)
+        if s == 4:
+            return torch.from_numpy(a.view(np.float32)).to(dev)
+        return torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
 
     info = {"workload": name, "desc": w.desc, "N": w.N, "B": w.B, "H": w.H, "D": w.D,
             "io_dtype": w.dtype, "lse_base": "2" if w.base2 else "e",
             "return_lse": w.return_lse, "parallelism": "none (one GPU)"}
+    if out_f32:
+        info["result_dtype"] = "f32"
     if w.kind == "correct":
         rank = 3
         o, l = synth.combine_inputs(w)
@@ -108,7 +130,7 @@ def build_workload(name: str, dev):
         del o
         out = torch.empty((w.B, w.H, w.D), dtype=tdt, device=dev)
         rows = w.B * w.H
-        nbytes = w.N * rows * 4 + 2 * rows * w.D * 2
+        nbytes = w.N * rows * 4 + 2 * rows * w.D * s
         kname = f"correct_tiled_kernel ({w.dtype}, N={w.N}, D={w.D}, rank {rank})"
 
         def step():
@@ -121,7 +143,7 @@ def build_workload(name: str, dev):
         o, l = synth.combine_inputs(w)
         og, lg = dev_bits(o), torch.from_numpy(l).to(dev)
         out = torch.empty((w.H, w.B, w.D), dtype=tdt, device=dev)   # token-major [C, A, D]
-        nbytes = combine_bytes(w.N, w.B, w.H, w.D, 2, False)
+        nbytes = combine_bytes(w.N, w.B, w.H, w.D, s, False)
         kname = f"{lsec.lsec_combine_path(w.N, w.B, w.H, w.D)} ({w.dtype}, N={w.N}, D={w.D}, " \
                 f"token-major store)"
 
@@ -137,14 +159,16 @@ def build_workload(name: str, dev):
         o, l = synth.combine_inputs(w)
         log(f"[bench] generated {name} inputs in {time.time() - t0:.1f}s")
         og, lg = dev_bits(o), torch.from_numpy(l).to(dev)
-        out = torch.empty((w.B, w.H, w.D), dtype=tdt, device=dev)
+        out = torch.empty((w.B, w.H, w.D), dtype=odt, device=dev)
         out_lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev) if w.return_lse else None
-        nbytes = combine_bytes(w.N, w.B, w.H, w.D, 2, w.return_lse)
-        kname = f"{lsec.lsec_combine_path(w.N, w.B, w.H, w.D)} ({w.dtype}, N={w.N}, D={w.D})"
+        nbytes = combine_bytes(w.N, w.B, w.H, w.D, s, w.return_lse, os_)
+        path = lsec.lsec_combine_path(w.N, w.B, w.H, w.D, dtype=tdt, out_dtype=odt)
+        res = " -> f32" if out_f32 and s == 2 else ""
+        kname = f"{path} ({w.dtype}{res}, N={w.N}, D={w.D})"
 
         def step():
             lsec.lsec_combine(og, lg, base_e=not w.base2, return_lse=w.return_lse, out=out,
-                              out_lse=out_lse)
+                              out_lse=out_lse, out_dtype=odt)
 
         kernels = [(kname, nbytes, step)]
         host = (o, l)
@@ -154,7 +178,7 @@ def build_workload(name: str, dev):
         outs = [synth.rank_inputs(w, r) for r in range(w.N)]
         a0 = dev_bits(outs[0][0])
         l0 = torch.from_numpy(outs[0][1]).to(dev)
-        send = torch.empty((w.N, w.B, Hl, w.D + 2), dtype=tdt, device=dev)
+        send = torch.empty((w.N, w.B, Hl, w.D + lsec.lsec_pack_dim(tdt)), dtype=tdt, device=dev)
         # rank 0's receive buffer: plane r is what rank r's pack put in its plane 0
         recv = torch.empty_like(send)
         for r in range(w.N):
@@ -172,10 +196,10 @@ def build_workload(name: str, dev):
             lsec.lsec_unpack_combine(recv, base_e=not w.base2, return_lse=True, out=out,
                                      out_lse=out_lse)
 
-        kernels = [("pack_rows_kernel", pack_bytes(w.N, w.B, w.H, w.D), pack),
-                   (f"{lsec.lsec_combine_path(w.N, w.B, Hl, w.D, packed=True)} "
+        kernels = [(f"pack_rows_kernel ({w.dtype})", pack_bytes(w.N, w.B, w.H, w.D, s), pack),
+                   (f"{lsec.lsec_combine_path(w.N, w.B, Hl, w.D, packed=True, dtype=tdt)} "
                     f"({w.dtype}, N={w.N}, D={w.D}, packed rows)",
-                    unpack_combine_bytes(w.N, w.B, Hl, w.D, 2, True), unpack_combine)]
+                    unpack_combine_bytes(w.N, w.B, Hl, w.D, s, True), unpack_combine)]
         host = None
         rows = w.B * Hl
     return w, info, kernels, host, rows
@@ -245,7 +269,7 @@ def cpu_baseline(w, host, threads: int):
     dt = time.perf_counter() - t0
     if errs:
         raise errs[0]
-    nbytes = combine_bytes(w.N, w.B, w.H, w.D, 2, w.return_lse)
+    nbytes = combine_bytes(w.N, w.B, w.H, w.D, 4 if w.dtype == "f32" else 2, w.return_lse)
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
             "rows_per_s": round(w.B * w.H / dt, 1),
@@ -273,7 +297,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large_batch",
                     choices=["large_batch", "mla_decode", "fp16_base2", "packed", "small",
-                             "merge_heads", "ag_correct"])
+                             "merge_heads", "ag_correct", "mla_decode_f32", "packed_f32"])
+    ap.add_argument("--out-f32", action="store_true",
+                    help="combine workloads: fp32 result from 16-bit partials")
     ap.add_argument("--flush-mib", type=int, default=-1,
                     help="cache flush before each step (default: 1024 MiB if the step's "
                          "working set is under 1 GiB, else none)")
@@ -301,7 +327,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
 
-    w, info, kernels, host, rows = build_workload(args.workload, dev)
+    w, info, kernels, host, rows = build_workload(args.workload, dev, args.out_f32)
     step_bytes = sum(b for _, b, _ in kernels)
     flush_mib = args.flush_mib if args.flush_mib >= 0 else (1024 if step_bytes < (1 << 30) else 0)
     log(f"[bench] {args.workload}: {step_bytes / 1e6:.1f} MB per step, warmup {args.warmup}, "
@@ -320,7 +346,8 @@ def main():
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "bytes_per_launch": kbytes, "avg_launch_us": round(k_ms * 1e3, 3),
-                "traffic": load_traffic(args.workload, kname)}
+                "traffic": load_traffic(args.workload + ("_f32out" if args.out_f32 else ""),
+                                        kname)}
     kernel_detail = [{"kernel": n, "bytes": b, "avg_us": round(per_kernel_ms[i] / args.steps * 1e3, 3),
                       "GB/s": round(b / (per_kernel_ms[i] / args.steps * 1e-3) / 1e9, 1)}
                      for i, (n, b, _) in enumerate(kernels)]

@@ -19,18 +19,22 @@
  *  - The caller owns and allocates every buffer; the library never allocates,
  *    frees or synchronises. Work is enqueued on `stream` (a hipStream_t; NULL
  *    means the null stream) and the call returns at once.
- *  - Elements of `outputs`, `out`, `send`, `recv` are 16-bit (bf16 or fp16,
- *    selected by `dtype`) and must be 2-byte aligned; LSE arrays are fp32 and
- *    must be 4-byte aligned. Faster kernels are chosen when the buffers are
- *    16-byte aligned (separate layout) or 4-byte aligned (packed layout) and D
- *    is a multiple of 8 no larger than 2048; other cases take a general path
+ *  - Elements of `outputs`, `partial`, `send`, `recv` are bf16, fp16 or fp32
+ *    (selected by `dtype`) and must be aligned to their size; LSE arrays are
+ *    fp32 and must be 4-byte aligned. `out` holds elements of the input dtype,
+ *    or fp32 when the combining calls (lsec_combine, lsec_merge,
+ *    lsec_unpack_combine, lsec_correct_partial) get `dtype | LSEC_OUT_FP32`.
+ *    Faster kernels are chosen when the buffers are 16-byte aligned (separate
+ *    layout) or 4-byte aligned (packed layout) and a row is whole 16-byte
+ *    chunks that fit 256 lanes (D a multiple of 8 up to 2048 for 16-bit
+ *    elements, of 4 up to 1024 for fp32); other cases take a general path
  *    with the same results.
  *  - Every argument is checked before anything is enqueued; on an error
  *    nothing is enqueued and a status other than LSEC_OK is returned. A
  *    pointer may be NULL only when the array it names has no elements.
  *  - Input and output buffers must not overlap.
- *  - Arithmetic: fp32 accumulation; outputs are rounded to the input dtype
- *    (round to nearest even); the global LSE is fp32. NaN and +-inf shard LSEs
+ *  - Arithmetic: fp32 accumulation; 16-bit outputs are rounded to nearest
+ *    even from fp32; the global LSE is fp32. NaN and +-inf shard LSEs
  *    count as -inf; a row whose shard LSEs are all non-finite yields a zero
  *    output and a -inf global LSE. Zero-weight shards are still multiplied, so
  *    a NaN in any shard's output propagates to the combined output.
@@ -50,7 +54,7 @@ enum {
     LSEC_ERR_NULL = 1,         /* a required pointer is NULL */
     LSEC_ERR_SHAPE = 2,        /* N < 1, B < 0, H < 1, D < 1, or a size overflows int64 */
     LSEC_ERR_DIVISIBILITY = 3, /* H is not a multiple of N (pack_send) */
-    LSEC_ERR_DTYPE = 4,        /* dtype is neither LSEC_BF16 nor LSEC_FP16 */
+    LSEC_ERR_DTYPE = 4,        /* unknown dtype, or LSEC_OUT_FP32 on a layout-only call */
     LSEC_ERR_ALIGNMENT = 5,    /* a pointer is not aligned to its element size */
     LSEC_ERR_BASE = 6,         /* base is neither LSEC_BASE_E nor LSEC_BASE_2 */
     LSEC_ERR_LAUNCH = 7,       /* the HIP runtime rejected the kernel launch */
@@ -59,16 +63,26 @@ enum {
 };
 
 /* Element types of the attention outputs. */
-enum { LSEC_BF16 = 0, LSEC_FP16 = 1 };
+enum { LSEC_BF16 = 0, LSEC_FP16 = 1, LSEC_FP32 = 2 };
+
+/*
+ * OR'ed into the `dtype` of a combining call: write the result in fp32 even
+ * for bf16 / fp16 inputs. The page's CPU function `_lse_weighted_combine`
+ * multiplies the 16-bit outputs by fp32 weights, so its result is promoted to
+ * fp32; without the flag the result is rounded back to the input dtype (what
+ * the exchange paths return). fp32 inputs always give fp32 results.
+ */
+enum { LSEC_OUT_FP32 = 256 };
 
 /* Base of the log-sum-exp values (`is_lse_base_on_e` true / false). */
 enum { LSEC_BASE_E = 0, LSEC_BASE_2 = 1 };
 
 /*
  * lsec_pack_dim -- number of output-dtype elements that carry one fp32 LSE in
- * a packed row: 4 / sizeof(element) = 2 for bf16 and fp16. Returns -1 for an
- * unknown dtype. (`_dcp_a2a_lse_pack_dim`; its body is not on the page, this
- * is the reading that makes the packed row D + P elements wide.)
+ * a packed row: P = 4 / sizeof(element) = 2 for bf16 and fp16, 1 for fp32.
+ * Returns -1 for an unknown dtype (the LSEC_OUT_FP32 flag included).
+ * (`_dcp_a2a_lse_pack_dim`; its body is not on the page, this is the reading
+ * that makes the packed row D + P elements wide.)
  */
 int lsec_pack_dim(int dtype);
 
@@ -76,7 +90,8 @@ int lsec_pack_dim(int dtype);
  * lsec_combine -- `_lse_weighted_combine`.
  *   outputs : [N, B, H, D] dtype   partial attention output of each shard
  *   lses    : [N, B, H]    fp32    per-shard log-sum-exp, base `base`
- *   out     : [B, H, D]    dtype   combined output (written)
+ *   out     : [B, H, D]    dtype   combined output (written; fp32 with
+ *                                  LSEC_OUT_FP32 or fp32 inputs)
  *   out_lse : [B, H]       fp32    global LSE (written), or NULL to skip it
  *                                  (`return_lse` false)
  * Per (b, h) row: l'_n = -inf if l_n is NaN or +-inf; m = max_n l'_n (0 if
@@ -115,7 +130,8 @@ int lsec_merge(const void* outputs, const float* lses, int64_t N, int64_t A, int
  *   lses    : [N, B, H]  fp32   every shard's LSE (after the all-gather)
  *   rank    : r in [0, N)       this rank's shard
  *   partial : [B, H, D]  dtype  this rank's partial output
- *   out     : [B, H, D]  dtype  partial * w_r / max(S, 1e-10) (written)
+ *   out     : [B, H, D]  dtype  partial * w_r / max(S, 1e-10) (written; fp32
+ *                               with LSEC_OUT_FP32, e.g. to sum in fp32)
  *   out_lse : [B, H]     fp32   global LSE (written), or NULL
  * with w_r and S exactly as in lsec_combine, so the sum of `out` over the N
  * ranks (what the reduce-scatter / all-reduce computes) is the combine.
@@ -129,11 +145,13 @@ int lsec_correct_partial(const float* lses, int64_t N, int64_t rank, const void*
  * lsec_pack_send -- `_dcp_a2a_pack_send`.
  *   attn_out : [B, H, D]           dtype  this rank's partial attention output
  *   attn_lse : [B, H]              fp32   its log-sum-exp
- *   send     : [N, B, H/N, D + 2]  dtype  packed send buffer (written)
+ *   send     : [N, B, H/N, D + P]  dtype  packed send buffer (written),
+ *                                         P = lsec_pack_dim(dtype)
  * Plane r holds heads [r*H/N, (r+1)*H/N): the chunk an all-to-all delivers to
- * rank r. In each packed row, elements 0..D-1 are the output row, and elements
- * D and D+1 hold the four bytes of the fp32 LSE in memory order (element D =
- * bits 0..15, element D+1 = bits 16..31). Pure bit moves (NaN payloads kept).
+ * rank r. In each packed row, elements 0..D-1 are the output row, and the P
+ * tail elements hold the four bytes of the fp32 LSE in memory order (16-bit:
+ * element D = bits 0..15, element D+1 = bits 16..31; fp32: element D is the
+ * LSE's own pattern). Pure bit moves (NaN payloads kept).
  * Errors: NULL, SHAPE, DIVISIBILITY (H % N != 0), DTYPE, ALIGNMENT, LAUNCH.
  */
 int lsec_pack_send(const void* attn_out, const float* attn_lse, int64_t N, int64_t B, int64_t H,
@@ -141,8 +159,9 @@ int lsec_pack_send(const void* attn_out, const float* attn_lse, int64_t N, int64
 
 /*
  * lsec_unpack_combine -- `_dcp_a2a_unpack_combine`.
- *   recv    : [N, B, Hl, D + 2] dtype  packed planes; plane n came from rank n
- *   out     : [B, Hl, D]        dtype  combined output (written)
+ *   recv    : [N, B, Hl, D + P] dtype  packed planes; plane n came from rank n
+ *   out     : [B, Hl, D]        dtype  combined output (written; fp32 with
+ *                                      LSEC_OUT_FP32 or fp32 inputs)
  *   out_lse : [B, Hl]           fp32   global LSE (written), or NULL
  * Equivalent to lsec_unpack followed by lsec_combine with H = Hl, in one pass.
  * Errors: NULL, SHAPE, DTYPE, BASE, ALIGNMENT, LAUNCH.
@@ -152,7 +171,7 @@ int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int6
 
 /*
  * lsec_unpack -- the layout half of the receive step.
- *   recv    : [N, B, Hl, D + 2] dtype
+ *   recv    : [N, B, Hl, D + P] dtype
  *   outputs : [N, B, Hl, D]     dtype  (written)
  *   lses    : [N, B, Hl]        fp32   (written; the tail bits reinterpreted)
  * Pure bit moves; the inverse of lsec_pack_send's per-row layout.
@@ -164,13 +183,14 @@ int lsec_unpack(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, i
 /*
  * lsec_combine_path -- diagnostics: the name of the kernel lsec_combine
  * (packed == 0, H = heads) or lsec_unpack_combine (packed != 0, H = heads per
- * rank, Hl) launches for these sizes, given whether the buffers meet the fast
- * alignment (aligned_buffers != 0: 16 bytes for outputs / out, 4 bytes for
- * recv). Returns a static string such as "combine_tiled_kernel S=16",
- * "combine_rows_kernel" or "combine_elems_kernel"; "none" when the sizes
- * launch nothing or are invalid. Touches no GPU state.
+ * rank, Hl) launches for these sizes and `dtype` (as passed to those calls),
+ * given whether the buffers meet the fast alignment (aligned_buffers != 0: 16
+ * bytes for outputs / out, 4 bytes for recv). Returns a static string such as
+ * "combine_tiled_kernel S=16", "combine_rows_kernel" or
+ * "combine_elems_kernel"; "none" when the arguments launch nothing or are
+ * invalid. Touches no GPU state.
  */
-const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int packed,
+const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int dtype, int packed,
                               int aligned_buffers);
 
 /* Human-readable text for a status code (static storage; never NULL). */

@@ -12,7 +12,8 @@ Entry points (same names as the C ABI):
   "vllm.v1.attention.ops.dcp_alltoall": ``[N,B,H,D]`` + ``[N,B,H]`` ->
   ``[B,H,D]`` (+ ``[B,H]``).
 * ``lsec_pack_send(attn_out, attn_lse, N)`` -- that page's
-  ``_dcp_a2a_pack_send``: ``[B,H,D]`` + ``[B,H]`` -> ``[N,B,H/N,D+2]``.
+  ``_dcp_a2a_pack_send``: ``[B,H,D]`` + ``[B,H]`` -> ``[N,B,H/N,D+P]``
+  (P = 2 for bf16 / fp16, 1 for fp32).
 * ``lsec_unpack_combine(recv, ...)`` -- ``_dcp_a2a_unpack_combine``.
 * ``lsec_unpack(recv)`` -- the layout half of the receive step.
 * ``lsec_pack_dim(dtype)`` -- ``_dcp_a2a_lse_pack_dim``.
@@ -27,6 +28,11 @@ Entry points (same names as the C ABI):
 
 ``lse_weighted_combine`` and ``merge_dcp_outputs`` keep the argument names of
 the pages' functions.
+
+Element dtypes: bfloat16, float16 and float32. The combining calls take
+``out_dtype=torch.float32`` to return an fp32 result from 16-bit inputs (the
+dtype the page's CPU function promotes to); by default the result has the
+input dtype.
 """
 from __future__ import annotations
 
@@ -50,10 +56,12 @@ LSEC_ERR_TOKEN_DIM = 8
 LSEC_ERR_RANK = 9
 LSEC_BF16 = 0
 LSEC_FP16 = 1
+LSEC_FP32 = 2
+LSEC_OUT_FP32 = 256
 LSEC_BASE_E = 0
 LSEC_BASE_2 = 1
 
-_DTYPES = {torch.bfloat16: LSEC_BF16, torch.float16: LSEC_FP16}
+_DTYPES = {torch.bfloat16: LSEC_BF16, torch.float16: LSEC_FP16, torch.float32: LSEC_FP32}
 _VALUE_ERRORS = (LSEC_ERR_SHAPE, LSEC_ERR_DIVISIBILITY, LSEC_ERR_DTYPE, LSEC_ERR_BASE,
                  LSEC_ERR_RANK)
 
@@ -96,7 +104,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_correct_partial.restype = I
     lib.lsec_correct_partial.argtypes = [P, I64, I64, P, I64, I64, I64, I, I, P, P, P]
     lib.lsec_combine_path.restype = ctypes.c_char_p
-    lib.lsec_combine_path.argtypes = [I64, I64, I64, I64, I, I]
+    lib.lsec_combine_path.argtypes = [I64, I64, I64, I64, I, I, I]
     _lib = lib
     return lib
 
@@ -117,7 +125,18 @@ def _dtype_code(t: torch.Tensor) -> int:
     try:
         return _DTYPES[t.dtype]
     except KeyError:
-        raise ValueError(f"unsupported dtype {t.dtype}: bfloat16 or float16 only") from None
+        raise ValueError(f"unsupported dtype {t.dtype}: bfloat16, float16 or float32 only") \
+            from None
+
+
+def _result_dtype(t: torch.Tensor, out_dtype) -> tuple[int, torch.dtype]:
+    """(dtype code for a combining call, torch dtype of its result)."""
+    code = _dtype_code(t)
+    if out_dtype is None or out_dtype == t.dtype:
+        return code, t.dtype
+    if out_dtype == torch.float32:
+        return code | LSEC_OUT_FP32, torch.float32
+    raise ValueError(f"out_dtype must be None, {t.dtype} or torch.float32, got {out_dtype}")
 
 
 def _check_dev(*ts: torch.Tensor) -> torch.device:
@@ -143,7 +162,7 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 
 
 def lsec_pack_dim(dtype: torch.dtype) -> int:
-    """Output-dtype elements per packed fp32 LSE (2 for bf16 / fp16)."""
+    """Output-dtype elements per packed fp32 LSE (2 for bf16 / fp16, 1 for fp32)."""
     code = _DTYPES.get(dtype, -1)
     r = load_library().lsec_pack_dim(code)
     if r < 0:
@@ -153,11 +172,12 @@ def lsec_pack_dim(dtype: torch.dtype) -> int:
 
 def lsec_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
                  return_lse: bool = False, out: torch.Tensor | None = None,
-                 out_lse: torch.Tensor | None = None, stream=None):
+                 out_lse: torch.Tensor | None = None, stream=None, out_dtype=None):
     """Combine partial outputs [N,B,H,D] by their LSEs [N,B,H] (fp32).
 
-    Returns the combined [B,H,D] output in the input dtype, and the [B,H] fp32
-    global LSE when ``return_lse``. ``base_e`` False means base-2 LSEs.
+    Returns the combined [B,H,D] output in the input dtype (or ``out_dtype``
+    torch.float32), and the [B,H] fp32 global LSE when ``return_lse``.
+    ``base_e`` False means base-2 LSEs.
     """
     lib = load_library()
     if outputs.dim() != 4 or lses.dim() != 3 or tuple(lses.shape) != tuple(outputs.shape[:3]):
@@ -165,14 +185,14 @@ def lsec_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
                          f"{tuple(outputs.shape)} and {tuple(lses.shape)}")
     if lses.dtype != torch.float32:
         raise ValueError("lses must be float32")
-    dt = _dtype_code(outputs)
+    dt, rdt = _result_dtype(outputs, out_dtype)
     N, B, H, D = outputs.shape
     dev = _check_dev(outputs, lses)
     if out is None:
-        out = torch.empty((B, H, D), dtype=outputs.dtype, device=dev)
+        out = torch.empty((B, H, D), dtype=rdt, device=dev)
     if return_lse and out_lse is None:
         out_lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    _check_out(out, (B, H, D), outputs.dtype, dev)
+    _check_out(out, (B, H, D), rdt, dev)
     if return_lse:
         _check_out(out_lse, (B, H), torch.float32, dev)
     st = lib.lsec_combine(_ptr(outputs), _ptr(lses), N, B, H, D, dt,
@@ -184,7 +204,7 @@ def lsec_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
 
 def lsec_merge(outputs: torch.Tensor, lses: torch.Tensor, token_dim: int, base_e: bool = True,
                return_lse: bool = False, out: torch.Tensor | None = None,
-               out_lse: torch.Tensor | None = None, stream=None):
+               out_lse: torch.Tensor | None = None, stream=None, out_dtype=None):
     """Token-major merge of received planes outputs [N,A,C,D] + lses [N,A,C].
 
     token_dim 1: tokens are A -> [A,C,D] (+ [A,C]); token_dim 2: tokens are C
@@ -198,15 +218,15 @@ def lsec_merge(outputs: torch.Tensor, lses: torch.Tensor, token_dim: int, base_e
         raise RuntimeError(f"merge token_dim must be 1 or 2, got {token_dim}")
     if lses.dtype != torch.float32:
         raise ValueError("lses must be float32")
-    dt = _dtype_code(outputs)
+    dt, rdt = _result_dtype(outputs, out_dtype)
     N, A, C, D = outputs.shape
     dev = _check_dev(outputs, lses)
     rows = (A, C) if token_dim == 1 else (C, A)
     if out is None:
-        out = torch.empty(rows + (D,), dtype=outputs.dtype, device=dev)
+        out = torch.empty(rows + (D,), dtype=rdt, device=dev)
     if return_lse and out_lse is None:
         out_lse = torch.empty(rows, dtype=torch.float32, device=dev)
-    _check_out(out, rows + (D,), outputs.dtype, dev)
+    _check_out(out, rows + (D,), rdt, dev)
     if return_lse:
         _check_out(out_lse, rows, torch.float32, dev)
     st = lib.lsec_merge(_ptr(outputs), _ptr(lses), N, A, C, D, int(token_dim), dt,
@@ -219,7 +239,7 @@ def lsec_merge(outputs: torch.Tensor, lses: torch.Tensor, token_dim: int, base_e
 def lsec_correct_partial(lses: torch.Tensor, rank: int, partial: torch.Tensor,
                          base_e: bool = True, return_lse: bool = False,
                          out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None,
-                         stream=None):
+                         stream=None, out_dtype=None):
     """Scale rank ``rank``'s partial output [B,H,D] by its normalised LSE weight
     among the gathered LSEs [N,B,H] (fp32); summing the results over the N
     ranks (a reduce-scatter or all-reduce) gives the combine."""
@@ -229,15 +249,15 @@ def lsec_correct_partial(lses: torch.Tensor, rank: int, partial: torch.Tensor,
                          f"and {tuple(partial.shape)}")
     if lses.dtype != torch.float32:
         raise ValueError("lses must be float32")
-    dt = _dtype_code(partial)
+    dt, rdt = _result_dtype(partial, out_dtype)
     N, B, H = lses.shape
     D = partial.shape[2]
     dev = _check_dev(lses, partial)
     if out is None:
-        out = torch.empty((B, H, D), dtype=partial.dtype, device=dev)
+        out = torch.empty((B, H, D), dtype=rdt, device=dev)
     if return_lse and out_lse is None:
         out_lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    _check_out(out, (B, H, D), partial.dtype, dev)
+    _check_out(out, (B, H, D), rdt, dev)
     if return_lse:
         _check_out(out_lse, (B, H), torch.float32, dev)
     st = lib.lsec_correct_partial(_ptr(lses), N, int(rank), _ptr(partial), B, H, D, dt,
@@ -255,7 +275,7 @@ def merge_dcp_outputs(output_recv: torch.Tensor, lse_recv: torch.Tensor, token_d
 
 def lsec_pack_send(attn_out: torch.Tensor, attn_lse: torch.Tensor, N: int,
                    send: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Pack [B,H,D] output + [B,H] fp32 LSE into the [N,B,H/N,D+2] send buffer."""
+    """Pack [B,H,D] output + [B,H] fp32 LSE into the [N,B,H/N,D+P] send buffer."""
     lib = load_library()
     if attn_out.dim() != 3 or attn_lse.dim() != 2 or \
             tuple(attn_lse.shape) != tuple(attn_out.shape[:2]):
@@ -280,7 +300,7 @@ def lsec_pack_send(attn_out: torch.Tensor, attn_lse: torch.Tensor, N: int,
 
 def _recv_dims(recv: torch.Tensor):
     if recv.dim() != 4:
-        raise ValueError(f"expected recv [N,B,Hl,D+2], got {tuple(recv.shape)}")
+        raise ValueError(f"expected recv [N,B,Hl,D+P], got {tuple(recv.shape)}")
     N, B, Hl, W = recv.shape
     D = W - lsec_pack_dim(recv.dtype)
     if D < 1:
@@ -290,17 +310,17 @@ def _recv_dims(recv: torch.Tensor):
 
 def lsec_unpack_combine(recv: torch.Tensor, base_e: bool = True, return_lse: bool = False,
                         out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None,
-                        stream=None):
-    """Combine the N packed planes of recv [N,B,Hl,D+2] -> [B,Hl,D] (+ [B,Hl])."""
+                        stream=None, out_dtype=None):
+    """Combine the N packed planes of recv [N,B,Hl,D+P] -> [B,Hl,D] (+ [B,Hl])."""
     lib = load_library()
-    dt = _dtype_code(recv)
+    dt, rdt = _result_dtype(recv, out_dtype)
     N, B, Hl, D = _recv_dims(recv)
     dev = _check_dev(recv)
     if out is None:
-        out = torch.empty((B, Hl, D), dtype=recv.dtype, device=dev)
+        out = torch.empty((B, Hl, D), dtype=rdt, device=dev)
     if return_lse and out_lse is None:
         out_lse = torch.empty((B, Hl), dtype=torch.float32, device=dev)
-    _check_out(out, (B, Hl, D), recv.dtype, dev)
+    _check_out(out, (B, Hl, D), rdt, dev)
     if return_lse:
         _check_out(out_lse, (B, Hl), torch.float32, dev)
     st = lib.lsec_unpack_combine(_ptr(recv), N, B, Hl, D, dt,
@@ -312,7 +332,7 @@ def lsec_unpack_combine(recv: torch.Tensor, base_e: bool = True, return_lse: boo
 
 def lsec_unpack(recv: torch.Tensor, outputs: torch.Tensor | None = None,
                 lses: torch.Tensor | None = None, stream=None):
-    """Split recv [N,B,Hl,D+2] into outputs [N,B,Hl,D] and fp32 lses [N,B,Hl]."""
+    """Split recv [N,B,Hl,D+P] into outputs [N,B,Hl,D] and fp32 lses [N,B,Hl]."""
     lib = load_library()
     dt = _dtype_code(recv)
     N, B, Hl, D = _recv_dims(recv)
@@ -330,16 +350,24 @@ def lsec_unpack(recv: torch.Tensor, outputs: torch.Tensor | None = None,
 
 
 def lsec_combine_path(N: int, B: int, H: int, D: int, packed: bool = False,
-                      aligned: bool = True) -> str:
+                      aligned: bool = True, dtype: torch.dtype = torch.bfloat16,
+                      out_dtype=None) -> str:
     """Name of the kernel a combine of these sizes launches (diagnostics)."""
-    return load_library().lsec_combine_path(N, B, H, D, int(packed), int(aligned)).decode()
+    code = _DTYPES.get(dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {dtype}")
+    if out_dtype == torch.float32 and dtype != torch.float32:
+        code |= LSEC_OUT_FP32
+    return load_library().lsec_combine_path(N, B, H, D, code, int(packed), int(aligned)).decode()
 
 
 def lse_weighted_combine(outputs: torch.Tensor, lses: torch.Tensor, return_lse: bool = False,
                          is_lse_base_on_e: bool = True):
     """The page's ``_lse_weighted_combine(outputs, lses, return_lse, is_lse_base_on_e)``,
-    computed by the HIP kernel (output in the input dtype)."""
-    return lsec_combine(outputs, lses, base_e=is_lse_base_on_e, return_lse=return_lse)
+    computed by the HIP kernel. Like the page's function it returns fp32 for
+    every input dtype: bf16 / fp16 outputs times fp32 weights promote to fp32."""
+    return lsec_combine(outputs, lses, base_e=is_lse_base_on_e, return_lse=return_lse,
+                        out_dtype=torch.float32)
 
 
 def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:

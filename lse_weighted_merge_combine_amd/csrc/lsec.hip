@@ -6,16 +6,15 @@
 // lsec_unpack). The argument contract of each entry point is in lsec.h.
 //
 // Design. The combine is a streaming reduction: per (token, head) row it reads
-// N planes of D 16-bit values and writes one, so it is bound by HBM bandwidth
-// at about one FMA per byte. It runs on plain VALU (no MFMA): a group of D/8
-// consecutive lanes owns a row, each lane moving 16 bytes (8 elements) per
-// plane. Every lane loads the row's N LSE values itself (the loads are
-// broadcasts inside the group) and computes the weights in registers, so the
-// kernels need no LDS and no cross-lane traffic. All N plane loads of a lane
-// are issued before the first is consumed, which keeps N x 16 B per lane in
-// flight. Packed rows are D + 2 elements wide, so in the packed layout a row
-// start is only 4-byte aligned; gfx950 serves dwordx4 accesses at 4-byte
-// alignment, so the packed kernels read and write those rows directly.
+// N planes of D values and writes one, so it is bound by HBM bandwidth at
+// about one FMA per byte. It runs on plain VALU (no MFMA): a group of
+// consecutive lanes owns a row, each lane moving one 16-byte chunk (8 bf16 /
+// fp16 or 4 fp32 elements) per plane. The weights are computed in registers
+// from the row's N LSE values, so the kernels need no LDS. Packed rows are
+// D + P elements wide (P = 2 for 16-bit elements, 1 for fp32), so in the
+// packed layout a row start is only 4-byte aligned; gfx950 serves dwordx4
+// accesses at 4-byte alignment, so the packed kernels read and write those
+// rows directly.
 //
 // Build with -Xclang -target-feature -Xclang -packed-fp32-ops and without
 // fast-math (the NaN / infinity tests must survive).
@@ -27,8 +26,7 @@
 
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kFastMaxD = 2048;  // D / 8 lanes per row must fit one block
+constexpr int kBlock = 256;  // a row's lanes (D / elements per chunk) must fit one block
 
 // ---------------------------------------------------------------- helpers
 
@@ -68,7 +66,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// The same four dwords at 4-byte alignment (packed rows start every D + 2
+// The same four dwords at 4-byte alignment (packed rows start every D + P
 // elements, i.e. on 4-byte boundaries).
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -76,21 +74,21 @@ typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 // streaming accesses are non-temporal (the `nt` cache policy); on MI355X plain
 // loads cost 12-15 % at 2 GB per call and up to 40 % on small cold calls.
 // 16-byte load / store at a 16-byte aligned address.
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+__device__ __forceinline__ u32x4 ld16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) {
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 // 16-byte load / store at a 4-byte aligned address (packed rows): gfx950
-// serves dwordx4 at dword alignment. Packed rows (D + 2 elements) are written
-// in pieces that straddle cache lines, so those stores keep the default
-// policy: L2 assembles whole lines before they go to HBM (non-temporal stores
-// here measured about 10 % slower).
-__device__ __forceinline__ u32x4 ld16_a4(const uint16_t* p) {
+// serves dwordx4 at dword alignment. Packed rows are written in pieces that
+// straddle cache lines, so those stores keep the default policy: L2 assembles
+// whole lines before they go to HBM (non-temporal stores here measured about
+// 10 % slower).
+__device__ __forceinline__ u32x4 ld16_a4(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(p));
 }
-__device__ __forceinline__ void st16_a4(uint16_t* p, u32x4 v) {
+__device__ __forceinline__ void st16_a4(void* p, u32x4 v) {
     *reinterpret_cast<u32x4_a4*>(p) = static_cast<u32x4_a4>(v);
 }
 // The fp32 LSE in the tail of a packed row (same cache lines as the row).
@@ -99,12 +97,17 @@ __device__ __forceinline__ float ld_tail(const void* p) {
 }
 __device__ __forceinline__ void st_tail(void* p, float v) { *reinterpret_cast<float*>(p) = v; }
 
-// Element type: decode two packed 16-bit values, encode two floats (RNE).
+// Element types. T is the storage word; kEpc elements make one 16-byte chunk;
+// kPack elements carry one fp32 LSE in a packed row. dec / enc convert to and
+// from fp32 (round to nearest even).
 template <int DT>
 struct Elem;
 
 template <>
 struct Elem<LSEC_BF16> {
+    using T = uint16_t;
+    static constexpr int kEpc = 8;
+    static constexpr int kPack = 2;
     __device__ static __forceinline__ void dec2(uint32_t u, float& a, float& b) {
         a = __uint_as_float(u << 16);
         b = __uint_as_float(u & 0xffff0000u);
@@ -123,6 +126,9 @@ struct Elem<LSEC_BF16> {
 
 template <>
 struct Elem<LSEC_FP16> {
+    using T = uint16_t;
+    static constexpr int kEpc = 8;
+    static constexpr int kPack = 2;
     __device__ static __forceinline__ void dec2(uint32_t u, float& a, float& b) {
         f16x2 h = __builtin_bit_cast(f16x2, u);
         a = (float)h.x;
@@ -138,6 +144,15 @@ struct Elem<LSEC_FP16> {
     __device__ static __forceinline__ uint16_t enc1(float a) {
         return __builtin_bit_cast(uint16_t, (_Float16)a);
     }
+};
+
+template <>
+struct Elem<LSEC_FP32> {
+    using T = uint32_t;
+    static constexpr int kEpc = 4;
+    static constexpr int kPack = 1;
+    __device__ static __forceinline__ float dec1(uint32_t u) { return __uint_as_float(u); }
+    __device__ static __forceinline__ uint32_t enc1(float a) { return __float_as_uint(a); }
 };
 
 // NaN and +-inf shard LSEs count as -inf (exponent field all ones).
@@ -159,43 +174,82 @@ __device__ __forceinline__ float global_lse(float s, float m, float inv_scale) {
     return log2f(s) * inv_scale + m;
 }
 
-// Accumulate one 16-byte chunk (8 elements) scaled by w into acc[8].
+// Accumulate one 16-byte chunk (kEpc elements) scaled by w into acc.
 template <int DT>
-__device__ __forceinline__ void fma8(u32x4 v, float w, float (&acc)[8]) {
-    float a, b;
-    Elem<DT>::dec2(v.x, a, b);
-    acc[0] = fmaf(a, w, acc[0]);
-    acc[1] = fmaf(b, w, acc[1]);
-    Elem<DT>::dec2(v.y, a, b);
-    acc[2] = fmaf(a, w, acc[2]);
-    acc[3] = fmaf(b, w, acc[3]);
-    Elem<DT>::dec2(v.z, a, b);
-    acc[4] = fmaf(a, w, acc[4]);
-    acc[5] = fmaf(b, w, acc[5]);
-    Elem<DT>::dec2(v.w, a, b);
-    acc[6] = fmaf(a, w, acc[6]);
-    acc[7] = fmaf(b, w, acc[7]);
+__device__ __forceinline__ void fma_chunk(u32x4 v, float w, float (&acc)[Elem<DT>::kEpc]) {
+    if constexpr (DT == LSEC_FP32) {
+        acc[0] = fmaf(__uint_as_float(v.x), w, acc[0]);
+        acc[1] = fmaf(__uint_as_float(v.y), w, acc[1]);
+        acc[2] = fmaf(__uint_as_float(v.z), w, acc[2]);
+        acc[3] = fmaf(__uint_as_float(v.w), w, acc[3]);
+    } else {
+        float a, b;
+        Elem<DT>::dec2(v.x, a, b);
+        acc[0] = fmaf(a, w, acc[0]);
+        acc[1] = fmaf(b, w, acc[1]);
+        Elem<DT>::dec2(v.y, a, b);
+        acc[2] = fmaf(a, w, acc[2]);
+        acc[3] = fmaf(b, w, acc[3]);
+        Elem<DT>::dec2(v.z, a, b);
+        acc[4] = fmaf(a, w, acc[4]);
+        acc[5] = fmaf(b, w, acc[5]);
+        Elem<DT>::dec2(v.w, a, b);
+        acc[6] = fmaf(a, w, acc[6]);
+        acc[7] = fmaf(b, w, acc[7]);
+    }
 }
 
-template <int DT>
-__device__ __forceinline__ u32x4 enc8(const float (&acc)[8]) {
-    u32x4 r = {Elem<DT>::enc2(acc[0], acc[1]), Elem<DT>::enc2(acc[2], acc[3]),
-               Elem<DT>::enc2(acc[4], acc[5]), Elem<DT>::enc2(acc[6], acc[7])};
+__device__ __forceinline__ u32x4 f32_chunk(float a, float b, float c, float d) {
+    u32x4 r = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
     return r;
+}
+
+// Store a lane's kEpc results at element `idx` of `out` (16-byte aligned): in
+// the input dtype, or as fp32 when `out_f32` (16-bit inputs then write two
+// 16-byte chunks). fp32 inputs always give fp32 results.
+template <int DT>
+__device__ __forceinline__ void store_chunk(void* out, uint64_t idx,
+                                            const float (&acc)[Elem<DT>::kEpc], int out_f32) {
+    if constexpr (DT == LSEC_FP32) {
+        st16(static_cast<float*>(out) + idx, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
+    } else {
+        if (out_f32) {
+            float* p = static_cast<float*>(out) + idx;
+            st16(p, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
+            st16(p + 4, f32_chunk(acc[4], acc[5], acc[6], acc[7]));
+        } else {
+            u32x4 r = {Elem<DT>::enc2(acc[0], acc[1]), Elem<DT>::enc2(acc[2], acc[3]),
+                       Elem<DT>::enc2(acc[4], acc[5]), Elem<DT>::enc2(acc[6], acc[7])};
+            st16(static_cast<uint16_t*>(out) + idx, r);
+        }
+    }
+}
+
+// One result element (general paths).
+template <int DT>
+__device__ __forceinline__ void store_elem(void* out, int64_t idx, float v, int out_f32) {
+    if (DT == LSEC_FP32 || out_f32)
+        static_cast<float*>(out)[idx] = v;
+    else
+        static_cast<typename Elem<DT>::T*>(out)[idx] = Elem<DT>::enc1(v);
 }
 
 // ---------------------------------------------------------------- combine (fast path)
 //
 // Row r of plane n starts at element n * plane + r * stride of `src`.
 // Separate layout (lsec_combine): stride = D, plane = rows * D, LSE n of row r
-// at lse[n * rows + r]. Packed layout (lsec_unpack_combine): stride = D + 2,
-// plane = rows * (D + 2), LSE = the fp32 in elements D, D+1 of the row.
-// Launch: rows_per_block = kBlock / (D/8) rows per block, lane group D/8.
+// at lse[n * rows + r]. Packed layout (lsec_unpack_combine): stride = D + P,
+// plane = rows * (D + P), LSE = the fp32 in elements D .. D+P-1 of the row.
+// Launch: a lane group of g = D / kEpc lanes owns a row; rows_per_block =
+// kBlock / g. Every lane loads the row's N LSE values itself (broadcasts
+// within the group) and issues all N chunk loads before it uses the first.
 template <int DT, int NT, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
-    const uint16_t* __restrict__ src, const float* __restrict__ lse, int n_rt, uint32_t rows,
-    FastDiv g, uint32_t rows_per_block, int64_t stride, int64_t plane, int D, float scale,
-    float inv_scale, uint16_t* __restrict__ out, float* __restrict__ out_lse, OutMap om) {
+    const typename Elem<DT>::T* __restrict__ src, const float* __restrict__ lse, int n_rt,
+    uint32_t rows, FastDiv g, uint32_t rows_per_block, int64_t stride, int64_t plane, int D,
+    float scale, float inv_scale, void* __restrict__ out, int out_f32,
+    float* __restrict__ out_lse, OutMap om) {
+    constexpr int E = Elem<DT>::kEpc;
     const uint32_t t = threadIdx.x;
     const uint32_t rib = fdiv(t, g);
     const uint32_t lane = t - rib * g.d;
@@ -203,8 +257,8 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     const uint32_t row = blockIdx.x * rows_per_block + rib;
     if (row >= rows) return;
     const int N = NT > 0 ? NT : n_rt;
-    const uint16_t* rp = src + int64_t(row) * stride;
-    const uint16_t* cp = rp + lane * 8;
+    const typename Elem<DT>::T* rp = src + int64_t(row) * stride;
+    const typename Elem<DT>::T* cp = rp + lane * E;
 
     auto load_lse = [&](int n) -> float {
         if (PACKED) return ld_tail(rp + n * plane + D);
@@ -215,7 +269,9 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
         return ld16(cp + n * plane);
     };
 
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = 0.0f;
     float m, s;
     if constexpr (NT > 0) {
         float l[NT];
@@ -243,7 +299,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
         }
         const float inv = 1.0f / fmaxf(s, 1e-10f);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) fma8<DT>(v[n], w[n] * inv, acc);
+        for (int n = 0; n < NT; ++n) fma_chunk<DT>(v[n], w[n] * inv, acc);
     } else {
         m = -__builtin_inff();
         for (int n = 0; n < N; ++n) m = fmaxf(m, sanitize(load_lse(n)));
@@ -263,30 +319,30 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                if (n0 + k < N) fma8<DT>(v[k], w[k], acc);
+                if (n0 + k < N) fma_chunk<DT>(v[k], w[k], acc);
         }
     }
     const uint32_t orow = out_row(row, om);
-    st16(out + int64_t(orow) * D + lane * 8, enc8<DT>(acc));
+    store_chunk<DT>(out, uint64_t(orow) * D + lane * E, acc, out_f32);
     if (out_lse != nullptr && lane == 0) out_lse[orow] = global_lse(s, m, inv_scale);
 }
 
 // ---------------------------------------------------------------- combine (tiled path)
 //
-// For D in {128, 256, 512} and N in {2, 4, 8, 16}. A row is owned by G = D/8
-// lanes (16 bytes each). A block of 256 threads covers S slots of 256/G
-// consecutive rows, so per plane it reads one contiguous run of S*256/G rows
-// (32 KB at S = 8). The planes are walked in order, PG at a time: each lane has
-// PG*S 16-byte loads in flight and a block keeps few DRAM pages open. On
-// MI355X this streams markedly faster than issuing all N planes of one row at
-// once, which spreads every block over N distant pages.
+// For D in {128, 256, 512} and N in {2, 4, 8, 16}. A row is owned by
+// G = D / kEpc lanes (16 bytes each). A block of 256 threads covers S slots of
+// 256/G consecutive rows, so per plane it reads one contiguous run of
+// S*256/G rows (32 KB at S = 8). The planes are walked in order, PG at a time:
+// each lane has PG*S 16-byte loads in flight and a block keeps few DRAM pages
+// open. On MI355X this streams markedly faster than issuing all N planes of
+// one row at once, which spreads every block over N distant pages.
 //
 // Weights: lane j of each 16-lane DPP row loads shard j's LSE for its row
 // (j < N; the 16-lane segments of a row group hold identical copies). Max and
 // sum are 16-lane DPP reductions; during the sweep the weight of plane n comes
-// from lane n of the segment (a lane shuffle, or readlane when one wave is one
-// row). The global LSE is written before the sweep so nothing but the weights
-// stays live through it.
+// from lane n of the segment (a lane shuffle, or readlane when a wave holds
+// one row or part of one). The global LSE is written before the sweep so
+// nothing but the weights stays live through it.
 //
 // Addresses: plane n starts at n * plane_bytes (uniform, scalar registers);
 // a lane's chunk sits at a 32-bit byte offset inside the plane. The host
@@ -314,21 +370,20 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// Value held by lane n of this lane's 16-lane segment (n uniform).
+// Value held by lane n of this lane's 16-lane segment (n uniform). With
+// G >= 64 every lane of a wave belongs to the same row, and each 16-lane
+// segment holds the same values, so lane n of the wave is lane n of the
+// segment.
 template <int G>
 __device__ __forceinline__ float lane_value(float v, int n) {
-    if constexpr (G == 64)
+    if constexpr (G >= 64)
         return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), n));
     else
         return __shfl(v, n, 16);
 }
 
-__device__ __forceinline__ u32x4 ld16_nt_at(const char* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ u32x4 ld16_a4_at(const char* p) {
-    return ld16_a4(reinterpret_cast<const uint16_t*>(p));
-}
+__device__ __forceinline__ u32x4 ld16_nt_at(const char* p) { return ld16(p); }
+__device__ __forceinline__ u32x4 ld16_a4_at(const char* p) { return ld16_a4(p); }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
 // XCD i mod 8). Remap so that each XCD takes chunks of kXcdChunk consecutive
@@ -352,13 +407,16 @@ constexpr int tiled_pg() {
 
 template <int DT, int NT, int G, int S, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
-    const uint16_t* src, const float* __restrict__ lse, uint32_t rows, uint32_t stride,
-    uint64_t plane_bytes, float scale, float inv_scale, uint16_t* __restrict__ out,
+    const void* src, const float* __restrict__ lse, uint32_t rows, uint32_t stride,
+    uint64_t plane_bytes, float scale, float inv_scale, void* __restrict__ out, int out_f32,
     float* __restrict__ out_lse, OutMap om) {
+    constexpr int E = Elem<DT>::kEpc;
+    constexpr uint32_t ES = sizeof(typename Elem<DT>::T);
     constexpr int RPS = kBlock / G;  // rows per slot
-    constexpr int D = G * 8;
+    constexpr int D = G * E;
     constexpr int PG = tiled_pg<S, NT>();
     static_assert(NT % PG == 0, "plane groups must tile N");
+    static_assert(RPS >= 1 && kBlock % G == 0, "a row's lanes must fit the block");
     const uint32_t t = threadIdx.x;
     const uint32_t rib = t / G;
     const uint32_t lane = t % G;
@@ -372,7 +430,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     for (int s = 0; s < S; ++s) {
         row[s] = row0 + s * RPS + rib;
         const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
-        off[s] = (rc * stride + lane * 8) * 2;
+        off[s] = (rc * stride + lane * E) * ES;
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -380,7 +438,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
         float l = -__builtin_inff();
         if (j < NT) {
             if (PACKED)
-                l = ld_tail(base + j * plane_bytes + (rc * stride + D) * 2);
+                l = ld_tail(base + j * plane_bytes + (rc * stride + D) * ES);
             else
                 l = lse[j * rows + rc];
         }
@@ -413,11 +471,11 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
             out_lse[out_row(row[s], om)] = global_lse(sum, m, inv_scale);
     }
 
-    float acc[S][8];
+    float acc[S][E];
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[s][k] = 0.0f;
+        for (int k = 0; k < E; ++k) acc[s][k] = 0.0f;
 #pragma unroll 1
     for (int n0 = 0; n0 < NT; n0 += PG) {
         if (n0 > 0) load_group(n0);
@@ -425,32 +483,37 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
 #pragma unroll
         for (int p = 0; p < PG; ++p)
 #pragma unroll
-            for (int s = 0; s < S; ++s) fma8<DT>(v[p][s], lane_value<G>(lw[s], n0 + p), acc[s]);
+            for (int s = 0; s < S; ++s) fma_chunk<DT>(v[p][s], lane_value<G>(lw[s], n0 + p), acc[s]);
     }
 #pragma unroll
     for (int s = 0; s < S; ++s)
-        if (row[s] < rows) st16(out + uint64_t(out_row(row[s], om)) * D + lane * 8, enc8<DT>(acc[s]));
+        if (row[s] < rows) store_chunk<DT>(out, uint64_t(out_row(row[s], om)) * D + lane * E, acc[s], out_f32);
 }
 
 // ---------------------------------------------------------------- combine (general path)
 //
-// Any D, 2-byte aligned buffers. One thread per (row, element); each thread
-// recomputes its row's weights. Packed rows read the LSE as two 16-bit halves.
+// Any D, element-aligned buffers. One thread per (row, element); each thread
+// recomputes its row's weights. Packed rows read the LSE from its P tail
+// elements (two 16-bit halves, or one fp32 element).
 template <int DT, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
-    const uint16_t* __restrict__ src, const float* __restrict__ lse, int N, int64_t rows,
-    int64_t stride, int64_t plane, int64_t D, float scale, float inv_scale,
-    uint16_t* __restrict__ out, float* __restrict__ out_lse, int64_t map_a, int64_t map_c) {
+    const typename Elem<DT>::T* __restrict__ src, const float* __restrict__ lse, int N,
+    int64_t rows, int64_t stride, int64_t plane, int64_t D, float scale, float inv_scale,
+    void* __restrict__ out, int out_f32, float* __restrict__ out_lse, int64_t map_a,
+    int64_t map_c) {
     const int64_t total = rows * D;
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
          i += int64_t(gridDim.x) * kBlock) {
         const int64_t row = i / D;
         const int64_t d = i - row * D;
-        const uint16_t* rp = src + row * stride;
+        const typename Elem<DT>::T* rp = src + row * stride;
         auto load_lse = [&](int n) -> float {
             if (PACKED) {
-                const uint16_t* q = rp + n * plane + D;
-                return __uint_as_float(uint32_t(q[0]) | (uint32_t(q[1]) << 16));
+                const typename Elem<DT>::T* q = rp + n * plane + D;
+                if constexpr (Elem<DT>::kPack == 1)
+                    return __uint_as_float(q[0]);
+                else
+                    return __uint_as_float(uint32_t(q[0]) | (uint32_t(q[1]) << 16));
             }
             return lse[int64_t(n) * rows + row];
         };
@@ -466,7 +529,7 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
             acc = fmaf(Elem<DT>::dec1(rp[n * plane + d]), w, acc);
         }
         const int64_t orow = map_a == 0 ? row : (row % map_c) * map_a + row / map_c;
-        out[orow * D + d] = Elem<DT>::enc1(acc);
+        store_elem<DT>(out, orow * D + d, acc, out_f32);
         if (out_lse != nullptr && d == 0) out_lse[orow] = global_lse(s, m, inv_scale);
     }
 }
@@ -478,15 +541,16 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
 // shard r's normalised weight; summing the scaled partials over the ranks
 // gives the combine. Per row: the same sanitise / max / weight / clamped
 // normalisation as the combine, then one plane read and one written.
-// Tiled path for D in {128, 256, 512} and N <= 16: G = D/8 lanes per row, S
-// row slots per lane, lane j of each 16-lane DPP row loads shard j's LSE.
+// Tiled path for D in {128, 256, 512} and N <= 16: G = D / kEpc lanes per row,
+// S row slots per lane, lane j of each 16-lane DPP row loads shard j's LSE.
 template <int DT, int G, int S>
 __global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
-    const float* __restrict__ lse, int N, int rank, const uint16_t* __restrict__ part,
-    uint32_t rows, float scale, float inv_scale, uint16_t* __restrict__ out,
+    const float* __restrict__ lse, int N, int rank, const typename Elem<DT>::T* __restrict__ part,
+    uint32_t rows, float scale, float inv_scale, void* __restrict__ out, int out_f32,
     float* __restrict__ out_lse) {
+    constexpr int E = Elem<DT>::kEpc;
     constexpr int RPS = kBlock / G;
-    constexpr int D = G * 8;
+    constexpr int D = G * E;
     const uint32_t t = threadIdx.x;
     const uint32_t rib = t / G;
     const uint32_t lane = t % G;
@@ -504,7 +568,7 @@ __global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
-        v[s] = ld16(part + uint64_t(rc) * D + lane * 8);
+        v[s] = ld16(part + uint64_t(rc) * D + lane * E);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -516,19 +580,21 @@ __global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
         const float sum = row16_sum(w);
         const float wr = lane_value<G>(w * (1.0f / fmaxf(sum, 1e-10f)), rank);
         if (row[s] < rows) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            fma8<DT>(v[s], wr, acc);
-            st16(out + uint64_t(row[s]) * D + lane * 8, enc8<DT>(acc));
+            float acc[E];
+#pragma unroll
+            for (int k = 0; k < E; ++k) acc[k] = 0.0f;
+            fma_chunk<DT>(v[s], wr, acc);
+            store_chunk<DT>(out, uint64_t(row[s]) * D + lane * E, acc, out_f32);
             if (out_lse != nullptr && lane == 0) out_lse[row[s]] = global_lse(sum, m, inv_scale);
         }
     }
 }
 
-// General path: any N, any D, 2-byte alignment; one thread per element.
+// General path: any N, any D, element alignment; one thread per element.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void correct_elems_kernel(
-    const float* __restrict__ lse, int N, int rank, const uint16_t* __restrict__ part, int64_t rows,
-    int64_t D, float scale, float inv_scale, uint16_t* __restrict__ out,
+    const float* __restrict__ lse, int N, int rank, const typename Elem<DT>::T* __restrict__ part,
+    int64_t rows, int64_t D, float scale, float inv_scale, void* __restrict__ out, int out_f32,
     float* __restrict__ out_lse) {
     const int64_t total = rows * D;
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
@@ -545,7 +611,7 @@ __global__ __launch_bounds__(kBlock) void correct_elems_kernel(
             if (n == rank) wr = w;
         }
         wr *= 1.0f / fmaxf(s, 1e-10f);
-        out[i] = Elem<DT>::enc1(fmaf(Elem<DT>::dec1(part[i]), wr, 0.0f));
+        store_elem<DT>(out, i, fmaf(Elem<DT>::dec1(part[i]), wr, 0.0f), out_f32);
         if (out_lse != nullptr && d == 0) out_lse[row] = global_lse(s, m, inv_scale);
     }
 }
@@ -553,15 +619,20 @@ __global__ __launch_bounds__(kBlock) void correct_elems_kernel(
 // ---------------------------------------------------------------- pack (fast path)
 //
 // Send row s = (r * B + b) * Hl + hl takes attention-output row
-// src = b * H + r * Hl + hl: D elements, then the fp32 LSE's 32 bits.
-// A lane group of D/8 lanes owns a send row; each group handles kPackRows
-// send rows (spaced one block-width apart) with all their loads in flight.
+// src = b * H + r * Hl + hl: D elements, then the fp32 LSE's 32 bits in the P
+// tail elements. T is the element word (2 or 4 bytes); the kernel moves bits
+// only. A lane group of D / (16 / sizeof(T)) lanes owns a send row; each group
+// handles kPackRows send rows (spaced one block-width apart) with all their
+// loads in flight.
 constexpr int kPackRows = 4;
 
+template <typename T>
 __global__ __launch_bounds__(kBlock) void pack_rows_kernel(
-    const uint16_t* __restrict__ in, const float* __restrict__ lse, uint32_t send_rows,
-    FastDiv g, uint32_t rows_per_block, FastDiv hl_div, FastDiv b_div, uint32_t H, int D,
-    uint16_t* __restrict__ send) {
+    const T* __restrict__ in, const float* __restrict__ lse, uint32_t send_rows, FastDiv g,
+    uint32_t rows_per_block, FastDiv hl_div, FastDiv b_div, uint32_t H, int D,
+    T* __restrict__ send) {
+    constexpr int E = 16 / sizeof(T);
+    constexpr int P = 4 / sizeof(T);
     const uint32_t t = threadIdx.x;
     const uint32_t rib = fdiv(t, g);
     const uint32_t lane = t - rib * g.d;
@@ -579,24 +650,26 @@ __global__ __launch_bounds__(kBlock) void pack_rows_kernel(
         const uint32_t r = fdiv(rb, b_div);
         const uint32_t b = rb - r * b_div.d;
         const uint32_t src = b * H + r * hl_div.d + hl;
-        v[k] = ld16(in + int64_t(src) * D + lane * 8);
+        v[k] = ld16(in + int64_t(src) * D + lane * E);
         lv[k] = lse[src];
     }
 #pragma unroll
     for (int k = 0; k < kPackRows; ++k) {
         if (sr[k] < send_rows) {
-            uint16_t* dp = send + int64_t(sr[k]) * (D + 2);
-            st16_a4(dp + lane * 8, v[k]);
+            T* dp = send + int64_t(sr[k]) * (D + P);
+            st16_a4(dp + lane * E, v[k]);
             if (lane == 0) st_tail(dp + D, lv[k]);
         }
     }
 }
 
 // ---------------------------------------------------------------- pack (general path)
+template <typename T>
 __global__ __launch_bounds__(kBlock) void pack_elems_kernel(
-    const uint16_t* __restrict__ in, const float* __restrict__ lse, int64_t B, int64_t H,
-    int64_t Hl, int64_t D, int64_t total, uint16_t* __restrict__ send) {
-    const int64_t W = D + 2;
+    const T* __restrict__ in, const float* __restrict__ lse, int64_t B, int64_t H, int64_t Hl,
+    int64_t D, int64_t total, T* __restrict__ send) {
+    constexpr int P = 4 / sizeof(T);
+    const int64_t W = D + P;
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
          i += int64_t(gridDim.x) * kBlock) {
         const int64_t s = i / W;
@@ -606,36 +679,44 @@ __global__ __launch_bounds__(kBlock) void pack_elems_kernel(
         const int64_t r = rb / B;
         const int64_t b = rb - r * B;
         const int64_t src = b * H + r * Hl + hl;
-        uint16_t v;
+        T v;
         if (d < D) {
             v = in[src * D + d];
         } else {
             const uint32_t bits = __float_as_uint(lse[src]);
-            v = uint16_t(d == D ? (bits & 0xffffu) : (bits >> 16));
+            if constexpr (P == 1)
+                v = T(bits);
+            else
+                v = T(d == D ? (bits & 0xffffu) : (bits >> 16));
         }
         send[i] = v;
     }
 }
 
 // ---------------------------------------------------------------- unpack
+template <typename T>
 __global__ __launch_bounds__(kBlock) void unpack_rows_kernel(
-    const uint16_t* __restrict__ recv, uint32_t total_rows, FastDiv g, uint32_t rows_per_block,
-    int D, uint16_t* __restrict__ outs, float* __restrict__ lses) {
+    const T* __restrict__ recv, uint32_t total_rows, FastDiv g, uint32_t rows_per_block, int D,
+    T* __restrict__ outs, float* __restrict__ lses) {
+    constexpr int E = 16 / sizeof(T);
+    constexpr int P = 4 / sizeof(T);
     const uint32_t t = threadIdx.x;
     const uint32_t rib = fdiv(t, g);
     const uint32_t lane = t - rib * g.d;
     if (rib >= rows_per_block) return;
     const uint32_t q = blockIdx.x * rows_per_block + rib;
     if (q >= total_rows) return;
-    const uint16_t* sp = recv + int64_t(q) * (D + 2);
-    st16(outs + int64_t(q) * D + lane * 8, ld16_a4(sp + lane * 8));
+    const T* sp = recv + int64_t(q) * (D + P);
+    st16(outs + int64_t(q) * D + lane * E, ld16_a4(sp + lane * E));
     if (lane == 0) lses[q] = ld_tail(sp + D);
 }
 
+template <typename T>
 __global__ __launch_bounds__(kBlock) void unpack_elems_kernel(
-    const uint16_t* __restrict__ recv, int64_t total_rows, int64_t D,
-    uint16_t* __restrict__ outs, float* __restrict__ lses) {
-    const int64_t W = D + 2;
+    const T* __restrict__ recv, int64_t total_rows, int64_t D, T* __restrict__ outs,
+    float* __restrict__ lses) {
+    constexpr int P = 4 / sizeof(T);
+    const int64_t W = D + P;
     const int64_t total = total_rows * W;
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
          i += int64_t(gridDim.x) * kBlock) {
@@ -644,7 +725,10 @@ __global__ __launch_bounds__(kBlock) void unpack_elems_kernel(
         if (d < D) {
             outs[q * D + d] = recv[i];
         } else if (d == D) {
-            lses[q] = __uint_as_float(uint32_t(recv[i]) | (uint32_t(recv[i + 1]) << 16));
+            if constexpr (P == 1)
+                lses[q] = __uint_as_float(uint32_t(recv[i]));
+            else
+                lses[q] = __uint_as_float(uint32_t(recv[i]) | (uint32_t(recv[i + 1]) << 16));
         }
     }
 }
@@ -666,32 +750,61 @@ unsigned general_grid(int64_t total) {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? LSEC_OK : LSEC_ERR_LAUNCH; }
 
-bool fast_d(int64_t D) { return D % 8 == 0 && D <= kFastMaxD; }
+// A `dtype` argument: the element type of the inputs, optionally with
+// LSEC_OUT_FP32 (fp32 results from 16-bit inputs; fp32 inputs always give
+// fp32 results). `esize` / `out_esize` are element sizes in bytes.
+struct Dtype {
+    int in;
+    int out_f32;
+    int64_t esize, out_esize;
+};
+
+bool parse_dtype(int code, bool allow_out_flag, Dtype* d) {
+    const int in = code & ~LSEC_OUT_FP32;
+    const bool flag = (code & LSEC_OUT_FP32) != 0;
+    if (in != LSEC_BF16 && in != LSEC_FP16 && in != LSEC_FP32) return false;
+    if (flag && !allow_out_flag) return false;
+    d->in = in;
+    d->out_f32 = (flag || in == LSEC_FP32) ? 1 : 0;
+    d->esize = in == LSEC_FP32 ? 4 : 2;
+    d->out_esize = d->out_f32 ? 4 : 2;
+    return true;
+}
+
+// Fast kernels take D as whole 16-byte chunks, one lane each, within a block.
+bool fast_d(int64_t D, int64_t esize) {
+    const int64_t epc = 16 / esize;
+    return D % epc == 0 && D / epc <= kBlock;
+}
 
 template <int DT, int NT, bool PACKED>
-void launch_combine_rows(const uint16_t* src, const float* lse, int N, uint32_t rows, int D,
-                         float scale, float inv_scale, uint16_t* out, float* out_lse,
+void launch_combine_rows(const void* src, const float* lse, int N, uint32_t rows, int D,
+                         float scale, float inv_scale, void* out, int out_f32, float* out_lse,
                          OutMap om, hipStream_t st) {
-    const uint32_t g = uint32_t(D / 8);
+    const uint32_t g = uint32_t(D / Elem<DT>::kEpc);
     const uint32_t rpb = kBlock / g;
     const unsigned blocks = (rows + rpb - 1) / rpb;
-    const int64_t stride = PACKED ? D + 2 : D;
+    const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
     combine_rows_kernel<DT, NT, PACKED><<<blocks, kBlock, 0, st>>>(
-        src, lse, N, rows, make_fastdiv(g), rpb, stride, int64_t(rows) * stride, D, scale,
-        inv_scale, out, out_lse, om);
+        static_cast<const typename Elem<DT>::T*>(src), lse, N, rows, make_fastdiv(g), rpb, stride,
+        int64_t(rows) * stride, D, scale, inv_scale, out, out_f32, out_lse, om);
 }
 
 template <int DT, bool PACKED>
-void dispatch_n(const uint16_t* src, const float* lse, int N, uint32_t rows, int D, float scale,
-                float inv_scale, uint16_t* out, float* out_lse, OutMap om, hipStream_t st) {
+void dispatch_n(const void* src, const float* lse, int N, uint32_t rows, int D, float scale,
+                float inv_scale, void* out, int out_f32, float* out_lse, OutMap om,
+                hipStream_t st) {
+#define LSEC_ROWS(NV) \
+    launch_combine_rows<DT, NV, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_f32, out_lse, om, st)
     switch (N) {
-        case 1: launch_combine_rows<DT, 1, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
-        case 2: launch_combine_rows<DT, 2, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
-        case 4: launch_combine_rows<DT, 4, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
-        case 8: launch_combine_rows<DT, 8, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
-        case 16: launch_combine_rows<DT, 16, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
-        default: launch_combine_rows<DT, 0, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_lse, om, st); break;
+        case 1: LSEC_ROWS(1); break;
+        case 2: LSEC_ROWS(2); break;
+        case 4: LSEC_ROWS(4); break;
+        case 8: LSEC_ROWS(8); break;
+        case 16: LSEC_ROWS(16); break;
+        default: LSEC_ROWS(0); break;
     }
+#undef LSEC_ROWS
 }
 
 // Tiled path: the largest S in {16, 8, 4, 2, 1} that still gives at least
@@ -704,15 +817,27 @@ void dispatch_n(const uint16_t* src, const float* lse, int N, uint32_t rows, int
 constexpr uint64_t kTiledMinBlocks = 2048;
 constexpr uint64_t kTiledMinBlocksN16 = 1024;
 
+struct TiledArgs {
+    const void* src;
+    const float* lse;
+    uint32_t rows, stride;
+    uint64_t plane_bytes;
+    float scale, inv_scale;
+    void* out;
+    int out_f32;
+    float* out_lse;
+    OutMap om;
+    hipStream_t st;
+};
+
 template <int DT, int NT, int G, bool PACKED>
-void launch_tiled_s(int S, const uint16_t* src, const float* lse, uint32_t rows, uint32_t stride,
-                    uint64_t plane_bytes, float scale, float inv_scale, uint16_t* out,
-                    float* out_lse, OutMap om, hipStream_t st) {
+void launch_tiled_s(int S, const TiledArgs& a) {
     constexpr uint32_t RPS = kBlock / G;
-    const unsigned blocks = (rows + RPS * S - 1) / (RPS * S);
+    const unsigned blocks = (a.rows + RPS * S - 1) / (RPS * S);
 #define LSEC_TILED(SV)                                                                         \
-    combine_tiled_kernel<DT, NT, G, SV, PACKED><<<blocks, kBlock, 0, st>>>(                    \
-        src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om)
+    combine_tiled_kernel<DT, NT, G, SV, PACKED><<<blocks, kBlock, 0, a.st>>>(                  \
+        a.src, a.lse, a.rows, a.stride, a.plane_bytes, a.scale, a.inv_scale, a.out, a.out_f32, \
+        a.out_lse, a.om)
     switch (S) {
         case 16: LSEC_TILED(16); break;
         case 8: LSEC_TILED(8); break;
@@ -724,49 +849,46 @@ void launch_tiled_s(int S, const uint16_t* src, const float* lse, uint32_t rows,
 }
 
 template <int DT, int G, bool PACKED>
-void launch_tiled_n(int N, int S, const uint16_t* src, const float* lse, uint32_t rows,
-                    uint32_t stride, uint64_t plane_bytes, float scale, float inv_scale,
-                    uint16_t* out, float* out_lse, OutMap om, hipStream_t st) {
+void launch_tiled_n(int N, int S, const TiledArgs& a) {
     switch (N) {
-        case 2: launch_tiled_s<DT, 2, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
-        case 4: launch_tiled_s<DT, 4, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
-        case 8: launch_tiled_s<DT, 8, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
-        default: launch_tiled_s<DT, 16, G, PACKED>(S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
+        case 2: launch_tiled_s<DT, 2, G, PACKED>(S, a); break;
+        case 4: launch_tiled_s<DT, 4, G, PACKED>(S, a); break;
+        case 8: launch_tiled_s<DT, 8, G, PACKED>(S, a); break;
+        default: launch_tiled_s<DT, 16, G, PACKED>(S, a); break;
     }
 }
 
 template <int DT, bool PACKED>
-void launch_tiled(int N, int S, uint32_t rows, int D, const uint16_t* src, const float* lse,
-                  float scale, float inv_scale, uint16_t* out, float* out_lse, OutMap om,
-                  hipStream_t st) {
-    const uint32_t stride = uint32_t(PACKED ? D + 2 : D);
-    const uint64_t plane_bytes = uint64_t(rows) * stride * 2;
+void launch_tiled(int N, int S, int D, const TiledArgs& a) {
+    constexpr int E = Elem<DT>::kEpc;
     switch (D) {
-        case 128: launch_tiled_n<DT, 16, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
-        case 256: launch_tiled_n<DT, 32, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
-        default: launch_tiled_n<DT, 64, PACKED>(N, S, src, lse, rows, stride, plane_bytes, scale, inv_scale, out, out_lse, om, st); break;
+        case 128: launch_tiled_n<DT, 128 / E, PACKED>(N, S, a); break;
+        case 256: launch_tiled_n<DT, 256 / E, PACKED>(N, S, a); break;
+        default: launch_tiled_n<DT, 512 / E, PACKED>(N, S, a); break;
     }
 }
 
-// Which combine kernel serves a call. `fast` = D % 8 == 0, D <= 2048,
-// rows < 2^31 and the buffers meet the 16-byte (separate) or 4-byte (packed)
-// alignment; otherwise the element-wise kernel runs.
+// Which combine kernel serves a call. `fast` = fast_d(D), rows < 2^31 and the
+// buffers meet the 16-byte (separate) or 4-byte (packed) alignment; otherwise
+// the element-wise kernel runs.
 enum { kPathTiled = 0, kPathRows = 1, kPathElems = 2 };
 struct CombinePlan {
     int kind;
     int S;  // row slots per lane (tiled path)
 };
 
-CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, bool packed, bool fast) {
+CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, int64_t esize, bool packed,
+                         bool fast) {
     if (!fast) return {kPathElems, 0};
     const bool tiled_shape = (D == 128 || D == 256 || D == 512) &&
                              (N == 2 || N == 4 || N == 8 || N == 16);
     if (tiled_shape) {
-        const uint64_t plane_bytes = uint64_t(rows) * uint64_t(packed ? D + 2 : D) * 2;
+        const int64_t P = 4 / esize;
+        const uint64_t plane_bytes = uint64_t(rows) * uint64_t(packed ? D + P : D) * uint64_t(esize);
         const bool fits32 = plane_bytes < (uint64_t(1) << 32) &&
                             (packed || uint64_t(N) * uint64_t(rows) < (uint64_t(1) << 32));
         if (fits32) {
-            const uint64_t rps = kBlock / uint64_t(D / 8);
+            const uint64_t rps = kBlock / uint64_t(D * esize / 16);
             const uint64_t min_blocks = N >= 16 ? kTiledMinBlocksN16 : kTiledMinBlocks;
             int S = 16;
             while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < min_blocks) S /= 2;
@@ -776,53 +898,59 @@ CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, bool packed, bool f
     return {kPathRows, 0};
 }
 
+template <int DT, bool PACKED>
+void run_combine_dt(const void* src, const float* lse, int64_t N, int64_t rows, int64_t D,
+                    float scale, float inv_scale, void* out, int out_f32, float* out_lse,
+                    const CombinePlan& plan, OutMap om, int64_t map_a, int64_t map_c,
+                    hipStream_t st) {
+    if (plan.kind == kPathTiled) {
+        const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
+        const TiledArgs a{src, lse, uint32_t(rows), uint32_t(stride),
+                          uint64_t(rows) * uint64_t(stride) * sizeof(typename Elem<DT>::T),
+                          scale, inv_scale, out, out_f32, out_lse, om, st};
+        launch_tiled<DT, PACKED>(int(N), plan.S, int(D), a);
+    } else if (plan.kind == kPathRows) {
+        dispatch_n<DT, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale, inv_scale, out,
+                               out_f32, out_lse, om, st);
+    } else {
+        const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
+        combine_elems_kernel<DT, PACKED><<<general_grid(rows * D), kBlock, 0, st>>>(
+            static_cast<const typename Elem<DT>::T*>(src), lse, int(N), rows, stride,
+            rows * stride, D, scale, inv_scale, out, out_f32, out_lse, map_a, map_c);
+    }
+}
+
 template <bool PACKED>
-int run_combine(const uint16_t* src, const float* lse, int64_t N, int64_t rows, int64_t D,
-                int dtype, int base, uint16_t* out, float* out_lse, bool fast, hipStream_t st,
+int run_combine(const void* src, const float* lse, int64_t N, int64_t rows, int64_t D,
+                const Dtype& dt, int base, void* out, float* out_lse, bool fast, hipStream_t st,
                 int64_t map_a = 0, int64_t map_c = 1) {
     const OutMap om{uint32_t(map_a), make_fastdiv(uint32_t(map_c))};
     const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
     const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
-    const CombinePlan plan = plan_combine(N, rows, D, PACKED, fast);
+    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, PACKED, fast);
     (void)hipGetLastError();
-    if (plan.kind == kPathTiled) {
-        if (dtype == LSEC_BF16)
-            launch_tiled<LSEC_BF16, PACKED>(int(N), plan.S, uint32_t(rows), int(D), src, lse,
-                                            scale, inv_scale, out, out_lse, om, st);
-        else
-            launch_tiled<LSEC_FP16, PACKED>(int(N), plan.S, uint32_t(rows), int(D), src, lse,
-                                            scale, inv_scale, out, out_lse, om, st);
-    } else if (plan.kind == kPathRows) {
-        if (dtype == LSEC_BF16)
-            dispatch_n<LSEC_BF16, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale,
-                                          inv_scale, out, out_lse, om, st);
-        else
-            dispatch_n<LSEC_FP16, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale,
-                                          inv_scale, out, out_lse, om, st);
-    } else {
-        const int64_t stride = PACKED ? D + 2 : D;
-        const unsigned blocks = general_grid(rows * D);
-        if (dtype == LSEC_BF16)
-            combine_elems_kernel<LSEC_BF16, PACKED><<<blocks, kBlock, 0, st>>>(
-                src, lse, int(N), rows, stride, rows * stride, D, scale, inv_scale, out, out_lse,
-                map_a, map_c);
-        else
-            combine_elems_kernel<LSEC_FP16, PACKED><<<blocks, kBlock, 0, st>>>(
-                src, lse, int(N), rows, stride, rows * stride, D, scale, inv_scale, out, out_lse,
-                map_a, map_c);
+#define LSEC_RUN(DTV)                                                                        \
+    run_combine_dt<DTV, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, dt.out_f32, \
+                                out_lse, plan, om, map_a, map_c, st)
+    switch (dt.in) {
+        case LSEC_BF16: LSEC_RUN(LSEC_BF16); break;
+        case LSEC_FP16: LSEC_RUN(LSEC_FP16); break;
+        default: LSEC_RUN(LSEC_FP32); break;
     }
+#undef LSEC_RUN
     return launch_status();
 }
 
 template <int DT, int G>
-void launch_correct_s(int S, const float* lse, int N, int rank, const uint16_t* part, uint32_t rows,
-                      float scale, float inv_scale, uint16_t* out, float* out_lse,
+void launch_correct_s(int S, const float* lse, int N, int rank, const void* part, uint32_t rows,
+                      float scale, float inv_scale, void* out, int out_f32, float* out_lse,
                       hipStream_t st) {
     constexpr uint32_t RPS = kBlock / G;
     const unsigned blocks = (rows + RPS * S - 1) / (RPS * S);
-#define LSEC_CORRECT(SV)                                                                        \
-    correct_tiled_kernel<DT, G, SV><<<blocks, kBlock, 0, st>>>(lse, N, rank, part, rows, scale, \
-                                                               inv_scale, out, out_lse)
+    const auto* p = static_cast<const typename Elem<DT>::T*>(part);
+#define LSEC_CORRECT(SV)                                                                   \
+    correct_tiled_kernel<DT, G, SV><<<blocks, kBlock, 0, st>>>(lse, N, rank, p, rows, scale, \
+                                                               inv_scale, out, out_f32, out_lse)
     switch (S) {
         case 8: LSEC_CORRECT(8); break;
         case 4: LSEC_CORRECT(4); break;
@@ -833,22 +961,88 @@ void launch_correct_s(int S, const float* lse, int N, int rank, const uint16_t* 
 }
 
 template <int DT>
-void launch_correct(bool tiled, const float* lse, int64_t N, int64_t rank, const uint16_t* part,
-                    int64_t rows, int64_t D, float scale, float inv_scale, uint16_t* out,
-                    float* out_lse, hipStream_t st) {
+void launch_correct(bool tiled, const float* lse, int64_t N, int64_t rank, const void* part,
+                    int64_t rows, int64_t D, float scale, float inv_scale, void* out,
+                    int out_f32, float* out_lse, hipStream_t st) {
     if (!tiled) {
         correct_elems_kernel<DT><<<general_grid(rows * D), kBlock, 0, st>>>(
-            lse, int(N), int(rank), part, rows, D, scale, inv_scale, out, out_lse);
+            lse, int(N), int(rank), static_cast<const typename Elem<DT>::T*>(part), rows, D,
+            scale, inv_scale, out, out_f32, out_lse);
         return;
     }
-    const uint64_t rps = kBlock / uint64_t(D / 8);
+    constexpr int E = Elem<DT>::kEpc;
+    const uint64_t rps = kBlock / uint64_t(D / E);
     int S = 8;
     while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < kTiledMinBlocks) S /= 2;
+#define LSEC_CORRECT_G(GV) \
+    launch_correct_s<DT, GV>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_f32, out_lse, st)
     switch (D) {
-        case 128: launch_correct_s<DT, 16>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_lse, st); break;
-        case 256: launch_correct_s<DT, 32>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_lse, st); break;
-        default: launch_correct_s<DT, 64>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_lse, st); break;
+        case 128: LSEC_CORRECT_G(128 / E); break;
+        case 256: LSEC_CORRECT_G(256 / E); break;
+        default: LSEC_CORRECT_G(512 / E); break;
     }
+#undef LSEC_CORRECT_G
+}
+
+template <typename T>
+void launch_pack(bool fast, const void* attn_out, const float* lse, int64_t B, int64_t H,
+                 int64_t Hl, int64_t D, int64_t rows, int64_t total, void* send, hipStream_t st) {
+    const T* in = static_cast<const T*>(attn_out);
+    T* dst = static_cast<T*>(send);
+    if (fast) {
+        const uint32_t g = uint32_t(D / (16 / sizeof(T)));
+        const uint32_t rpb = kBlock / g;
+        const unsigned blocks = unsigned((rows + rpb * kPackRows - 1) / (rpb * kPackRows));
+        pack_rows_kernel<T><<<blocks, kBlock, 0, st>>>(in, lse, uint32_t(rows), make_fastdiv(g),
+                                                       rpb, make_fastdiv(uint32_t(Hl)),
+                                                       make_fastdiv(uint32_t(B)), uint32_t(H),
+                                                       int(D), dst);
+    } else {
+        pack_elems_kernel<T><<<general_grid(total), kBlock, 0, st>>>(in, lse, B, H, Hl, D, total,
+                                                                      dst);
+    }
+}
+
+template <typename T>
+void launch_unpack(bool fast, const void* recv, int64_t total_rows, int64_t D, int64_t total,
+                   void* outputs, float* lses, hipStream_t st) {
+    const T* src = static_cast<const T*>(recv);
+    T* outs = static_cast<T*>(outputs);
+    if (fast) {
+        const uint32_t g = uint32_t(D / (16 / sizeof(T)));
+        const uint32_t rpb = kBlock / g;
+        const unsigned blocks = unsigned((total_rows + rpb - 1) / rpb);
+        unpack_rows_kernel<T><<<blocks, kBlock, 0, st>>>(src, uint32_t(total_rows),
+                                                         make_fastdiv(g), rpb, int(D), outs, lses);
+    } else {
+        unpack_elems_kernel<T><<<general_grid(total), kBlock, 0, st>>>(src, total_rows, D, outs,
+                                                                        lses);
+    }
+}
+
+// Shared by lsec_combine and lsec_merge: rows (b, h) of a [B, H] grid, stored
+// in input order or, when `transposed`, at row h * B + b.
+int combine_entry(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
+                  int64_t D, int dtype, int base, void* out, float* out_lse, void* stream,
+                  bool transposed) {
+    if (N < 1 || B < 0 || H < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
+    Dtype dt;
+    if (!parse_dtype(dtype, true, &dt)) return LSEC_ERR_DTYPE;
+    if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
+    int64_t rows, rd, all, ob;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, N, &all) ||
+        !mul_ok(all, dt.esize, &all) || !mul_ok(rd, dt.out_esize, &ob))
+        return LSEC_ERR_SHAPE;
+    if (rows == 0) return LSEC_OK;
+    if (!outputs || !lses || !out) return LSEC_ERR_NULL;
+    if (!aligned(outputs, dt.esize) || !aligned(out, dt.out_esize) || !aligned(lses, 4) ||
+        (out_lse && !aligned(out_lse, 4)))
+        return LSEC_ERR_ALIGNMENT;
+    const bool fast = fast_d(D, dt.esize) && rows < (int64_t(1) << 31) && aligned(outputs, 16) &&
+                      aligned(out, 16);
+    return run_combine<false>(outputs, lses, N, rows, D, dt, base, out, out_lse, fast,
+                              static_cast<hipStream_t>(stream), transposed ? B : 0,
+                              transposed ? H : 1);
 }
 
 }  // namespace
@@ -857,10 +1051,11 @@ void launch_correct(bool tiled, const float* lse, int64_t N, int64_t rank, const
 
 extern "C" {
 
-int lsec_version(void) { return 100; }
+int lsec_version(void) { return 200; }
 
 int lsec_pack_dim(int dtype) {
-    return (dtype == LSEC_BF16 || dtype == LSEC_FP16) ? 2 : -1;
+    if (dtype == LSEC_BF16 || dtype == LSEC_FP16) return 2;
+    return dtype == LSEC_FP32 ? 1 : -1;
 }
 
 const char* lsec_status_string(int status) {
@@ -869,7 +1064,8 @@ const char* lsec_status_string(int status) {
         case LSEC_ERR_NULL: return "a required pointer is NULL";
         case LSEC_ERR_SHAPE: return "invalid shape (need N >= 1, B >= 0, H >= 1, D >= 1, sizes within int64)";
         case LSEC_ERR_DIVISIBILITY: return "H must be divisible by N";
-        case LSEC_ERR_DTYPE: return "unsupported dtype (bf16 or fp16 only)";
+        case LSEC_ERR_DTYPE:
+            return "unsupported dtype (bf16, fp16 or fp32; LSEC_OUT_FP32 only on combining calls)";
         case LSEC_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
         case LSEC_ERR_BASE: return "base must be LSEC_BASE_E or LSEC_BASE_2";
         case LSEC_ERR_LAUNCH: return "kernel launch failed";
@@ -879,12 +1075,14 @@ const char* lsec_status_string(int status) {
     }
 }
 
-const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int packed,
+const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int dtype, int packed,
                               int aligned_buffers) {
     int64_t rows;
-    if (N < 1 || B < 1 || H < 1 || D < 1 || !mul_ok(B, H, &rows)) return "none";
-    const bool fast = aligned_buffers && fast_d(D) && rows < (int64_t(1) << 31);
-    const CombinePlan plan = plan_combine(N, rows, D, packed != 0, fast);
+    Dtype dt;
+    if (N < 1 || B < 1 || H < 1 || D < 1 || !mul_ok(B, H, &rows) || !parse_dtype(dtype, true, &dt))
+        return "none";
+    const bool fast = aligned_buffers && fast_d(D, dt.esize) && rows < (int64_t(1) << 31);
+    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, packed != 0, fast);
     if (plan.kind == kPathElems) return "combine_elems_kernel";
     if (plan.kind == kPathRows) return "combine_rows_kernel";
     switch (plan.S) {
@@ -895,39 +1093,6 @@ const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int pa
         default: return "combine_tiled_kernel S=1";
     }
 }
-
-}  // extern "C"
-
-namespace {
-
-// Shared by lsec_combine and lsec_merge: rows (b, h) of a [B, H] grid, stored
-// in input order or, when `transposed`, at row h * B + b.
-int combine_entry(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
-                  int64_t D, int dtype, int base, void* out, float* out_lse, void* stream,
-                  bool transposed) {
-    if (N < 1 || B < 0 || H < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
-    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
-    if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
-    int64_t rows, rd, all;
-    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, N, &all) ||
-        !mul_ok(all, 2, &all))
-        return LSEC_ERR_SHAPE;
-    if (rows == 0) return LSEC_OK;
-    if (!outputs || !lses || !out) return LSEC_ERR_NULL;
-    if (!aligned(outputs, 2) || !aligned(out, 2) || !aligned(lses, 4) ||
-        (out_lse && !aligned(out_lse, 4)))
-        return LSEC_ERR_ALIGNMENT;
-    const bool fast = fast_d(D) && rows < (int64_t(1) << 31) && aligned(outputs, 16) &&
-                      aligned(out, 16);
-    return run_combine<false>(static_cast<const uint16_t*>(outputs), lses, N, rows, D, dtype,
-                              base, static_cast<uint16_t*>(out), out_lse, fast,
-                              static_cast<hipStream_t>(stream), transposed ? B : 0,
-                              transposed ? H : 1);
-}
-
-}  // namespace
-
-extern "C" {
 
 int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
                  int64_t D, int dtype, int base, void* out, float* out_lse, void* stream) {
@@ -945,20 +1110,21 @@ int lsec_merge(const void* outputs, const float* lses, int64_t N, int64_t A, int
 int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,
                         int base, void* out, float* out_lse, void* stream) {
     if (N < 1 || B < 0 || Hl < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
-    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    Dtype dt;
+    if (!parse_dtype(dtype, true, &dt)) return LSEC_ERR_DTYPE;
     if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
-    int64_t rows, rw, all;
-    if (!mul_ok(B, Hl, &rows) || !mul_ok(rows, D + 2, &rw) || !mul_ok(rw, N, &all) ||
-        !mul_ok(all, 2, &all))
+    const int64_t P = 4 / dt.esize;
+    int64_t rows, rw, all, rd;
+    if (!mul_ok(B, Hl, &rows) || !mul_ok(rows, D + P, &rw) || !mul_ok(rw, N, &all) ||
+        !mul_ok(all, dt.esize, &all) || !mul_ok(rows, D, &rd) || !mul_ok(rd, dt.out_esize, &rd))
         return LSEC_ERR_SHAPE;
     if (rows == 0) return LSEC_OK;
     if (!recv || !out) return LSEC_ERR_NULL;
-    if (!aligned(recv, 2) || !aligned(out, 2) || (out_lse && !aligned(out_lse, 4)))
+    if (!aligned(recv, dt.esize) || !aligned(out, dt.out_esize) || (out_lse && !aligned(out_lse, 4)))
         return LSEC_ERR_ALIGNMENT;
-    const bool fast = fast_d(D) && rows < (int64_t(1) << 31) && aligned(recv, 4) &&
+    const bool fast = fast_d(D, dt.esize) && rows < (int64_t(1) << 31) && aligned(recv, 4) &&
                       aligned(out, 16);
-    return run_combine<true>(static_cast<const uint16_t*>(recv), nullptr, N, rows, D, dtype, base,
-                             static_cast<uint16_t*>(out), out_lse, fast,
+    return run_combine<true>(recv, nullptr, N, rows, D, dt, base, out, out_lse, fast,
                              static_cast<hipStream_t>(stream));
 }
 
@@ -967,15 +1133,16 @@ int lsec_correct_partial(const float* lses, int64_t N, int64_t rank, const void*
                          float* out_lse, void* stream) {
     if (N < 1 || B < 0 || H < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
     if (rank < 0 || rank >= N) return LSEC_ERR_RANK;
-    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    Dtype dt;
+    if (!parse_dtype(dtype, true, &dt)) return LSEC_ERR_DTYPE;
     if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
-    int64_t rows, rd, nl;
-    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, 2, &rd) ||
-        !mul_ok(rows, N, &nl) || !mul_ok(nl, 4, &nl))
+    int64_t rows, rd, ib, ob, nl;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, dt.esize, &ib) ||
+        !mul_ok(rd, dt.out_esize, &ob) || !mul_ok(rows, N, &nl) || !mul_ok(nl, 4, &nl))
         return LSEC_ERR_SHAPE;
     if (rows == 0) return LSEC_OK;
     if (!lses || !partial || !out) return LSEC_ERR_NULL;
-    if (!aligned(partial, 2) || !aligned(out, 2) || !aligned(lses, 4) ||
+    if (!aligned(partial, dt.esize) || !aligned(out, dt.out_esize) || !aligned(lses, 4) ||
         (out_lse && !aligned(out_lse, 4)))
         return LSEC_ERR_ALIGNMENT;
     const bool tiled = (D == 128 || D == 256 || D == 512) && N <= 16 &&
@@ -985,12 +1152,14 @@ int lsec_correct_partial(const float* lses, int64_t N, int64_t rank, const void*
     const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (dtype == LSEC_BF16)
-        launch_correct<LSEC_BF16>(tiled, lses, N, rank, static_cast<const uint16_t*>(partial), rows,
-                                  D, scale, inv_scale, static_cast<uint16_t*>(out), out_lse, st);
-    else
-        launch_correct<LSEC_FP16>(tiled, lses, N, rank, static_cast<const uint16_t*>(partial), rows,
-                                  D, scale, inv_scale, static_cast<uint16_t*>(out), out_lse, st);
+#define LSEC_CORRECT_DT(DTV) \
+    launch_correct<DTV>(tiled, lses, N, rank, partial, rows, D, scale, inv_scale, out, dt.out_f32, out_lse, st)
+    switch (dt.in) {
+        case LSEC_BF16: LSEC_CORRECT_DT(LSEC_BF16); break;
+        case LSEC_FP16: LSEC_CORRECT_DT(LSEC_FP16); break;
+        default: LSEC_CORRECT_DT(LSEC_FP32); break;
+    }
+#undef LSEC_CORRECT_DT
     return launch_status();
 }
 
@@ -998,63 +1167,50 @@ int lsec_pack_send(const void* attn_out, const float* attn_lse, int64_t N, int64
                    int64_t D, int dtype, void* send, void* stream) {
     if (N < 1 || B < 0 || H < 1 || D < 1) return LSEC_ERR_SHAPE;
     if (H % N != 0) return LSEC_ERR_DIVISIBILITY;
-    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    Dtype dt;
+    if (!parse_dtype(dtype, false, &dt)) return LSEC_ERR_DTYPE;
+    const int64_t P = 4 / dt.esize;
     int64_t rows, total, bytes;
-    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D + 2, &total) || !mul_ok(total, 2, &bytes))
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D + P, &total) || !mul_ok(total, dt.esize, &bytes))
         return LSEC_ERR_SHAPE;
     if (rows == 0) return LSEC_OK;
     if (!attn_out || !attn_lse || !send) return LSEC_ERR_NULL;
-    if (!aligned(attn_out, 2) || !aligned(send, 2) || !aligned(attn_lse, 4))
+    if (!aligned(attn_out, dt.esize) || !aligned(send, dt.esize) || !aligned(attn_lse, 4))
         return LSEC_ERR_ALIGNMENT;
     const int64_t Hl = H / N;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const auto* in = static_cast<const uint16_t*>(attn_out);
-    auto* dst = static_cast<uint16_t*>(send);
     (void)hipGetLastError();
-    const bool fast = fast_d(D) && rows < (int64_t(1) << 31) && aligned(attn_out, 16) &&
+    const bool fast = fast_d(D, dt.esize) && rows < (int64_t(1) << 31) && aligned(attn_out, 16) &&
                       aligned(send, 4);
-    if (fast) {
-        const uint32_t g = uint32_t(D / 8);
-        const uint32_t rpb = kBlock / g;
-        const unsigned blocks = unsigned((rows + rpb * kPackRows - 1) / (rpb * kPackRows));
-        pack_rows_kernel<<<blocks, kBlock, 0, st>>>(in, attn_lse, uint32_t(rows), make_fastdiv(g),
-                                                    rpb, make_fastdiv(uint32_t(Hl)),
-                                                    make_fastdiv(uint32_t(B)), uint32_t(H),
-                                                    int(D), dst);
-    } else {
-        pack_elems_kernel<<<general_grid(total), kBlock, 0, st>>>(in, attn_lse, B, H, Hl, D,
-                                                                   total, dst);
-    }
+    if (dt.esize == 4)
+        launch_pack<uint32_t>(fast, attn_out, attn_lse, B, H, Hl, D, rows, total, send, st);
+    else
+        launch_pack<uint16_t>(fast, attn_out, attn_lse, B, H, Hl, D, rows, total, send, st);
     return launch_status();
 }
 
 int lsec_unpack(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,
                 void* outputs, float* lses, void* stream) {
     if (N < 1 || B < 0 || Hl < 1 || D < 1) return LSEC_ERR_SHAPE;
-    if (dtype != LSEC_BF16 && dtype != LSEC_FP16) return LSEC_ERR_DTYPE;
+    Dtype dt;
+    if (!parse_dtype(dtype, false, &dt)) return LSEC_ERR_DTYPE;
+    const int64_t P = 4 / dt.esize;
     int64_t rows, total_rows, total, bytes;
     if (!mul_ok(B, Hl, &rows) || !mul_ok(rows, N, &total_rows) ||
-        !mul_ok(total_rows, D + 2, &total) || !mul_ok(total, 2, &bytes))
+        !mul_ok(total_rows, D + P, &total) || !mul_ok(total, dt.esize, &bytes))
         return LSEC_ERR_SHAPE;
     if (total_rows == 0) return LSEC_OK;
     if (!recv || !outputs || !lses) return LSEC_ERR_NULL;
-    if (!aligned(recv, 2) || !aligned(outputs, 2) || !aligned(lses, 4)) return LSEC_ERR_ALIGNMENT;
+    if (!aligned(recv, dt.esize) || !aligned(outputs, dt.esize) || !aligned(lses, 4))
+        return LSEC_ERR_ALIGNMENT;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const auto* src = static_cast<const uint16_t*>(recv);
-    auto* outs = static_cast<uint16_t*>(outputs);
     (void)hipGetLastError();
-    const bool fast = fast_d(D) && total_rows < (int64_t(1) << 31) && aligned(recv, 4) &&
+    const bool fast = fast_d(D, dt.esize) && total_rows < (int64_t(1) << 31) && aligned(recv, 4) &&
                       aligned(outputs, 16);
-    if (fast) {
-        const uint32_t g = uint32_t(D / 8);
-        const uint32_t rpb = kBlock / g;
-        const unsigned blocks = unsigned((total_rows + rpb - 1) / rpb);
-        unpack_rows_kernel<<<blocks, kBlock, 0, st>>>(src, uint32_t(total_rows), make_fastdiv(g),
-                                                      rpb, int(D), outs, lses);
-    } else {
-        unpack_elems_kernel<<<general_grid(total), kBlock, 0, st>>>(src, total_rows, D, outs,
-                                                                     lses);
-    }
+    if (dt.esize == 4)
+        launch_unpack<uint32_t>(fast, recv, total_rows, D, total, outputs, lses, st);
+    else
+        launch_unpack<uint16_t>(fast, recv, total_rows, D, total, outputs, lses, st);
     return launch_status();
 }
 

@@ -130,7 +130,7 @@ class Workload:
     B: int
     H: int
     D: int
-    dtype: str  # "bf16" | "f16"
+    dtype: str  # "bf16" | "f16" | "f32"
     out_dist: tuple  # (dist, a, b)
     lse_dist: tuple
     special: tuple = ()  # ((probability, value), ...) applied in order on one uniform per entry
@@ -170,6 +170,13 @@ WORKLOADS = {
                  return_lse=False,
                  desc="gathered LSEs [8,4096,16] base 2 + rank 3's partial [4096,16,512] bf16 -> "
                       "its share of the combine (all-gather + reduce-scatter local step)"),
+        Workload("mla_decode_f32", 8, "combine", 8, 4096, 16, 512, "f32", ("normal", 0.0, 0.5),
+                 ("normal", 10.0, 3.0), special=((0.01, float("-inf")),), base2=True,
+                 return_lse=False,
+                 desc="N=8 B=4096 H=16 D=512 fp32 partials, LSE base 2 N(10,3), 1% -inf"),
+        Workload("packed_f32", 9, "packed", 8, 2048, 64, 128, "f32", ("normal", 0.0, 1.0),
+                 ("uniform", -5.0, 15.0), base2=False, return_lse=True,
+                 desc="per-rank [2048,64,128] fp32 + [2048,64] fp32 -> [8,2048,8,129] fp32"),
         Workload("large_batch", 5, "combine", 16, 16384, 32, 128, "bf16", ("normal", 0.0, 1.0),
                  ("uniform", -10.0, 30.0),
                  special=((0.005 / 3, float("nan")), (0.005 / 3, float("inf")),

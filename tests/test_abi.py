@@ -46,13 +46,15 @@ def test_constants_match_header(lib):
     for name in ("LSEC_OK", "LSEC_ERR_NULL", "LSEC_ERR_SHAPE", "LSEC_ERR_DIVISIBILITY",
                  "LSEC_ERR_DTYPE", "LSEC_ERR_ALIGNMENT", "LSEC_ERR_BASE", "LSEC_ERR_LAUNCH",
                  "LSEC_ERR_TOKEN_DIM", "LSEC_ERR_RANK",
-                 "LSEC_BF16", "LSEC_FP16", "LSEC_BASE_E", "LSEC_BASE_2"):
+                 "LSEC_BF16", "LSEC_FP16", "LSEC_FP32", "LSEC_OUT_FP32", "LSEC_BASE_E",
+                 "LSEC_BASE_2"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m and int(m.group(1)) == getattr(lsec, name), name
 
 
 def test_pack_dim_and_strings(lib):
-    assert lib.lsec_pack_dim(0) == 2 and lib.lsec_pack_dim(1) == 2 and lib.lsec_pack_dim(7) == -1
+    assert lib.lsec_pack_dim(0) == 2 and lib.lsec_pack_dim(1) == 2 and lib.lsec_pack_dim(2) == 1
+    assert lib.lsec_pack_dim(7) == -1 and lib.lsec_pack_dim(0 | 256) == -1
     assert lib.lsec_version() >= 100
     for s in range(0, 11):
         assert lib.lsec_status_string(s)
@@ -68,6 +70,12 @@ FAKE = 0x100000  # a 16-byte aligned non-null address; never dereferenced (calls
     ((FAKE, FAKE, 2, 1, 1, 0, 0, 0, FAKE, None, None), 2),      # D < 1
     ((FAKE, FAKE, 2, 1 << 40, 1 << 20, 1 << 10, 0, 0, FAKE, None, None), 2),  # overflow
     ((FAKE, FAKE, 2, 1, 1, 8, 5, 0, FAKE, None, None), 4),      # dtype
+    ((FAKE, FAKE, 2, 1, 1, 8, 3 | 256, 0, FAKE, None, None), 4),  # flag on an unknown dtype
+    ((FAKE, FAKE, 2, 1, 1, 8, 512, 0, FAKE, None, None), 4),    # unknown flag bit
+    ((FAKE + 2, FAKE, 2, 1, 1, 8, 2, 0, FAKE, None, None), 5),  # fp32 outputs not 4-aligned
+    ((FAKE, FAKE, 2, 1, 1, 8, 2, 0, FAKE + 2, None, None), 5),  # fp32 out not 4-aligned
+    ((FAKE, FAKE, 2, 1, 1, 8, 0 | 256, 0, FAKE + 2, None, None), 5),  # fp32 result, out 2-aligned
+    ((FAKE, FAKE, 2, 1 << 40, 1 << 20, 1 << 9, 2, 0, FAKE, None, None), 2),  # fp32 overflow
     ((FAKE, FAKE, 2, 1, 1, 8, 0, 3, FAKE, None, None), 6),      # base
     ((None, FAKE, 2, 1, 1, 8, 0, 0, FAKE, None, None), 1),      # NULL outputs
     ((FAKE, None, 2, 1, 1, 8, 0, 0, FAKE, None, None), 1),      # NULL lses
@@ -86,6 +94,8 @@ def test_pack_send_validation(lib):
     assert f(FAKE, FAKE, 3, 2, 8, 16, 0, FAKE, None) == 3   # 8 % 3 != 0
     assert f(FAKE, FAKE, 0, 2, 8, 16, 0, FAKE, None) == 2
     assert f(FAKE, FAKE, 2, 2, 8, 16, 9, FAKE, None) == 4
+    assert f(FAKE, FAKE, 2, 2, 8, 16, 0 | 256, FAKE, None) == 4  # no fp32 result on a layout call
+    assert f(FAKE, FAKE, 2, 2, 8, 16, 2, FAKE + 2, None) == 5    # fp32 send 2-aligned
     assert f(None, FAKE, 2, 2, 8, 16, 0, FAKE, None) == 1
     assert f(FAKE, FAKE, 2, 2, 8, 16, 0, FAKE + 1, None) == 5
     assert f(None, None, 2, 0, 8, 16, 0, None, None) == 0
@@ -94,13 +104,17 @@ def test_pack_send_validation(lib):
 def test_unpack_validation(lib):
     uc = lib.lsec_unpack_combine
     assert uc(FAKE, 0, 2, 2, 16, 0, 0, FAKE, None, None) == 2
-    assert uc(FAKE, 2, 2, 2, 16, 2, 0, FAKE, None, None) == 4
+    assert uc(FAKE, 2, 2, 2, 16, 3, 0, FAKE, None, None) == 4
     assert uc(FAKE, 2, 2, 2, 16, 0, 9, FAKE, None, None) == 6
     assert uc(None, 2, 2, 2, 16, 0, 0, FAKE, None, None) == 1
     assert uc(FAKE, 2, 2, 2, 16, 0, 0, FAKE, FAKE + 2, None) == 5
     u = lib.lsec_unpack
     assert u(FAKE, 2, 2, 0, 16, 0, FAKE, FAKE, None) == 2
     assert u(FAKE, 2, 2, 2, 16, 0, FAKE, None, None) == 1
+    assert u(FAKE, 2, 2, 2, 16, 1 | 256, FAKE, FAKE, None) == 4
+    assert u(FAKE + 2, 2, 2, 2, 16, 2, FAKE, FAKE, None) == 5
+    assert uc(FAKE + 2, 2, 2, 2, 16, 2, 0, FAKE, None, None) == 5
+    assert uc(FAKE, 2, 2, 2, 16, 1 | 256, 0, FAKE + 2, None, None) == 5
     assert u(FAKE, 2, 2, 2, 16, 0, FAKE, FAKE + 2, None) == 5
     assert u(None, 2, 0, 2, 16, 0, None, None, None) == 0
 
@@ -114,23 +128,32 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         lsec.lsec_combine(torch.zeros(2, 1, 8, dtype=torch.bfloat16), torch.zeros(2, 1))
     with pytest.raises(ValueError):
-        lsec.lsec_pack_dim(torch.float32)
+        lsec.lsec_pack_dim(torch.float64)
+    assert lsec.lsec_pack_dim(torch.float32) == 1
     with pytest.raises(ValueError):
         lsec.lsec_pack_send(torch.zeros(1, 6, 8, dtype=torch.float16), torch.zeros(1, 6), 4)
 
 
 @pytest.mark.parametrize("args,want", [
-    ((16, 16384, 32, 128, 0, 1), "combine_tiled_kernel S=16"),
-    ((8, 4096, 16, 512, 0, 1), "combine_tiled_kernel S=8"),
-    ((4, 256, 32, 128, 0, 1), "combine_tiled_kernel S=1"),
-    ((8, 2048, 8, 128, 1, 1), "combine_tiled_kernel S=1"),
-    ((16, 16384, 32, 128, 0, 0), "combine_elems_kernel"),   # buffers not 16-byte aligned
-    ((1, 50, 3, 512, 0, 1), "combine_rows_kernel"),          # N = 1
-    ((32, 6, 4, 128, 0, 1), "combine_rows_kernel"),          # N outside {2, 4, 8, 16}
-    ((4, 10, 3, 64, 0, 1), "combine_rows_kernel"),           # D outside {128, 256, 512}
-    ((3, 5, 2, 3, 0, 1), "combine_elems_kernel"),            # D % 8 != 0
-    ((2, 2, 2, 4096, 0, 1), "combine_elems_kernel"),         # D > 2048
-    ((4, 0, 8, 128, 0, 1), "none"),
+    # N, B, H, D, dtype, packed, aligned
+    ((16, 16384, 32, 128, 0, 0, 1), "combine_tiled_kernel S=16"),
+    ((8, 4096, 16, 512, 0, 0, 1), "combine_tiled_kernel S=8"),
+    ((4, 256, 32, 128, 0, 0, 1), "combine_tiled_kernel S=1"),
+    ((8, 2048, 8, 128, 0, 1, 1), "combine_tiled_kernel S=1"),
+    ((16, 16384, 32, 128, 0, 0, 0), "combine_elems_kernel"),   # buffers not 16-byte aligned
+    ((1, 50, 3, 512, 0, 0, 1), "combine_rows_kernel"),          # N = 1
+    ((32, 6, 4, 128, 0, 0, 1), "combine_rows_kernel"),          # N outside {2, 4, 8, 16}
+    ((4, 10, 3, 64, 0, 0, 1), "combine_rows_kernel"),           # D outside {128, 256, 512}
+    ((3, 5, 2, 3, 0, 0, 1), "combine_elems_kernel"),            # D % 8 != 0
+    ((2, 2, 2, 4096, 0, 0, 1), "combine_elems_kernel"),         # D > 2048
+    ((4, 0, 8, 128, 0, 0, 1), "none"),
+    ((4, 8, 8, 128, 7, 0, 1), "none"),                          # unknown dtype
+    ((16, 16384, 32, 128, 256, 0, 1), "combine_tiled_kernel S=16"),  # bf16 -> fp32 result
+    ((2, 8197, 32, 128, 2, 0, 1), "combine_tiled_kernel S=16"),  # fp32: 262304 rows of 32 lanes
+    ((4, 3001, 33, 256, 2, 0, 1), "combine_tiled_kernel S=8"),
+    ((2, 2, 2, 1024, 2, 0, 1), "combine_rows_kernel"),          # fp32: 256 lanes per row
+    ((2, 2, 2, 2048, 2, 0, 1), "combine_elems_kernel"),         # fp32: D > 1024
+    ((3, 5, 2, 6, 2, 0, 1), "combine_elems_kernel"),            # fp32: D % 4 != 0
 ])
 def test_combine_path(lib, args, want):
     assert lib.lsec_combine_path(*args).decode() == want

@@ -171,7 +171,7 @@ SHAPES = [
     (32, 6, 4, 128, "bf16", False),
     (9, 20, 2, 24, "bf16", True),     # 3 lanes per row, rows straddle waves
     (2, 3, 3, 2048, "f16", False),    # 256 lanes per row
-    (4, 10, 3, 1000, "bf16", False),  # general path: D % 8 != 0
+    (4, 10, 3, 1000, "bf16", False),  # row kernel, 125 lanes per row
     (3, 5, 2, 3, "f16", True),        # general path: tiny D
     (2, 2, 2, 4096, "bf16", True),    # general path: D > 2048
 ]
@@ -482,7 +482,8 @@ def test_errors_raise(lsec):
         lsec.lsec_pack_send(torch.zeros(2, 6, 8, dtype=torch.bfloat16, device=DEV),
                             torch.zeros(2, 6, device=DEV), 4)
     with pytest.raises(ValueError):
-        lsec.lsec_combine(torch.zeros(2, 1, 1, 8, device=DEV), torch.zeros(2, 1, 1, device=DEV))
+        lsec.lsec_combine(torch.zeros(2, 1, 1, 8, dtype=torch.float64, device=DEV),
+                          torch.zeros(2, 1, 1, device=DEV))
     with pytest.raises(ValueError):
         lsec.lsec_combine(torch.zeros(2, 1, 1, 8, dtype=torch.bfloat16, device=DEV),
                           torch.zeros(2, 1, 1, dtype=torch.float64, device=DEV))
@@ -505,10 +506,12 @@ def test_side_stream_and_preallocated_outputs(lsec):
 
 
 def test_page_signature_alias(lsec):
+    """The page's function returns fp32 (bf16 outputs times fp32 weights)."""
     o, l = synth.custom_inputs(3, 4, 4, 64, seed=13)
     y, L = lsec.lse_weighted_combine(to_dev(o, "bf16", DEV), f32_to_dev(l, DEV), return_lse=True,
                                      is_lse_base_on_e=False)
     torch.cuda.synchronize()
+    assert y.dtype == torch.float32
     y_ref, L_ref = oracle.lse_combine(o, l, "bf16", base2=True)
-    assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
+    assert_output_close(y, y_ref, "f32", max_abs_input(o, "bf16"))
     assert_lse_close(L, L_ref)
