@@ -19,6 +19,9 @@ already resident in HBM:
   with the gathered LSEs [8, 4096, 16] (the local step of an all-gather +
   reduce-scatter combine).
 * ``mla_decode_f32``: lsec_combine of fp32 partials [8, 4096, 16, 512], base 2.
+* ``direct_planes``: lsec_combine_planes over one ubatch slot of a direct
+  exchange's receive buffer: 8 planes of [4096, 8, 128] bf16 of which the
+  first 2048 tokens are combined into [2048, 8, 128] (+ LSE).
 * ``packed_f32``: the ``packed`` pair on fp32 outputs (packed rows of D + 1
   fp32 elements, the LSE in the last).
 
@@ -139,6 +142,27 @@ def build_workload(name: str, dev, out_f32: bool = False):
         kernels = [(kname, nbytes, step)]
         host = None
         info["rank"] = rank
+    elif w.kind == "planes":
+        T_max = 2 * w.B
+        o, l = synth.combine_inputs(w)
+        buf = torch.zeros((w.N, T_max, w.H, w.D), dtype=tdt, device=dev)
+        lbuf = torch.zeros((w.N, T_max, w.H), dtype=torch.float32, device=dev)
+        buf[:, :w.B] = dev_bits(o)
+        lbuf[:, :w.B] = torch.from_numpy(l).to(dev)
+        out = torch.empty((w.B, w.H, w.D), dtype=tdt, device=dev)
+        out_lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        nbytes = combine_bytes(w.N, w.B, w.H, w.D, s, True)
+        kname = f"{lsec.lsec_combine_path(w.N, w.B, w.H, w.D, dtype=tdt)} ({w.dtype}, N={w.N}, " \
+                f"D={w.D}, {w.B} of {T_max} tokens per plane)"
+
+        def step():
+            lsec.lsec_combine_planes(buf, lbuf, w.B, base_e=not w.base2, return_lse=True, out=out,
+                                     out_lse=out_lse)
+
+        kernels = [(kname, nbytes, step)]
+        host = (o, l)
+        rows = w.B * w.H
+        info["T_max"] = T_max
     elif w.kind == "merge":
         o, l = synth.combine_inputs(w)
         og, lg = dev_bits(o), torch.from_numpy(l).to(dev)
@@ -297,7 +321,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large_batch",
                     choices=["large_batch", "mla_decode", "fp16_base2", "packed", "small",
-                             "merge_heads", "ag_correct", "mla_decode_f32", "packed_f32"])
+                             "merge_heads", "ag_correct", "mla_decode_f32", "packed_f32",
+                             "direct_planes"])
     ap.add_argument("--out-f32", action="store_true",
                     help="combine workloads: fp32 result from 16-bit partials")
     ap.add_argument("--flush-mib", type=int, default=-1,

@@ -104,6 +104,30 @@ int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, i
                  int64_t D, int dtype, int base, void* out, float* out_lse, void* stream);
 
 /*
+ * lsec_combine_planes -- lsec_combine over planes that are the leading rows of
+ * longer ones: the local combine of the page's fused direct all-to-all
+ * (`DirectDCPA2AWorkspace.lse_reduce`, page "vllm.v1.attention.ops.
+ * dcp_alltoall"), whose receive buffers hold, per ubatch and slot, W planes
+ * [W, T_max, H_r, D] (+ LSEs [W, T_max, H_r]) of which the first T tokens
+ * belong to the current step. The caller picks the ubatch and slot by the
+ * base pointers; the library reads nothing beyond the first T tokens.
+ *   outputs          : plane n = the T * H * D elements at
+ *                      outputs + n * plane_stride (dtype)
+ *   plane_stride     : elements between planes, >= T * H * D (T_max * H * D)
+ *   lses             : plane n = the T * H fp32 at lses + n * lse_plane_stride
+ *   lse_plane_stride : >= T * H (T_max * H)
+ *   out, out_lse     : [T, H, D], [T, H] exactly as in lsec_combine
+ * With plane_stride = T*H*D and lse_plane_stride = T*H this is lsec_combine.
+ * The fast kernels also need plane_stride * sizeof(element) to be a multiple
+ * of 16 bytes; other strides take the general path with the same results.
+ * Errors: NULL, SHAPE (also a stride below its plane's size), DTYPE, BASE,
+ * ALIGNMENT, LAUNCH.
+ */
+int lsec_combine_planes(const void* outputs, int64_t plane_stride, const float* lses,
+                        int64_t lse_plane_stride, int64_t N, int64_t T, int64_t H, int64_t D,
+                        int dtype, int base, void* out, float* out_lse, void* stream);
+
+/*
  * lsec_merge -- the merge of page "vllm_ascend/attention/context_parallel/
  * sfa_cp.py", `_merge_dcp_outputs_with_torch`: the combine of lsec_combine over
  * received planes whose token index is the first or the second of the two row

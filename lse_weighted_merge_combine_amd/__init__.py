@@ -22,6 +22,10 @@ Entry points (same names as the C ABI):
   of the page "vllm_ascend/attention/context_parallel/sfa_cp.py": the same
   combine over received planes, stored token-major.
 
+* ``lsec_combine_planes(outputs, lses, num_tokens)`` -- the local combine of
+  that page's fused direct all-to-all (``DirectDCPA2AWorkspace.lse_reduce``):
+  the first ``num_tokens`` tokens of one ubatch slot's receive planes.
+
 * ``lsec_correct_partial(lses, rank, partial)`` -- the local step of the LSE
   all-gather + output reduce-scatter strategies named on the page
   "vllm.v1.attention.ops.dcp" (``cp_lse_ag_out_rs`` / ``cp_lse_ag_out_ar``).
@@ -99,6 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_unpack_combine.argtypes = [P, I64, I64, I64, I64, I, I, P, P, P]
     lib.lsec_unpack.restype = I
     lib.lsec_unpack.argtypes = [P, I64, I64, I64, I64, I, P, P, P]
+    lib.lsec_combine_planes.restype = I
+    lib.lsec_combine_planes.argtypes = [P, I64, P, I64, I64, I64, I64, I64, I, I, P, P, P]
     lib.lsec_merge.restype = I
     lib.lsec_merge.argtypes = [P, P, I64, I64, I64, I64, I, I, I, P, P, P]
     lib.lsec_correct_partial.restype = I
@@ -199,6 +205,52 @@ def lsec_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
                           LSEC_BASE_E if base_e else LSEC_BASE_2, _ptr(out),
                           _ptr(out_lse) if return_lse else None, _stream(dev, stream))
     _raise_on(st, "lsec_combine")
+    return (out, out_lse) if return_lse else out
+
+
+def lsec_combine_planes(outputs: torch.Tensor, lses: torch.Tensor, num_tokens: int,
+                        base_e: bool = True, return_lse: bool = False,
+                        out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None,
+                        stream=None, out_dtype=None):
+    """Combine the first ``num_tokens`` tokens of receive planes
+    outputs [N,T_max,H,D] + lses [N,T_max,H] -> [num_tokens,H,D] (+ [num_tokens,H]).
+
+    The planes of the fused direct all-to-all's receive buffers
+    (``received_output[ubatch][slot]``). Each plane must be contiguous; the
+    stride between planes may be anything at least a plane's size (so a view
+    such as ``buf[u, s]`` or ``buf[u, s, :, :T]`` works as is).
+    """
+    lib = load_library()
+    if outputs.dim() != 4 or lses.dim() != 3 or tuple(lses.shape) != tuple(outputs.shape[:3]):
+        raise ValueError(f"expected outputs [N,T_max,H,D] and lses [N,T_max,H], got "
+                         f"{tuple(outputs.shape)} and {tuple(lses.shape)}")
+    if lses.dtype != torch.float32:
+        raise ValueError("lses must be float32")
+    N, T_max, H, D = outputs.shape
+    if not 0 <= num_tokens <= T_max:
+        raise ValueError(f"num_tokens must be in [0, {T_max}], got {num_tokens}")
+    for t in (outputs, lses):
+        if t.device.type != "cuda":
+            raise ValueError("tensors must live on a GPU device")
+        if N > 0 and not t[0].is_contiguous():
+            raise ValueError("each plane (dimension 0 index) must be contiguous")
+    if outputs.device != lses.device:
+        raise ValueError("all tensors must be on the same device")
+    dt, rdt = _result_dtype(outputs, out_dtype)
+    dev = outputs.device
+    T = int(num_tokens)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=rdt, device=dev)
+    if return_lse and out_lse is None:
+        out_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _check_out(out, (T, H, D), rdt, dev)
+    if return_lse:
+        _check_out(out_lse, (T, H), torch.float32, dev)
+    st = lib.lsec_combine_planes(_ptr(outputs), outputs.stride(0) if N > 1 else T * H * D,
+                                 _ptr(lses), lses.stride(0) if N > 1 else T * H, N, T, H, D, dt,
+                                 LSEC_BASE_E if base_e else LSEC_BASE_2, _ptr(out),
+                                 _ptr(out_lse) if return_lse else None, _stream(dev, stream))
+    _raise_on(st, "lsec_combine_planes")
     return (out, out_lse) if return_lse else out
 
 
@@ -380,5 +432,6 @@ def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
 __all__ = [
     "lsec_pack_dim", "lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
     "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
+    "lsec_combine_planes",
     "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
 ]

@@ -207,6 +207,12 @@ __device__ __forceinline__ u32x4 f32_chunk(float a, float b, float c, float d) {
 // Store a lane's kEpc results at element `idx` of `out` (16-byte aligned): in
 // the input dtype, or as fp32 when `out_f32` (16-bit inputs then write two
 // 16-byte chunks). fp32 inputs always give fp32 results.
+// The two chunks of an fp32 result go out as two store instructions, each
+// covering every other 16 bytes of the wave's span, so every cache line is
+// written in two halves. Measured on MI355X (N=16 D=128, 2^19 rows): with
+// non-temporal stores L2 writes about 18 % more than the result holds, and
+// with the default policy exactly the result, yet the default policy is 6 %
+// slower overall, so the stores stay non-temporal.
 template <int DT>
 __device__ __forceinline__ void store_chunk(void* out, uint64_t idx,
                                             const float (&acc)[Elem<DT>::kEpc], int out_f32) {
@@ -237,17 +243,19 @@ __device__ __forceinline__ void store_elem(void* out, int64_t idx, float v, int 
 // ---------------------------------------------------------------- combine (fast path)
 //
 // Row r of plane n starts at element n * plane + r * stride of `src`.
-// Separate layout (lsec_combine): stride = D, plane = rows * D, LSE n of row r
-// at lse[n * rows + r]. Packed layout (lsec_unpack_combine): stride = D + P,
-// plane = rows * (D + P), LSE = the fp32 in elements D .. D+P-1 of the row.
+// Separate layout (lsec_combine): stride = D, plane >= rows * D (rows * D
+// when dense; more when the planes are the leading rows of longer ones), LSE
+// n of row r at lse[n * lse_plane + r]. Packed layout (lsec_unpack_combine):
+// stride = D + P, plane = rows * (D + P), LSE = the fp32 in elements
+// D .. D+P-1 of the row.
 // Launch: a lane group of g = D / kEpc lanes owns a row; rows_per_block =
 // kBlock / g. Every lane loads the row's N LSE values itself (broadcasts
 // within the group) and issues all N chunk loads before it uses the first.
 template <int DT, int NT, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     const typename Elem<DT>::T* __restrict__ src, const float* __restrict__ lse, int n_rt,
-    uint32_t rows, FastDiv g, uint32_t rows_per_block, int64_t stride, int64_t plane, int D,
-    float scale, float inv_scale, void* __restrict__ out, int out_f32,
+    uint32_t rows, FastDiv g, uint32_t rows_per_block, int64_t stride, int64_t plane,
+    int64_t lse_plane, int D, float scale, float inv_scale, void* __restrict__ out, int out_f32,
     float* __restrict__ out_lse, OutMap om) {
     constexpr int E = Elem<DT>::kEpc;
     const uint32_t t = threadIdx.x;
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
 
     auto load_lse = [&](int n) -> float {
         if (PACKED) return ld_tail(rp + n * plane + D);
-        return lse[int64_t(n) * rows + row];
+        return lse[int64_t(n) * lse_plane + row];
     };
     auto load_chunk = [&](int n) -> u32x4 {
         if (PACKED) return ld16_a4(cp + n * plane);
@@ -345,9 +353,10 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
 // nothing but the weights stays live through it.
 //
 // Addresses: plane n starts at n * plane_bytes (uniform, scalar registers);
-// a lane's chunk sits at a 32-bit byte offset inside the plane. The host
-// checks plane_bytes < 2^32. Rows past the end of the last block are clamped
-// to the last row for loading and are not stored.
+// a lane's chunk sits at a 32-bit byte offset inside the plane; shard j's LSE
+// of row r is lse[j * lse_plane + r]. The host checks plane_bytes < 2^32 and
+// N * lse_plane < 2^32. Rows past the end of the last block are clamped to
+// the last row for loading and are not stored.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
@@ -408,8 +417,8 @@ constexpr int tiled_pg() {
 template <int DT, int NT, int G, int S, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     const void* src, const float* __restrict__ lse, uint32_t rows, uint32_t stride,
-    uint64_t plane_bytes, float scale, float inv_scale, void* __restrict__ out, int out_f32,
-    float* __restrict__ out_lse, OutMap om) {
+    uint64_t plane_bytes, uint32_t lse_plane, float scale, float inv_scale,
+    void* __restrict__ out, int out_f32, float* __restrict__ out_lse, OutMap om) {
     constexpr int E = Elem<DT>::kEpc;
     constexpr uint32_t ES = sizeof(typename Elem<DT>::T);
     constexpr int RPS = kBlock / G;  // rows per slot
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
             if (PACKED)
                 l = ld_tail(base + j * plane_bytes + (rc * stride + D) * ES);
             else
-                l = lse[j * rows + rc];
+                l = lse[j * lse_plane + rc];
         }
         lw[s] = l;
     }
@@ -498,9 +507,9 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
 template <int DT, bool PACKED>
 __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
     const typename Elem<DT>::T* __restrict__ src, const float* __restrict__ lse, int N,
-    int64_t rows, int64_t stride, int64_t plane, int64_t D, float scale, float inv_scale,
-    void* __restrict__ out, int out_f32, float* __restrict__ out_lse, int64_t map_a,
-    int64_t map_c) {
+    int64_t rows, int64_t stride, int64_t plane, int64_t lse_plane, int64_t D, float scale,
+    float inv_scale, void* __restrict__ out, int out_f32, float* __restrict__ out_lse,
+    int64_t map_a, int64_t map_c) {
     const int64_t total = rows * D;
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
          i += int64_t(gridDim.x) * kBlock) {
@@ -515,7 +524,7 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
                 else
                     return __uint_as_float(uint32_t(q[0]) | (uint32_t(q[1]) << 16));
             }
-            return lse[int64_t(n) * rows + row];
+            return lse[int64_t(n) * lse_plane + row];
         };
         float m = -__builtin_inff();
         for (int n = 0; n < N; ++n) m = fmaxf(m, sanitize(load_lse(n)));
@@ -777,25 +786,31 @@ bool fast_d(int64_t D, int64_t esize) {
     return D % epc == 0 && D / epc <= kBlock;
 }
 
+// Plane geometry of a combine: plane n of the partial outputs starts at
+// element n * plane, its LSEs at n * lse_plane (separate layout).
+struct Planes {
+    int64_t plane, lse_plane;
+};
+
 template <int DT, int NT, bool PACKED>
 void launch_combine_rows(const void* src, const float* lse, int N, uint32_t rows, int D,
-                         float scale, float inv_scale, void* out, int out_f32, float* out_lse,
-                         OutMap om, hipStream_t st) {
+                         Planes pl, float scale, float inv_scale, void* out, int out_f32,
+                         float* out_lse, OutMap om, hipStream_t st) {
     const uint32_t g = uint32_t(D / Elem<DT>::kEpc);
     const uint32_t rpb = kBlock / g;
     const unsigned blocks = (rows + rpb - 1) / rpb;
     const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
     combine_rows_kernel<DT, NT, PACKED><<<blocks, kBlock, 0, st>>>(
         static_cast<const typename Elem<DT>::T*>(src), lse, N, rows, make_fastdiv(g), rpb, stride,
-        int64_t(rows) * stride, D, scale, inv_scale, out, out_f32, out_lse, om);
+        pl.plane, pl.lse_plane, D, scale, inv_scale, out, out_f32, out_lse, om);
 }
 
 template <int DT, bool PACKED>
-void dispatch_n(const void* src, const float* lse, int N, uint32_t rows, int D, float scale,
-                float inv_scale, void* out, int out_f32, float* out_lse, OutMap om,
+void dispatch_n(const void* src, const float* lse, int N, uint32_t rows, int D, Planes pl,
+                float scale, float inv_scale, void* out, int out_f32, float* out_lse, OutMap om,
                 hipStream_t st) {
 #define LSEC_ROWS(NV) \
-    launch_combine_rows<DT, NV, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, out_f32, out_lse, om, st)
+    launch_combine_rows<DT, NV, PACKED>(src, lse, N, rows, D, pl, scale, inv_scale, out, out_f32, out_lse, om, st)
     switch (N) {
         case 1: LSEC_ROWS(1); break;
         case 2: LSEC_ROWS(2); break;
@@ -822,6 +837,7 @@ struct TiledArgs {
     const float* lse;
     uint32_t rows, stride;
     uint64_t plane_bytes;
+    uint32_t lse_plane;
     float scale, inv_scale;
     void* out;
     int out_f32;
@@ -836,8 +852,8 @@ void launch_tiled_s(int S, const TiledArgs& a) {
     const unsigned blocks = (a.rows + RPS * S - 1) / (RPS * S);
 #define LSEC_TILED(SV)                                                                         \
     combine_tiled_kernel<DT, NT, G, SV, PACKED><<<blocks, kBlock, 0, a.st>>>(                  \
-        a.src, a.lse, a.rows, a.stride, a.plane_bytes, a.scale, a.inv_scale, a.out, a.out_f32, \
-        a.out_lse, a.om)
+        a.src, a.lse, a.rows, a.stride, a.plane_bytes, a.lse_plane, a.scale, a.inv_scale, a.out, \
+        a.out_f32, a.out_lse, a.om)
     switch (S) {
         case 16: LSEC_TILED(16); break;
         case 8: LSEC_TILED(8); break;
@@ -877,16 +893,19 @@ struct CombinePlan {
     int S;  // row slots per lane (tiled path)
 };
 
+// `pl` gives the plane geometry of the separate layout (packed planes are
+// always dense).
 CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, int64_t esize, bool packed,
-                         bool fast) {
+                         bool fast, Planes pl) {
     if (!fast) return {kPathElems, 0};
     const bool tiled_shape = (D == 128 || D == 256 || D == 512) &&
                              (N == 2 || N == 4 || N == 8 || N == 16);
     if (tiled_shape) {
         const int64_t P = 4 / esize;
-        const uint64_t plane_bytes = uint64_t(rows) * uint64_t(packed ? D + P : D) * uint64_t(esize);
+        const uint64_t plane_bytes =
+            packed ? uint64_t(rows) * uint64_t(D + P) * uint64_t(esize) : uint64_t(pl.plane) * uint64_t(esize);
         const bool fits32 = plane_bytes < (uint64_t(1) << 32) &&
-                            (packed || uint64_t(N) * uint64_t(rows) < (uint64_t(1) << 32));
+                            (packed || uint64_t(N) * uint64_t(pl.lse_plane) < (uint64_t(1) << 32));
         if (fits32) {
             const uint64_t rps = kBlock / uint64_t(D * esize / 16);
             const uint64_t min_blocks = N >= 16 ? kTiledMinBlocksN16 : kTiledMinBlocks;
@@ -900,37 +919,39 @@ CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, int64_t esize, bool
 
 template <int DT, bool PACKED>
 void run_combine_dt(const void* src, const float* lse, int64_t N, int64_t rows, int64_t D,
-                    float scale, float inv_scale, void* out, int out_f32, float* out_lse,
-                    const CombinePlan& plan, OutMap om, int64_t map_a, int64_t map_c,
-                    hipStream_t st) {
+                    Planes pl, float scale, float inv_scale, void* out, int out_f32,
+                    float* out_lse, const CombinePlan& plan, OutMap om, int64_t map_a,
+                    int64_t map_c, hipStream_t st) {
     if (plan.kind == kPathTiled) {
         const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
         const TiledArgs a{src, lse, uint32_t(rows), uint32_t(stride),
-                          uint64_t(rows) * uint64_t(stride) * sizeof(typename Elem<DT>::T),
+                          uint64_t(pl.plane) * sizeof(typename Elem<DT>::T), uint32_t(pl.lse_plane),
                           scale, inv_scale, out, out_f32, out_lse, om, st};
         launch_tiled<DT, PACKED>(int(N), plan.S, int(D), a);
     } else if (plan.kind == kPathRows) {
-        dispatch_n<DT, PACKED>(src, lse, int(N), uint32_t(rows), int(D), scale, inv_scale, out,
-                               out_f32, out_lse, om, st);
+        dispatch_n<DT, PACKED>(src, lse, int(N), uint32_t(rows), int(D), pl, scale, inv_scale,
+                               out, out_f32, out_lse, om, st);
     } else {
         const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
         combine_elems_kernel<DT, PACKED><<<general_grid(rows * D), kBlock, 0, st>>>(
-            static_cast<const typename Elem<DT>::T*>(src), lse, int(N), rows, stride,
-            rows * stride, D, scale, inv_scale, out, out_f32, out_lse, map_a, map_c);
+            static_cast<const typename Elem<DT>::T*>(src), lse, int(N), rows, stride, pl.plane,
+            pl.lse_plane, D, scale, inv_scale, out, out_f32, out_lse, map_a, map_c);
     }
 }
 
+// Runs a validated combine. `pl` is the plane geometry in elements; packed
+// planes are dense (plane = rows * (D + P); lse_plane unused).
 template <bool PACKED>
 int run_combine(const void* src, const float* lse, int64_t N, int64_t rows, int64_t D,
                 const Dtype& dt, int base, void* out, float* out_lse, bool fast, hipStream_t st,
-                int64_t map_a = 0, int64_t map_c = 1) {
+                Planes pl, int64_t map_a = 0, int64_t map_c = 1) {
     const OutMap om{uint32_t(map_a), make_fastdiv(uint32_t(map_c))};
     const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
     const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
-    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, PACKED, fast);
+    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, PACKED, fast, pl);
     (void)hipGetLastError();
 #define LSEC_RUN(DTV)                                                                        \
-    run_combine_dt<DTV, PACKED>(src, lse, N, rows, D, scale, inv_scale, out, dt.out_f32, \
+    run_combine_dt<DTV, PACKED>(src, lse, N, rows, D, pl, scale, inv_scale, out, dt.out_f32, \
                                 out_lse, plan, om, map_a, map_c, st)
     switch (dt.in) {
         case LSEC_BF16: LSEC_RUN(LSEC_BF16); break;
@@ -1020,18 +1041,24 @@ void launch_unpack(bool fast, const void* recv, int64_t total_rows, int64_t D, i
     }
 }
 
-// Shared by lsec_combine and lsec_merge: rows (b, h) of a [B, H] grid, stored
-// in input order or, when `transposed`, at row h * B + b.
-int combine_entry(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
-                  int64_t D, int dtype, int base, void* out, float* out_lse, void* stream,
-                  bool transposed) {
+// Shared by lsec_combine, lsec_merge and lsec_combine_planes: rows (b, h) of a
+// [B, H] grid, stored in input order or, when `transposed`, at row h * B + b.
+// Plane n of the partial outputs starts at element n * plane_stride, its LSEs
+// at n * lse_plane_stride; the first B * H rows of each plane are combined.
+int combine_entry(const void* outputs, int64_t plane_stride, const float* lses,
+                  int64_t lse_plane_stride, int64_t N, int64_t B, int64_t H, int64_t D, int dtype,
+                  int base, void* out, float* out_lse, void* stream, bool transposed) {
     if (N < 1 || B < 0 || H < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
     Dtype dt;
     if (!parse_dtype(dtype, true, &dt)) return LSEC_ERR_DTYPE;
     if (base != LSEC_BASE_E && base != LSEC_BASE_2) return LSEC_ERR_BASE;
-    int64_t rows, rd, all, ob;
-    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, N, &all) ||
-        !mul_ok(all, dt.esize, &all) || !mul_ok(rd, dt.out_esize, &ob))
+    int64_t rows, rd, ob, span, lspan;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, dt.out_esize, &ob))
+        return LSEC_ERR_SHAPE;
+    if (plane_stride < rd || lse_plane_stride < rows) return LSEC_ERR_SHAPE;
+    if (!mul_ok(N - 1, plane_stride, &span) || __builtin_add_overflow(span, rd, &span) ||
+        !mul_ok(span, dt.esize, &span) || !mul_ok(N - 1, lse_plane_stride, &lspan) ||
+        __builtin_add_overflow(lspan, rows, &lspan) || !mul_ok(lspan, 4, &lspan))
         return LSEC_ERR_SHAPE;
     if (rows == 0) return LSEC_OK;
     if (!outputs || !lses || !out) return LSEC_ERR_NULL;
@@ -1039,10 +1066,10 @@ int combine_entry(const void* outputs, const float* lses, int64_t N, int64_t B, 
         (out_lse && !aligned(out_lse, 4)))
         return LSEC_ERR_ALIGNMENT;
     const bool fast = fast_d(D, dt.esize) && rows < (int64_t(1) << 31) && aligned(outputs, 16) &&
-                      aligned(out, 16);
+                      aligned(out, 16) && (plane_stride * dt.esize) % 16 == 0;
     return run_combine<false>(outputs, lses, N, rows, D, dt, base, out, out_lse, fast,
-                              static_cast<hipStream_t>(stream), transposed ? B : 0,
-                              transposed ? H : 1);
+                              static_cast<hipStream_t>(stream), Planes{plane_stride, lse_plane_stride},
+                              transposed ? B : 0, transposed ? H : 1);
 }
 
 }  // namespace
@@ -1082,7 +1109,9 @@ const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int dt
     if (N < 1 || B < 1 || H < 1 || D < 1 || !mul_ok(B, H, &rows) || !parse_dtype(dtype, true, &dt))
         return "none";
     const bool fast = aligned_buffers && fast_d(D, dt.esize) && rows < (int64_t(1) << 31);
-    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, packed != 0, fast);
+    int64_t rd;
+    if (!mul_ok(rows, D, &rd)) return "none";
+    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, packed != 0, fast, Planes{rd, rows});
     if (plan.kind == kPathElems) return "combine_elems_kernel";
     if (plan.kind == kPathRows) return "combine_rows_kernel";
     switch (plan.S) {
@@ -1094,17 +1123,33 @@ const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int dt
     }
 }
 
+// Dense planes: plane stride B*H*D elements, LSE plane stride B*H. When
+// those products overflow, combine_entry rejects the call (SHAPE).
+static int64_t dense_or_max(int64_t a, int64_t b, int64_t c) {
+    int64_t r;
+    if (a < 0 || b < 0 || c < 0 || !mul_ok(a, b, &r) || !mul_ok(r, c, &r)) return INT64_MAX;
+    return r;
+}
+
 int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
                  int64_t D, int dtype, int base, void* out, float* out_lse, void* stream) {
-    return combine_entry(outputs, lses, N, B, H, D, dtype, base, out, out_lse, stream, false);
+    return combine_entry(outputs, dense_or_max(B, H, D), lses, dense_or_max(B, H, 1), N, B, H, D,
+                         dtype, base, out, out_lse, stream, false);
+}
+
+int lsec_combine_planes(const void* outputs, int64_t plane_stride, const float* lses,
+                        int64_t lse_plane_stride, int64_t N, int64_t T, int64_t H, int64_t D,
+                        int dtype, int base, void* out, float* out_lse, void* stream) {
+    return combine_entry(outputs, plane_stride, lses, lse_plane_stride, N, T, H, D, dtype, base,
+                         out, out_lse, stream, false);
 }
 
 int lsec_merge(const void* outputs, const float* lses, int64_t N, int64_t A, int64_t C,
                int64_t D, int token_dim, int dtype, int base, void* out, float* out_lse,
                void* stream) {
     if (token_dim != 1 && token_dim != 2) return LSEC_ERR_TOKEN_DIM;
-    return combine_entry(outputs, lses, N, A, C, D, dtype, base, out, out_lse, stream,
-                         token_dim == 2);
+    return combine_entry(outputs, dense_or_max(A, C, D), lses, dense_or_max(A, C, 1), N, A, C, D,
+                         dtype, base, out, out_lse, stream, token_dim == 2);
 }
 
 int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, int dtype,
@@ -1125,7 +1170,7 @@ int lsec_unpack_combine(const void* recv, int64_t N, int64_t B, int64_t Hl, int6
     const bool fast = fast_d(D, dt.esize) && rows < (int64_t(1) << 31) && aligned(recv, 4) &&
                       aligned(out, 16);
     return run_combine<true>(recv, nullptr, N, rows, D, dt, base, out, out_lse, fast,
-                             static_cast<hipStream_t>(stream));
+                             static_cast<hipStream_t>(stream), Planes{rows * (D + P), 0});
 }
 
 int lsec_correct_partial(const float* lses, int64_t N, int64_t rank, const void* partial,

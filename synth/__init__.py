@@ -125,7 +125,7 @@ def f32_to_f16(x: float) -> int:
 class Workload:
     name: str
     wid: int
-    kind: str  # "combine", "packed", "merge" or "correct"
+    kind: str  # "combine", "packed", "merge", "correct" or "planes"
     N: int
     B: int
     H: int
@@ -177,6 +177,10 @@ WORKLOADS = {
         Workload("packed_f32", 9, "packed", 8, 2048, 64, 128, "f32", ("normal", 0.0, 1.0),
                  ("uniform", -5.0, 15.0), base2=False, return_lse=True,
                  desc="per-rank [2048,64,128] fp32 + [2048,64] fp32 -> [8,2048,8,129] fp32"),
+        Workload("direct_planes", 10, "planes", 8, 2048, 8, 128, "bf16", ("normal", 0.0, 1.0),
+                 ("uniform", -5.0, 15.0), base2=False, return_lse=True,
+                 desc="receive planes of a direct exchange: 8 ranks x [2048 of 4096 tokens, "
+                      "8 heads, 128] bf16 + LSEs -> [2048, 8, 128] (one ubatch slot)"),
         Workload("large_batch", 5, "combine", 16, 16384, 32, 128, "bf16", ("normal", 0.0, 1.0),
                  ("uniform", -10.0, 30.0),
                  special=((0.005 / 3, float("nan")), (0.005 / 3, float("inf")),
@@ -219,7 +223,8 @@ def combine_inputs(w: Workload | str, seed: int = 0, b_lo: int = 0, b_hi: int | 
     w = WORKLOADS[w] if isinstance(w, str) else w
     if w.kind == "packed":
         raise ValueError(f"{w.name} is a packed workload; use rank_inputs()")
-    # "correct" workloads draw all N shards; the caller uses one rank's plane
+    # "correct" workloads draw all N shards; the caller uses one rank's plane;
+    # "planes" workloads draw the B valid tokens of each receive plane
     b_hi = w.B if b_hi is None else b_hi
     if not (0 <= b_lo <= b_hi <= w.B):
         raise ValueError("token range out of bounds")

@@ -31,7 +31,8 @@ def _declared():
 def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("lsec_combine", "lsec_merge", "lsec_pack_send", "lsec_unpack_combine",
-              "lsec_unpack", "lsec_pack_dim", "lsec_status_string", "lsec_version"):
+              "lsec_unpack", "lsec_pack_dim", "lsec_status_string", "lsec_version",
+              "lsec_combine_planes", "lsec_correct_partial", "lsec_combine_path"):
         assert n in names
 
 
@@ -186,3 +187,19 @@ def test_correct_partial_validation(lib):
     assert c(None, 4, 1, FAKE, 2, 3, 8, 0, 0, FAKE, None, None) == 1    # NULL lses
     assert c(FAKE, 4, 1, FAKE + 1, 2, 3, 8, 0, 0, FAKE, None, None) == 5  # odd partial
     assert c(None, 4, 1, None, 0, 3, 8, 0, 0, None, None, None) == 0    # empty
+
+
+def test_combine_planes_validation(lib):
+    c = lib.lsec_combine_planes
+    # outputs, plane_stride, lses, lse_plane_stride, N, T, H, D, dtype, base, out, out_lse, stream
+    assert c(FAKE, 2 * 3 * 8 - 1, FAKE, 6, 2, 2, 3, 8, 0, 0, FAKE, None, None) == 2  # stride < plane
+    assert c(FAKE, 48, FAKE, 5, 2, 2, 3, 8, 0, 0, FAKE, None, None) == 2      # lse stride < plane
+    assert c(FAKE, 1 << 62, FAKE, 6, 3, 2, 3, 8, 0, 0, FAKE, None, None) == 2  # span overflows
+    assert c(FAKE, 48, FAKE, 1 << 62, 3, 2, 3, 8, 0, 0, FAKE, None, None) == 2  # lse span overflows
+    assert c(None, 64, FAKE, 8, 2, 2, 3, 8, 0, 0, FAKE, None, None) == 1
+    assert c(FAKE, 64, FAKE, 8, 2, 2, 3, 8, 9, 0, FAKE, None, None) == 4
+    assert c(FAKE, 64, FAKE, 8, 2, 2, 3, 8, 0, 7, FAKE, None, None) == 6
+    assert c(FAKE + 1, 64, FAKE, 8, 2, 2, 3, 8, 0, 0, FAKE, None, None) == 5
+    assert c(FAKE, 64, FAKE + 2, 8, 2, 2, 3, 8, 0, 0, FAKE, None, None) == 5
+    assert c(None, 64, None, 8, 2, 0, 3, 8, 0, 0, None, None, None) == 0      # T = 0
+    assert c(FAKE, 64, FAKE, 8, 0, 2, 3, 8, 0, 0, FAKE, None, None) == 2      # N < 1

@@ -368,6 +368,66 @@ def test_merge_page_alias(lsec):
     assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
 
 
+# ---------------------------------------------------------------- receive planes of the direct exchange
+
+PLANES = [
+    # W, T, T_max, H, D, dtype, base2   (path)
+    (8, 3000, 4096, 16, 128, "bf16", False),  # tiled
+    (4, 777, 1024, 8, 512, "f16", True),      # tiled, one wave per row
+    (8, 2051, 2304, 8, 128, "f32", False),    # tiled fp32
+    (3, 50, 64, 4, 128, "bf16", True),        # row kernel (N = 3)
+    (2, 9, 16, 4, 12, "bf16", False),         # element kernel (D % 8 != 0)
+    (4, 0, 16, 4, 128, "bf16", False),        # no valid tokens
+    (4, 16, 16, 4, 128, "bf16", False),       # T = T_max: the dense combine
+]
+
+
+@pytest.mark.parametrize("W,T,T_max,H,D,dtype,base2", PLANES)
+def test_combine_planes_of_a_ubatch_slot(lsec, W, T, T_max, H, D, dtype, base2):
+    """A [U=2, 2, W, T_max, H, D] receive buffer whose tokens past T hold NaN
+    (stale data of an earlier step): the combine of ubatch 1, slot 0 reads
+    only the first T tokens of each plane."""
+    _announce(f"combine_planes W={W} T={T} T_max={T_max} H={H} D={D} {dtype}")
+    o, l = synth.custom_inputs(W, T_max, H, D, dtype=dtype, seed=T_max + D, special=SPECIALS)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    buf = torch.full((2, 2, W, T_max, H, D), float("nan"), dtype=tdt, device=DEV)
+    lbuf = torch.full((2, 2, W, T_max, H), float("nan"), device=DEV)
+    buf[1, 0, :, :T] = to_dev(o, dtype, DEV)[:, :T]
+    lbuf[1, 0, :, :T] = f32_to_dev(l, DEV)[:, :T]
+    y, L = lsec.lsec_combine_planes(buf[1, 0], lbuf[1, 0], T, base_e=not base2, return_lse=True)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (T, H, D)
+    if T == 0:
+        return
+    oT = np.ascontiguousarray(o[:, :T])
+    y_ref, L_ref = oracle.lse_combine(oT, np.ascontiguousarray(l[:, :T]), dtype, base2)
+    assert_output_close(y, y_ref, dtype, max_abs_input(oT, dtype))
+    assert_lse_close(L, L_ref)
+
+
+def test_combine_planes_padded_stride(lsec):
+    """Planes 4 elements apart beyond their size (stride not a multiple of 16
+    bytes: the general kernel) and the same data as a leading-token view."""
+    W, T, H, D = 4, 37, 8, 128
+    _announce("combine_planes padded stride")
+    o, l = synth.custom_inputs(W, T, H, D, seed=88, special=SPECIALS)
+    pad = T * H * D + 4
+    flat = torch.full((W * pad,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    view = flat.as_strided((W, T, H, D), (pad, H * D, D, 1))
+    view.copy_(to_dev(o, "bf16", DEV))
+    lflat = torch.full((W * (T * H + 3),), float("nan"), device=DEV)
+    lview = lflat.as_strided((W, T, H), (T * H + 3, H, 1))
+    lview.copy_(f32_to_dev(l, DEV))
+    y, L = lsec.lsec_combine_planes(view, lview, T, return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.lse_combine(o, l, "bf16")
+    assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
+    assert_lse_close(L, L_ref)
+    with pytest.raises(ValueError):  # overlapping planes
+        lsec.lsec_combine_planes(flat.as_strided((W, T, H, D), (T * H * D - 8, H * D, D, 1)),
+                                 lview, T)
+
+
 # ---------------------------------------------------------------- all-gather + reduce-scatter local step
 
 CORRECT = [
