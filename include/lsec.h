@@ -105,9 +105,9 @@ int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, i
 
 /*
  * lsec_combine_planes -- lsec_combine over planes that are the leading rows of
- * longer ones: the local combine of the page's fused direct all-to-all
- * (`DirectDCPA2AWorkspace.lse_reduce`, page "vllm.v1.attention.ops.
- * dcp_alltoall"), whose receive buffers hold, per ubatch and slot, W planes
+ * longer ones: the local combine of the fused direct all-to-all of the page
+ * "vllm.v1.attention.ops.dcp" (`DirectDCPA2AWorkspace.lse_reduce`), whose
+ * receive buffers hold, per ubatch and slot, W planes
  * [W, T_max, H_r, D] (+ LSEs [W, T_max, H_r]) of which the first T tokens
  * belong to the current step. The caller picks the ubatch and slot by the
  * base pointers; the library reads nothing beyond the first T tokens.

@@ -23,8 +23,9 @@ Entry points (same names as the C ABI):
   combine over received planes, stored token-major.
 
 * ``lsec_combine_planes(outputs, lses, num_tokens)`` -- the local combine of
-  that page's fused direct all-to-all (``DirectDCPA2AWorkspace.lse_reduce``):
-  the first ``num_tokens`` tokens of one ubatch slot's receive planes.
+  the fused direct all-to-all on the page "vllm.v1.attention.ops.dcp"
+  (``DirectDCPA2AWorkspace.lse_reduce``): the first ``num_tokens`` tokens of
+  one ubatch slot's receive planes.
 
 * ``lsec_correct_partial(lses, rank, partial)`` -- the local step of the LSE
   all-gather + output reduce-scatter strategies named on the page
