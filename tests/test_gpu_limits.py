@@ -1,0 +1,109 @@
+"""GPU parity at the limits of the kernels' index arithmetic.
+
+The tiled combine addresses a lane's chunk by a 32-bit byte offset inside its
+plane, so it serves planes below 4 GiB; larger planes take the row kernel,
+which uses 64-bit offsets. These tests run a plane just below and just above
+4 GiB (8.6 GB of partial outputs each) and check sampled token ranges at the
+start, the middle and the very end of the planes against the oracle (rows are
+independent, so the oracle's result on a token slice of the inputs is exactly
+those rows' result).
+"""
+import gc
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import assert_lse_close, assert_output_close, f32_to_dev, max_abs_input, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+SPECIALS = ((0.01, float("nan")), (0.01, float("inf")), (0.01, float("-inf")))
+
+
+@pytest.fixture(scope="module")
+def lsec():
+    import lse_weighted_merge_combine_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    m.load_library()
+    return m
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _release():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _workload(N, B, H, D, wid):
+    return synth.Workload(f"limit_{wid}", wid, "combine", N, B, H, D, "bf16", ("normal", 0.0, 1.0),
+                          ("uniform", -10.0, 30.0), special=SPECIALS)
+
+
+def _ranges(B):
+    return ((0, 64), (B // 2 - 32, B // 2 + 32), (B - 64, B))
+
+
+@pytest.mark.parametrize("B,path", [
+    (524287, "combine_tiled_kernel S=16"),   # plane = 4,294,959,104 B: the largest 32-bit plane here
+    (524289, "combine_rows_kernel"),         # plane = 4,294,983,680 B > 2^32: 64-bit offsets
+])
+def test_combine_around_4gib_planes(lsec, B, path):
+    N, H, D = 2, 32, 128
+    _announce(f"combine N={N} B={B} H={H} D={D} bf16 ({B * H * D * 2} B per plane)")
+    assert lsec.lsec_combine_path(N, B, H, D) == path
+    w = _workload(N, B, H, D, 120 + (B & 7))
+    o, l = synth.combine_inputs(w)
+    M = max_abs_input(o[:, :64], "bf16")
+    og, lg = to_dev(o, "bf16", DEV), f32_to_dev(l, DEV)
+    del o, l
+    y, L = lsec.lsec_combine(og, lg, base_e=True, return_lse=True)
+    torch.cuda.synchronize()
+    del og, lg
+    for s, e in _ranges(B):
+        os_, ls_ = synth.combine_inputs(w, b_lo=s, b_hi=e)
+        y_ref, L_ref = oracle.lse_combine(os_, ls_, "bf16")
+        Ms = max(M, max_abs_input(os_, "bf16"))
+        assert_output_close(y[s:e], y_ref, "bf16", Ms, f"tokens {s}:{e}")
+        assert_lse_close(L[s:e], L_ref, f"tokens {s}:{e}")
+    del y, L
+    _release()
+
+
+@pytest.mark.parametrize("B,path", [
+    (516222, "combine_tiled_kernel S=16"),   # packed plane = 4,294,967,040 B, 256 B under 2^32
+    (516223, "combine_rows_kernel"),
+])
+def test_unpack_combine_around_4gib_planes(lsec, B, path):
+    """Packed receive planes [2, B, 32, 130] built on the host from generated
+    planes (output row, then the LSE's bytes)."""
+    N, Hl, D = 2, 32, 128
+    _announce(f"unpack_combine N={N} B={B} Hl={Hl} D={D} bf16 ({B * Hl * (D + 2) * 2} B per plane)")
+    assert lsec.lsec_combine_path(N, B, Hl, D, packed=True) == path
+    w = _workload(N, B, Hl, D, 130 + (B & 7))
+    o, l = synth.combine_inputs(w)
+    recv = np.empty((N, B, Hl, D + 2), dtype=np.uint16)
+    recv[..., :D] = o
+    recv[..., D:] = l.view(np.uint16).reshape(N, B, Hl, 2)
+    del o, l
+    rg = to_dev(recv, "bf16", DEV)
+    y, L = lsec.lsec_unpack_combine(rg, base_e=True, return_lse=True)
+    torch.cuda.synchronize()
+    del rg
+    for s, e in _ranges(B):
+        part = np.ascontiguousarray(recv[:, s:e])
+        y_ref, L_ref = oracle.unpack_combine(part, D, "bf16")
+        oo, _ = oracle.unpack(part, D)
+        assert_output_close(y[s:e], y_ref, "bf16", max_abs_input(oo, "bf16"), f"tokens {s}:{e}")
+        assert_lse_close(L[s:e], L_ref, f"tokens {s}:{e}")
+    del recv, y, L
+    _release()
