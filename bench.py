@@ -220,7 +220,8 @@ def build_workload(name: str, dev, out_f32: bool = False):
             lsec.lsec_unpack_combine(recv, base_e=not w.base2, return_lse=True, out=out,
                                      out_lse=out_lse)
 
-        kernels = [(f"pack_rows_kernel ({w.dtype})", pack_bytes(w.N, w.B, w.H, w.D, s), pack),
+        pack_kernel = "pack_lds_kernel" if send.data_ptr() % 16 == 0 else "pack_rows_kernel"
+        kernels = [(f"{pack_kernel} ({w.dtype})", pack_bytes(w.N, w.B, w.H, w.D, s), pack),
                    (f"{lsec.lsec_combine_path(w.N, w.B, Hl, w.D, packed=True, dtype=tdt)} "
                     f"({w.dtype}, N={w.N}, D={w.D}, packed rows)",
                     unpack_combine_bytes(w.N, w.B, Hl, w.D, s, True), unpack_combine)]

@@ -625,7 +625,7 @@ __global__ __launch_bounds__(kBlock) void correct_elems_kernel(
     }
 }
 
-// ---------------------------------------------------------------- pack (fast path)
+// ---------------------------------------------------------------- pack (fast paths)
 //
 // Send row s = (r * B + b) * Hl + hl takes attention-output row
 // src = b * H + r * Hl + hl: D elements, then the fp32 LSE's 32 bits in the P
@@ -670,6 +670,68 @@ __global__ __launch_bounds__(kBlock) void pack_rows_kernel(
             if (lane == 0) st_tail(dp + D, lv[k]);
         }
     }
+}
+
+// Pack through LDS (16-byte aligned send buffers). A block owns
+// R = kPackRows * rows_per_block consecutive send rows: one contiguous span
+// of R * (D + P) elements that starts on a 16-byte boundary, since R is a
+// multiple of 4 and a packed row is 4 bytes past a multiple of 16. The rows
+// are assembled in LDS at their packed offsets (dword writes; the rows are
+// only 4-byte aligned), then the span leaves as aligned, coalesced 16-byte
+// non-temporal stores. Measured on MI355X ([2048,64,128] bf16 -> 8 planes):
+// 8 % faster than storing the 4-byte aligned rows directly.
+constexpr int kPackLdsBytes = 5120 * kPackRows;  // max over g of (256/g) * kPackRows * (16g + 4)
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void pack_lds_kernel(
+    const T* __restrict__ in, const float* __restrict__ lse, uint32_t send_rows, FastDiv g,
+    uint32_t rows_per_block, FastDiv hl_div, FastDiv b_div, uint32_t H, int D,
+    T* __restrict__ send) {
+    constexpr int E = 16 / sizeof(T);
+    constexpr int P = 4 / sizeof(T);
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kPackLdsBytes / 4];
+    const uint32_t t = threadIdx.x;
+    const uint32_t rib = fdiv(t, g);
+    const uint32_t lane = t - rib * g.d;
+    const uint32_t row_dw = uint32_t(D + P) * sizeof(T) / 4;  // dwords per packed row
+    const uint32_t R = kPackRows * rows_per_block;
+    const uint32_t first = blockIdx.x * R;
+    if (rib < rows_per_block) {
+        u32x4 v[kPackRows];
+        float lv[kPackRows];
+#pragma unroll
+        for (int k = 0; k < kPackRows; ++k) {
+            const uint32_t q = first + k * rows_per_block + rib;
+            const uint32_t s = q < send_rows ? q : send_rows - 1;  // clamp: load a valid row
+            const uint32_t rb = fdiv(s, hl_div);
+            const uint32_t hl = s - rb * hl_div.d;
+            const uint32_t r = fdiv(rb, b_div);
+            const uint32_t b = rb - r * b_div.d;
+            const uint32_t src = b * H + r * hl_div.d + hl;
+            v[k] = ld16(in + int64_t(src) * D + lane * E);
+            lv[k] = lse[src];
+        }
+#pragma unroll
+        for (int k = 0; k < kPackRows; ++k) {
+            uint32_t* rowp = stage + (k * rows_per_block + rib) * row_dw;
+            uint32_t* cp = rowp + lane * 4;
+            cp[0] = v[k].x;
+            cp[1] = v[k].y;
+            cp[2] = v[k].z;
+            cp[3] = v[k].w;
+            if (lane == 0) rowp[row_dw - 1] = __float_as_uint(lv[k]);  // the P tail elements
+        }
+    }
+    __syncthreads();
+    // Rows past send_rows were staged from clamped loads but are not stored.
+    const uint32_t nrows = send_rows - first < R ? send_rows - first : R;
+    const uint32_t ndw = nrows * row_dw;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(send) + uint64_t(first) * row_dw;
+    const uint32_t nfull = ndw / 4;
+    for (uint32_t c = t; c < nfull; c += kBlock)
+        __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(stage)[c],
+                                    reinterpret_cast<u32x4*>(dst) + c);
+    for (uint32_t d = nfull * 4 + t; d < ndw; d += kBlock) dst[d] = stage[d];  // last block's tail
 }
 
 // ---------------------------------------------------------------- pack (general path)
@@ -1014,10 +1076,17 @@ void launch_pack(bool fast, const void* attn_out, const float* lse, int64_t B, i
         const uint32_t g = uint32_t(D / (16 / sizeof(T)));
         const uint32_t rpb = kBlock / g;
         const unsigned blocks = unsigned((rows + rpb * kPackRows - 1) / (rpb * kPackRows));
-        pack_rows_kernel<T><<<blocks, kBlock, 0, st>>>(in, lse, uint32_t(rows), make_fastdiv(g),
-                                                       rpb, make_fastdiv(uint32_t(Hl)),
-                                                       make_fastdiv(uint32_t(B)), uint32_t(H),
-                                                       int(D), dst);
+        if (aligned(send, 16))
+            pack_lds_kernel<T><<<blocks, kBlock, 0, st>>>(in, lse, uint32_t(rows), make_fastdiv(g),
+                                                          rpb, make_fastdiv(uint32_t(Hl)),
+                                                          make_fastdiv(uint32_t(B)), uint32_t(H),
+                                                          int(D), dst);
+        else
+            pack_rows_kernel<T><<<blocks, kBlock, 0, st>>>(in, lse, uint32_t(rows),
+                                                           make_fastdiv(g), rpb,
+                                                           make_fastdiv(uint32_t(Hl)),
+                                                           make_fastdiv(uint32_t(B)), uint32_t(H),
+                                                           int(D), dst);
     } else {
         pack_elems_kernel<T><<<general_grid(total), kBlock, 0, st>>>(in, lse, B, H, Hl, D, total,
                                                                       dst);

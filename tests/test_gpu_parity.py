@@ -321,6 +321,25 @@ def test_misaligned_buffers_take_general_path(lsec):
     assert_lse_close(L2, L2r)
 
 
+@pytest.mark.parametrize("dtype,shift", [("bf16", 2), ("f16", 6), ("f32", 1)])
+def test_pack_into_4byte_aligned_send(lsec, dtype, shift):
+    """A send buffer 4 bytes (or 12) past a 16-byte boundary: the pack stores
+    the packed rows directly instead of staging whole 16-byte chunks in LDS."""
+    N, B, H, D = 4, 37, 8, 128
+    _announce(f"pack into a 4-byte aligned send buffer {dtype}")
+    o, l = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=41, special=SPECIALS)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    P = lsec.lsec_pack_dim(tdt)
+    flat = torch.empty(N * B * (H // N) * (D + P) + shift, dtype=tdt, device=DEV)
+    send = flat[shift:].view(N, B, H // N, D + P)
+    assert send.data_ptr() % 16 != 0 and send.data_ptr() % 4 == 0
+    lsec.lsec_pack_send(to_dev(o[0], dtype, DEV), f32_to_dev(l[0], DEV), N, send=send)
+    torch.cuda.synchronize()
+    ref = oracle.pack_send(o[0], l[0], N, dtype=dtype)
+    got = f32_bits_of(send) if dtype == "f32" else bits_of(send)
+    assert np.array_equal(got, ref)
+
+
 # ---------------------------------------------------------------- token-major merge
 
 MERGE = [
