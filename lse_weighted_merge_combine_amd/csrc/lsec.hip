@@ -66,9 +66,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// The same four dwords at 4-byte alignment (packed rows start every D + P
-// elements, i.e. on 4-byte boundaries).
+// The same four (two) dwords at 4-byte alignment (packed rows start every
+// D + P elements, i.e. on 4-byte boundaries).
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 
 // Every input byte is read once and every output byte written once, so all
 // streaming accesses are non-temporal (the `nt` cache policy); on MI355X plain
@@ -209,10 +210,10 @@ __device__ __forceinline__ u32x4 f32_chunk(float a, float b, float c, float d) {
 // 16-byte chunks). fp32 inputs always give fp32 results.
 // The two chunks of an fp32 result go out as two store instructions, each
 // covering every other 16 bytes of the wave's span, so every cache line is
-// written in two halves. Measured on MI355X (N=16 D=128, 2^19 rows): with
-// non-temporal stores L2 writes about 18 % more than the result holds, and
-// with the default policy exactly the result, yet the default policy is 6 %
-// slower overall, so the stores stay non-temporal.
+// written in two halves (non-temporal stores then write 17-18 % more than the
+// result holds; the default policy writes exactly the result but measured
+// slower). The tiled combine avoids this layout (split loads, below); the
+// row and element kernels keep it.
 template <int DT>
 __device__ __forceinline__ void store_chunk(void* out, uint64_t idx,
                                             const float (&acc)[Elem<DT>::kEpc], int out_f32) {
@@ -414,11 +415,19 @@ constexpr int tiled_pg() {
     return (S >= 4 ? 1 : (8 / S < NT ? 8 / S : NT));
 }
 
-template <int DT, int NT, int G, int S, bool PACKED>
+// SPLIT (fp32 result from 16-bit partials): lane l of a row owns elements
+// [4l, 4l + 4) and [D/2 + 4l, D/2 + 4l + 4) instead of [8l, 8l + 8), read as
+// two 8-byte loads, so each of its two 16-byte fp32 stores belongs to an
+// instruction that writes one contiguous half of the row (whole cache
+// lines). Measured on MI355X: 6.6 % faster on N=16 D=128 2^19 rows, 4.5 % on
+// N=8 D=512 2^16 rows, than 16-byte loads with two interleaved stores.
+// Otherwise the result has the input dtype.
+template <int DT, int NT, int G, int S, bool PACKED, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     const void* src, const float* __restrict__ lse, uint32_t rows, uint32_t stride,
     uint64_t plane_bytes, uint32_t lse_plane, float scale, float inv_scale,
-    void* __restrict__ out, int out_f32, float* __restrict__ out_lse, OutMap om) {
+    void* __restrict__ out, float* __restrict__ out_lse, OutMap om) {
+    static_assert(!SPLIT || DT != LSEC_FP32, "fp32 partials already give fp32 results");
     constexpr int E = Elem<DT>::kEpc;
     constexpr uint32_t ES = sizeof(typename Elem<DT>::T);
     constexpr int RPS = kBlock / G;  // rows per slot
@@ -439,7 +448,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     for (int s = 0; s < S; ++s) {
         row[s] = row0 + s * RPS + rib;
         const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
-        off[s] = (rc * stride + lane * E) * ES;
+        off[s] = (rc * stride + lane * (SPLIT ? E / 2 : E)) * ES;
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -463,7 +472,17 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
         for (int p = 0; p < PG; ++p) {
             const char* pb = base + uint64_t(n0 + p) * plane_bytes;
 #pragma unroll
-            for (int s = 0; s < S; ++s) v[p][s] = PACKED ? ld16_a4_at(pb + off[s]) : ld16_nt_at(pb + off[s]);
+            for (int s = 0; s < S; ++s) {
+                if constexpr (SPLIT) {
+                    const u32x2_a4 lo = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x2_a4*>(pb + off[s]));
+                    const u32x2_a4 hi = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x2_a4*>(pb + off[s] + D * ES / 2));
+                    v[p][s] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                } else {
+                    v[p][s] = PACKED ? ld16_a4_at(pb + off[s]) : ld16_nt_at(pb + off[s]);
+                }
+            }
         }
     };
     load_group(0);
@@ -495,8 +514,16 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
             for (int s = 0; s < S; ++s) fma_chunk<DT>(v[p][s], lane_value<G>(lw[s], n0 + p), acc[s]);
     }
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-        if (row[s] < rows) store_chunk<DT>(out, uint64_t(out_row(row[s], om)) * D + lane * E, acc[s], out_f32);
+    for (int s = 0; s < S; ++s) {
+        if (row[s] >= rows) continue;
+        if constexpr (SPLIT) {
+            float* p = static_cast<float*>(out) + uint64_t(out_row(row[s], om)) * D + lane * 4;
+            st16(p, f32_chunk(acc[s][0], acc[s][1], acc[s][2], acc[s][3]));
+            st16(p + D / 2, f32_chunk(acc[s][4], acc[s][5], acc[s][6], acc[s][7]));
+        } else {
+            store_chunk<DT>(out, uint64_t(out_row(row[s], om)) * D + lane * E, acc[s], 0);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- combine (general path)
@@ -908,14 +935,14 @@ struct TiledArgs {
     hipStream_t st;
 };
 
-template <int DT, int NT, int G, bool PACKED>
+template <int DT, int NT, int G, bool PACKED, bool SPLIT>
 void launch_tiled_s(int S, const TiledArgs& a) {
     constexpr uint32_t RPS = kBlock / G;
     const unsigned blocks = (a.rows + RPS * S - 1) / (RPS * S);
 #define LSEC_TILED(SV)                                                                         \
-    combine_tiled_kernel<DT, NT, G, SV, PACKED><<<blocks, kBlock, 0, a.st>>>(                  \
+    combine_tiled_kernel<DT, NT, G, SV, PACKED, SPLIT><<<blocks, kBlock, 0, a.st>>>(           \
         a.src, a.lse, a.rows, a.stride, a.plane_bytes, a.lse_plane, a.scale, a.inv_scale, a.out, \
-        a.out_f32, a.out_lse, a.om)
+        a.out_lse, a.om)
     switch (S) {
         case 16: LSEC_TILED(16); break;
         case 8: LSEC_TILED(8); break;
@@ -926,24 +953,36 @@ void launch_tiled_s(int S, const TiledArgs& a) {
 #undef LSEC_TILED
 }
 
-template <int DT, int G, bool PACKED>
+template <int DT, int G, bool PACKED, bool SPLIT>
 void launch_tiled_n(int N, int S, const TiledArgs& a) {
     switch (N) {
-        case 2: launch_tiled_s<DT, 2, G, PACKED>(S, a); break;
-        case 4: launch_tiled_s<DT, 4, G, PACKED>(S, a); break;
-        case 8: launch_tiled_s<DT, 8, G, PACKED>(S, a); break;
-        default: launch_tiled_s<DT, 16, G, PACKED>(S, a); break;
+        case 2: launch_tiled_s<DT, 2, G, PACKED, SPLIT>(S, a); break;
+        case 4: launch_tiled_s<DT, 4, G, PACKED, SPLIT>(S, a); break;
+        case 8: launch_tiled_s<DT, 8, G, PACKED, SPLIT>(S, a); break;
+        default: launch_tiled_s<DT, 16, G, PACKED, SPLIT>(S, a); break;
     }
 }
 
-template <int DT, bool PACKED>
-void launch_tiled(int N, int S, int D, const TiledArgs& a) {
+template <int DT, bool PACKED, bool SPLIT>
+void launch_tiled_d(int N, int S, int D, const TiledArgs& a) {
     constexpr int E = Elem<DT>::kEpc;
     switch (D) {
-        case 128: launch_tiled_n<DT, 128 / E, PACKED>(N, S, a); break;
-        case 256: launch_tiled_n<DT, 256 / E, PACKED>(N, S, a); break;
-        default: launch_tiled_n<DT, 512 / E, PACKED>(N, S, a); break;
+        case 128: launch_tiled_n<DT, 128 / E, PACKED, SPLIT>(N, S, a); break;
+        case 256: launch_tiled_n<DT, 256 / E, PACKED, SPLIT>(N, S, a); break;
+        default: launch_tiled_n<DT, 512 / E, PACKED, SPLIT>(N, S, a); break;
     }
+}
+
+// 16-bit partials with an fp32 result take the split-load variant.
+template <int DT, bool PACKED>
+void launch_tiled(int N, int S, int D, const TiledArgs& a) {
+    if constexpr (DT != LSEC_FP32) {
+        if (a.out_f32) {
+            launch_tiled_d<DT, PACKED, true>(N, S, D, a);
+            return;
+        }
+    }
+    launch_tiled_d<DT, PACKED, false>(N, S, D, a);
 }
 
 // Which combine kernel serves a call. `fast` = fast_d(D), rows < 2^31 and the
