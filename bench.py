@@ -25,9 +25,9 @@ already resident in HBM:
 * ``packed_f32``: the ``packed`` pair on fp32 outputs (packed rows of D + 1
   fp32 elements, the LSE in the last).
 
-``--out-f32`` asks the combine workloads for an fp32 result from 16-bit
-partials (the promoted dtype of the page's CPU combine) instead of a result in
-the input dtype.
+``--out-f32`` asks the combine and corrected-partial workloads for an fp32
+result from 16-bit partials (the promoted dtype of the page's CPU combine)
+instead of a result in the input dtype.
 
 Workloads under 1 GiB are timed cold: a 1 GiB buffer is rewritten before each
 step, outside the timed events. Kernel time comes from HIP events recorded on
@@ -109,8 +109,8 @@ def build_workload(name: str, dev, out_f32: bool = False):
     w = synth.WORKLOADS[name]
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
     s = 4 if w.dtype == "f32" else 2
-    if out_f32 and w.kind != "combine":
-        raise SystemExit("--out-f32 applies to the combine workloads only")
+    if out_f32 and w.kind not in ("combine", "correct"):
+        raise SystemExit("--out-f32 applies to the combine and correct workloads only")
     odt = torch.float32 if out_f32 else tdt
     os_ = 4 if odt == torch.float32 else 2
 
@@ -131,13 +131,14 @@ def build_workload(name: str, dev, out_f32: bool = False):
         part = dev_bits(o[rank])
         lg = torch.from_numpy(l).to(dev)
         del o
-        out = torch.empty((w.B, w.H, w.D), dtype=tdt, device=dev)
+        out = torch.empty((w.B, w.H, w.D), dtype=odt, device=dev)
         rows = w.B * w.H
-        nbytes = w.N * rows * 4 + 2 * rows * w.D * s
-        kname = f"correct_tiled_kernel ({w.dtype}, N={w.N}, D={w.D}, rank {rank})"
+        nbytes = w.N * rows * 4 + rows * w.D * s + rows * w.D * os_
+        res = " -> f32" if out_f32 and s == 2 else ""
+        kname = f"correct_tiled_kernel ({w.dtype}{res}, N={w.N}, D={w.D}, rank {rank})"
 
         def step():
-            lsec.lsec_correct_partial(lg, rank, part, base_e=not w.base2, out=out)
+            lsec.lsec_correct_partial(lg, rank, part, base_e=not w.base2, out=out, out_dtype=odt)
 
         kernels = [(kname, nbytes, step)]
         host = None

@@ -579,11 +579,14 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
 // normalisation as the combine, then one plane read and one written.
 // Tiled path for D in {128, 256, 512} and N <= 16: G = D / kEpc lanes per row,
 // S row slots per lane, lane j of each 16-lane DPP row loads shard j's LSE.
-template <int DT, int G, int S>
+// SPLIT (fp32 result from 16-bit partials) as in combine_tiled_kernel: a lane
+// owns elements [4l, 4l + 4) and [D/2 + 4l, D/2 + 4l + 4) of its row.
+template <int DT, int G, int S, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
     const float* __restrict__ lse, int N, int rank, const typename Elem<DT>::T* __restrict__ part,
-    uint32_t rows, float scale, float inv_scale, void* __restrict__ out, int out_f32,
+    uint32_t rows, float scale, float inv_scale, void* __restrict__ out,
     float* __restrict__ out_lse) {
+    static_assert(!SPLIT || DT != LSEC_FP32, "fp32 partials already give fp32 results");
     constexpr int E = Elem<DT>::kEpc;
     constexpr int RPS = kBlock / G;
     constexpr int D = G * E;
@@ -604,7 +607,14 @@ __global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
-        v[s] = ld16(part + uint64_t(rc) * D + lane * E);
+        if constexpr (SPLIT) {
+            const auto* p = part + uint64_t(rc) * D + lane * (E / 2);
+            const u32x2_a4 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4*>(p));
+            const u32x2_a4 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4*>(p + D / 2));
+            v[s] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+            v[s] = ld16(part + uint64_t(rc) * D + lane * E);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -620,7 +630,13 @@ __global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
 #pragma unroll
             for (int k = 0; k < E; ++k) acc[k] = 0.0f;
             fma_chunk<DT>(v[s], wr, acc);
-            store_chunk<DT>(out, uint64_t(row[s]) * D + lane * E, acc, out_f32);
+            if constexpr (SPLIT) {
+                float* p = static_cast<float*>(out) + uint64_t(row[s]) * D + lane * 4;
+                st16(p, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
+                st16(p + D / 2, f32_chunk(acc[4], acc[5], acc[6], acc[7]));
+            } else {
+                store_chunk<DT>(out, uint64_t(row[s]) * D + lane * E, acc, 0);
+            }
             if (out_lse != nullptr && lane == 0) out_lse[row[s]] = global_lse(sum, m, inv_scale);
         }
     }
@@ -1063,16 +1079,15 @@ int run_combine(const void* src, const float* lse, int64_t N, int64_t rows, int6
     return launch_status();
 }
 
-template <int DT, int G>
+template <int DT, int G, bool SPLIT>
 void launch_correct_s(int S, const float* lse, int N, int rank, const void* part, uint32_t rows,
-                      float scale, float inv_scale, void* out, int out_f32, float* out_lse,
-                      hipStream_t st) {
+                      float scale, float inv_scale, void* out, float* out_lse, hipStream_t st) {
     constexpr uint32_t RPS = kBlock / G;
     const unsigned blocks = (rows + RPS * S - 1) / (RPS * S);
     const auto* p = static_cast<const typename Elem<DT>::T*>(part);
-#define LSEC_CORRECT(SV)                                                                   \
-    correct_tiled_kernel<DT, G, SV><<<blocks, kBlock, 0, st>>>(lse, N, rank, p, rows, scale, \
-                                                               inv_scale, out, out_f32, out_lse)
+#define LSEC_CORRECT(SV)                                                             \
+    correct_tiled_kernel<DT, G, SV, SPLIT><<<blocks, kBlock, 0, st>>>(lse, N, rank, p, rows, \
+                                                                     scale, inv_scale, out, out_lse)
     switch (S) {
         case 8: LSEC_CORRECT(8); break;
         case 4: LSEC_CORRECT(4); break;
@@ -1096,12 +1111,21 @@ void launch_correct(bool tiled, const float* lse, int64_t N, int64_t rank, const
     const uint64_t rps = kBlock / uint64_t(D / E);
     int S = 8;
     while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < kTiledMinBlocks) S /= 2;
-#define LSEC_CORRECT_G(GV) \
-    launch_correct_s<DT, GV>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_f32, out_lse, st)
-    switch (D) {
-        case 128: LSEC_CORRECT_G(128 / E); break;
-        case 256: LSEC_CORRECT_G(256 / E); break;
-        default: LSEC_CORRECT_G(512 / E); break;
+#define LSEC_CORRECT_G(GV, SPLIT) \
+    launch_correct_s<DT, GV, SPLIT>(S, lse, int(N), int(rank), part, uint32_t(rows), scale, inv_scale, out, out_lse, st)
+    constexpr bool kCanSplit = DT != LSEC_FP32;
+    if (kCanSplit && out_f32) {
+        switch (D) {
+            case 128: LSEC_CORRECT_G(128 / E, kCanSplit); break;
+            case 256: LSEC_CORRECT_G(256 / E, kCanSplit); break;
+            default: LSEC_CORRECT_G(512 / E, kCanSplit); break;
+        }
+    } else {
+        switch (D) {
+            case 128: LSEC_CORRECT_G(128 / E, false); break;
+            case 256: LSEC_CORRECT_G(256 / E, false); break;
+            default: LSEC_CORRECT_G(512 / E, false); break;
+        }
     }
 #undef LSEC_CORRECT_G
 }
