@@ -338,7 +338,9 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
 
 // ---------------------------------------------------------------- combine (tiled path)
 //
-// For D in {128, 256, 512} and N in {2, 4, 8, 16}. A row is owned by
+// For D in {128, 256, 512} and 2 <= N <= 16 (N = 2, 4, 8, 16 compiled in; other
+// N at run time, NT = 0, with the plane groups of N = 16 and the planes past N
+// skipped by a uniform branch). A row is owned by
 // G = D / kEpc lanes (16 bytes each). A block of 256 threads covers S slots of
 // 256/G consecutive rows, so per plane it reads one contiguous run of
 // S*256/G rows (32 KB at S = 8). The planes are walked in order, PG at a time:
@@ -424,7 +426,7 @@ constexpr int tiled_pg() {
 // Otherwise the result has the input dtype.
 template <int DT, int NT, int G, int S, bool PACKED, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
-    const void* src, const float* __restrict__ lse, uint32_t rows, uint32_t stride,
+    const void* src, const float* __restrict__ lse, int n_rt, uint32_t rows, uint32_t stride,
     uint64_t plane_bytes, uint32_t lse_plane, float scale, float inv_scale,
     void* __restrict__ out, float* __restrict__ out_lse, OutMap om) {
     static_assert(!SPLIT || DT != LSEC_FP32, "fp32 partials already give fp32 results");
@@ -432,8 +434,11 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     constexpr uint32_t ES = sizeof(typename Elem<DT>::T);
     constexpr int RPS = kBlock / G;  // rows per slot
     constexpr int D = G * E;
-    constexpr int PG = tiled_pg<S, NT>();
-    static_assert(NT % PG == 0, "plane groups must tile N");
+    constexpr int PG = tiled_pg<S, (NT > 0 ? NT : 16)>();
+    static_assert(NT == 0 || NT % PG == 0, "plane groups must tile N");
+    const int N = NT > 0 ? NT : n_rt;  // 2 <= n_rt <= 16
+    // Plane n0 + p exists (always for a compiled-in N).
+    auto has = [&](int n) { return NT > 0 || n < N; };
     static_assert(RPS >= 1 && kBlock % G == 0, "a row's lanes must fit the block");
     const uint32_t t = threadIdx.x;
     const uint32_t rib = t / G;
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     for (int s = 0; s < S; ++s) {
         const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
         float l = -__builtin_inff();
-        if (j < NT) {
+        if (int(j) < N) {
             if (PACKED)
                 l = ld_tail(base + j * plane_bytes + (rc * stride + D) * ES);
             else
@@ -470,6 +475,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     auto load_group = [&](int n0) {
 #pragma unroll
         for (int p = 0; p < PG; ++p) {
+            if (!has(n0 + p)) break;
             const char* pb = base + uint64_t(n0 + p) * plane_bytes;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
@@ -489,10 +495,10 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const float l = j < NT ? sanitize(lw[s]) : -__builtin_inff();
+        const float l = int(j) < N ? sanitize(lw[s]) : -__builtin_inff();
         float m = row16_max(l);
         if (m == -__builtin_inff()) m = 0.0f;
-        const float w = j < NT ? weight(l - m, scale) : 0.0f;
+        const float w = int(j) < N ? weight(l - m, scale) : 0.0f;
         const float sum = row16_sum(w);
         lw[s] = w * (1.0f / fmaxf(sum, 1e-10f));
         if (out_lse != nullptr && lane == 0 && row[s] < rows)
@@ -505,13 +511,15 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
 #pragma unroll
         for (int k = 0; k < E; ++k) acc[s][k] = 0.0f;
 #pragma unroll 1
-    for (int n0 = 0; n0 < NT; n0 += PG) {
+    for (int n0 = 0; n0 < N; n0 += PG) {
         if (n0 > 0) load_group(n0);
         __builtin_amdgcn_sched_barrier(0);  // all PG*S loads issued before the first is used
 #pragma unroll
-        for (int p = 0; p < PG; ++p)
+        for (int p = 0; p < PG; ++p) {
+            if (!has(n0 + p)) break;
 #pragma unroll
             for (int s = 0; s < S; ++s) fma_chunk<DT>(v[p][s], lane_value<G>(lw[s], n0 + p), acc[s]);
+        }
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -940,6 +948,7 @@ constexpr uint64_t kTiledMinBlocksN16 = 1024;
 struct TiledArgs {
     const void* src;
     const float* lse;
+    int n;
     uint32_t rows, stride;
     uint64_t plane_bytes;
     uint32_t lse_plane;
@@ -957,8 +966,8 @@ void launch_tiled_s(int S, const TiledArgs& a) {
     const unsigned blocks = (a.rows + RPS * S - 1) / (RPS * S);
 #define LSEC_TILED(SV)                                                                         \
     combine_tiled_kernel<DT, NT, G, SV, PACKED, SPLIT><<<blocks, kBlock, 0, a.st>>>(           \
-        a.src, a.lse, a.rows, a.stride, a.plane_bytes, a.lse_plane, a.scale, a.inv_scale, a.out, \
-        a.out_lse, a.om)
+        a.src, a.lse, a.n, a.rows, a.stride, a.plane_bytes, a.lse_plane, a.scale, a.inv_scale,   \
+        a.out, a.out_lse, a.om)
     switch (S) {
         case 16: LSEC_TILED(16); break;
         case 8: LSEC_TILED(8); break;
@@ -975,7 +984,8 @@ void launch_tiled_n(int N, int S, const TiledArgs& a) {
         case 2: launch_tiled_s<DT, 2, G, PACKED, SPLIT>(S, a); break;
         case 4: launch_tiled_s<DT, 4, G, PACKED, SPLIT>(S, a); break;
         case 8: launch_tiled_s<DT, 8, G, PACKED, SPLIT>(S, a); break;
-        default: launch_tiled_s<DT, 16, G, PACKED, SPLIT>(S, a); break;
+        case 16: launch_tiled_s<DT, 16, G, PACKED, SPLIT>(S, a); break;
+        default: launch_tiled_s<DT, 0, G, PACKED, SPLIT>(S, a); break;  // 2 < N < 16, at run time
     }
 }
 
@@ -1015,8 +1025,7 @@ struct CombinePlan {
 CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, int64_t esize, bool packed,
                          bool fast, Planes pl) {
     if (!fast) return {kPathElems, 0};
-    const bool tiled_shape = (D == 128 || D == 256 || D == 512) &&
-                             (N == 2 || N == 4 || N == 8 || N == 16);
+    const bool tiled_shape = (D == 128 || D == 256 || D == 512) && N >= 2 && N <= 16;
     if (tiled_shape) {
         const int64_t P = 4 / esize;
         const uint64_t plane_bytes =
@@ -1041,7 +1050,7 @@ void run_combine_dt(const void* src, const float* lse, int64_t N, int64_t rows, 
                     int64_t map_c, hipStream_t st) {
     if (plan.kind == kPathTiled) {
         const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
-        const TiledArgs a{src, lse, uint32_t(rows), uint32_t(stride),
+        const TiledArgs a{src, lse, int(N), uint32_t(rows), uint32_t(stride),
                           uint64_t(pl.plane) * sizeof(typename Elem<DT>::T), uint32_t(pl.lse_plane),
                           scale, inv_scale, out, out_f32, out_lse, om, st};
         launch_tiled<DT, PACKED>(int(N), plan.S, int(D), a);

@@ -143,7 +143,9 @@ def test_python_binding_rejects_bad_tensors():
     ((8, 2048, 8, 128, 0, 1, 1), "combine_tiled_kernel S=1"),
     ((16, 16384, 32, 128, 0, 0, 0), "combine_elems_kernel"),   # buffers not 16-byte aligned
     ((1, 50, 3, 512, 0, 0, 1), "combine_rows_kernel"),          # N = 1
-    ((32, 6, 4, 128, 0, 0, 1), "combine_rows_kernel"),          # N outside {2, 4, 8, 16}
+    ((32, 6, 4, 128, 0, 0, 1), "combine_rows_kernel"),          # N > 16
+    ((3, 16384, 32, 128, 0, 0, 1), "combine_tiled_kernel S=16"),  # N at run time
+    ((12, 8192, 16, 256, 0, 0, 1), "combine_tiled_kernel S=8"),
     ((4, 10, 3, 64, 0, 0, 1), "combine_rows_kernel"),           # D outside {128, 256, 512}
     ((3, 5, 2, 3, 0, 0, 1), "combine_elems_kernel"),            # D % 8 != 0
     ((2, 2, 2, 4096, 0, 0, 1), "combine_elems_kernel"),         # D > 2048

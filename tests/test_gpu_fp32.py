@@ -51,7 +51,7 @@ F32_SHAPES = [
     (4, 23, 6, 256, True),       # tiled S=1, one wave per row
     (2, 31, 7, 64, False),       # row kernel, 16 lanes per row
     (1, 50, 3, 512, False),      # row kernel, N = 1
-    (3, 11, 7, 128, True),       # row kernel, runtime N
+    (3, 11, 7, 128, True),       # tiled S=1, N at run time
     (9, 20, 2, 12, True),        # row kernel, 3 lanes per row
     (32, 6, 4, 128, False),      # row kernel, runtime N > 16
     (2, 3, 3, 1024, False),      # row kernel, 256 lanes per row
@@ -84,6 +84,8 @@ TILED_F32 = [
     (8, 3125, 31, 128, True, 4),    # 96875 rows
     (8, 1250, 31, 128, False, 2),   # 38750 rows
     (2, 1000, 3, 128, True, 1),     # 3000 rows
+    (12, 3000, 16, 256, False, 4),  # 48000 rows, N at run time
+    (5, 2051, 17, 512, True, 8),    # 34867 rows, N at run time, a row spans two waves
 ]
 
 
@@ -108,7 +110,8 @@ OUT_F32 = [
     (2, 2081, 63, 512, "bf16", True, "combine_tiled_kernel S=16"),
     (4, 4099, 32, 128, "f16", False, "combine_tiled_kernel S=4"),
     (8, 1250, 31, 128, "bf16", True, "combine_tiled_kernel S=1"),
-    (3, 11, 7, 128, "f16", True, "combine_rows_kernel"),
+    (3, 11, 7, 128, "f16", True, "combine_tiled_kernel S=1"),   # N at run time
+    (20, 11, 7, 128, "f16", True, "combine_rows_kernel"),       # N > 16
     (9, 20, 2, 24, "bf16", False, "combine_rows_kernel"),
     (4, 10, 3, 1004, "bf16", True, "combine_elems_kernel"),
 ]

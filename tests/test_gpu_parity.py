@@ -165,9 +165,9 @@ SHAPES = [
     (4, 23, 6, 256, "f16", True),
     (2, 31, 7, 64, "bf16", False),
     (1, 50, 3, 512, "bf16", False),
-    (3, 11, 7, 128, "f16", True),     # runtime N
+    (3, 11, 7, 128, "f16", True),     # tiled, N at run time
     (5, 9, 4, 64, "bf16", True),
-    (7, 13, 3, 256, "bf16", False),
+    (7, 13, 3, 256, "bf16", False),   # tiled, N at run time
     (32, 6, 4, 128, "bf16", False),
     (9, 20, 2, 24, "bf16", True),     # 3 lanes per row, rows straddle waves
     (2, 3, 3, 2048, "f16", False),    # 256 lanes per row
@@ -204,6 +204,14 @@ TILED = [
     (8, 3125, 31, 128, "bf16", False, 2),    # 96875 rows
     (8, 1250, 31, 128, "f16", True, 1),      # 38750 rows
     (2, 1000, 3, 128, "bf16", True, 1),      # 3000 rows
+    # N at run time (2 < N < 16, not a power of two): the plane groups of N = 16
+    # with the planes past N skipped
+    (3, 16389, 32, 128, "bf16", False, 16),  # 524448 rows
+    (6, 4099, 16, 512, "bf16", True, 8),     # 65584 rows, one wave per row
+    (12, 8193, 16, 256, "f16", False, 8),    # 131088 rows, two rows per wave
+    (7, 3125, 31, 128, "bf16", False, 2),    # 96875 rows, groups of 4 planes: 4 + 3
+    (15, 1250, 31, 128, "bf16", True, 1),    # 38750 rows, groups of 8 planes: 8 + 7
+    (5, 1000, 3, 128, "bf16", True, 1),      # 3000 rows
 ]
 
 
@@ -247,6 +255,8 @@ def test_tiled_n16_relaxed_block_count_sampled(lsec):
     (8, 4099, 64, 128, "bf16", 1),   # 32792 rows
     (2, 4097, 32, 512, "f16", 8),    # 65552 rows
     (2, 16389, 64, 128, "bf16", 16),  # 524448 rows
+    (5, 8193, 15, 128, "bf16", 1),    # 24579 rows, N at run time
+    (6, 16389, 12, 512, "f16", 4),    # 32778 rows, N at run time
 ])
 def test_tiled_unpack_combine_ragged(lsec, N, B, H, D, dtype, slots):
     _announce(f"tiled unpack_combine N={N} B={B} H={H} D={D} {dtype} S={slots}")
@@ -348,7 +358,8 @@ MERGE = [
     (4, 512, 64, 128, "bf16", 1, False),   # token-scattered [N, T/N, H, D] -> [T/N, H, D]
     (16, 4, 8197, 128, "bf16", 2, True),   # tiled 8 slots, ragged, transposed store
     (4, 16, 1031, 512, "f16", 2, False),   # one wave per row
-    (3, 5, 77, 64, "bf16", 2, True),       # row kernel (N = 3)
+    (3, 5, 77, 64, "bf16", 2, True),       # row kernel (D = 64)
+    (6, 4, 1031, 128, "bf16", 2, False),   # tiled, N at run time, transposed store
     (2, 7, 13, 12, "f16", 2, False),       # element kernel (D % 8 != 0)
 ]
 
