@@ -960,12 +960,21 @@ struct TiledArgs {
     hipStream_t st;
 };
 
+// Occupancy cap for the tiled combine, as dynamic LDS that the kernel never
+// touches (a CU has 160 KB): S = 8 launches at most 2 blocks per CU (56 KB
+// each), S = 4 at most 4 (36 KB each). HBM streams better from fewer, deeper
+// waves; measured on MI355X: N=8 D=512 2^16 rows (S = 8) 2.8 % faster, N=8
+// D=128 2^17 rows (S = 4) 7.0 % faster than at the occupancy the registers
+// allow (3 and 7 blocks per CU). S = 16 is already held to one or two blocks
+// by its registers; S <= 2 serves inputs too small to fill the chip.
+constexpr size_t tiled_lds_cap(int S) { return S == 8 ? 56000 : (S == 4 ? 36000 : 0); }
+
 template <int DT, int NT, int G, bool PACKED, bool SPLIT>
 void launch_tiled_s(int S, const TiledArgs& a) {
     constexpr uint32_t RPS = kBlock / G;
     const unsigned blocks = (a.rows + RPS * S - 1) / (RPS * S);
 #define LSEC_TILED(SV)                                                                         \
-    combine_tiled_kernel<DT, NT, G, SV, PACKED, SPLIT><<<blocks, kBlock, 0, a.st>>>(           \
+    combine_tiled_kernel<DT, NT, G, SV, PACKED, SPLIT><<<blocks, kBlock, tiled_lds_cap(SV), a.st>>>( \
         a.src, a.lse, a.n, a.rows, a.stride, a.plane_bytes, a.lse_plane, a.scale, a.inv_scale,   \
         a.out, a.out_lse, a.om)
     switch (S) {
