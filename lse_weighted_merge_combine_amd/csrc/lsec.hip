@@ -961,13 +961,18 @@ struct TiledArgs {
 };
 
 // Occupancy cap for the tiled combine, as dynamic LDS that the kernel never
-// touches (a CU has 160 KB): S = 8 launches at most 2 blocks per CU (56 KB
-// each), S = 4 at most 4 (36 KB each). HBM streams better from fewer, deeper
-// waves; measured on MI355X: N=8 D=512 2^16 rows (S = 8) 2.8 % faster, N=8
-// D=128 2^17 rows (S = 4) 7.0 % faster than at the occupancy the registers
-// allow (3 and 7 blocks per CU). S = 16 is already held to one or two blocks
-// by its registers; S <= 2 serves inputs too small to fill the chip.
-constexpr size_t tiled_lds_cap(int S) { return S == 8 ? 56000 : (S == 4 ? 36000 : 0); }
+// touches (a CU has 160 KB): S = 16 launches run at most 1 block per CU
+// (90 KB), S = 8 at most 2 (56 KB each), S = 4 at most 4 (36 KB each). HBM
+// streams better from fewer, deeper waves; measured on MI355X against the
+// occupancy the registers allow: fp32 N=8 D=512 2^16 rows (S = 16, 2 blocks)
+// 5.7 % faster, bf16 N=8 D=512 2^16 rows (S = 8, 3 blocks) 2.8 %, bf16 N=8
+// D=128 2^17 rows (S = 4, 7 blocks) 7.0 %. The 16-bit S = 16 kernels hold
+// one block per CU by their registers anyway. S <= 2 serves inputs too small
+// to fill the chip, and capping it (or the pack, or the corrected partial)
+// measured slower.
+constexpr size_t tiled_lds_cap(int S) {
+    return S == 16 ? 90000 : (S == 8 ? 56000 : (S == 4 ? 36000 : 0));
+}
 
 template <int DT, int NT, int G, bool PACKED, bool SPLIT>
 void launch_tiled_s(int S, const TiledArgs& a) {
