@@ -205,3 +205,15 @@ def test_combine_planes_validation(lib):
     assert c(FAKE, 64, FAKE + 2, 8, 2, 2, 3, 8, 0, 0, FAKE, None, None) == 5
     assert c(None, 64, None, 8, 2, 0, 3, 8, 0, 0, None, None, None) == 0      # T = 0
     assert c(FAKE, 64, FAKE, 8, 0, 2, 3, 8, 0, 0, FAKE, None, None) == 2      # N < 1
+
+
+def test_header_and_c_consumer_compile_as_c99():
+    """include/lsec.h is a plain C header: the C consumer of the library
+    compiles as C99 with warnings as errors (nothing is linked or run)."""
+    import subprocess
+    src = os.path.join(ROOT, "tests", "c_abi", "c_abi_check.c")
+    cmd = ["gcc", "-std=c99", "-fsyntax-only", "-Wall", "-Wextra", "-Werror",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", src]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
