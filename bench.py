@@ -76,8 +76,16 @@ def pack_bytes(N, B, H, D, s=2):
 
 
 def source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of the kernel source's code: comments, trailing blanks and empty
+    lines removed, so that only a change to the code (not to its comments)
+    invalidates counters taken on it."""
+    import re
+    with open(KERNEL_SRC) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def load_traffic(workload: str, kernel: str):

@@ -3,18 +3,25 @@
 // The operations are those of the page "vllm.v1.attention.ops.dcp_alltoall":
 // `_lse_weighted_combine` (lsec_combine), and the pack / unpack-and-combine
 // steps of `dcp_a2a_lse_reduce` (lsec_pack_send, lsec_unpack_combine,
-// lsec_unpack). The argument contract of each entry point is in lsec.h.
+// lsec_unpack); with the same kernels, the token-major merge of the page
+// "vllm_ascend/attention/context_parallel/sfa_cp.py" (lsec_merge), the
+// combine over strided receive planes of the direct exchange on the page
+// "vllm.v1.attention.ops.dcp" (lsec_combine_planes), and the local step of
+// the LSE all-gather strategies named there (lsec_correct_partial). The
+// argument contract of each entry point is in lsec.h.
 //
 // Design. The combine is a streaming reduction: per (token, head) row it reads
 // N planes of D values and writes one, so it is bound by HBM bandwidth at
 // about one FMA per byte. It runs on plain VALU (no MFMA): a group of
 // consecutive lanes owns a row, each lane moving one 16-byte chunk (8 bf16 /
 // fp16 or 4 fp32 elements) per plane. The weights are computed in registers
-// from the row's N LSE values, so the kernels need no LDS. Packed rows are
-// D + P elements wide (P = 2 for 16-bit elements, 1 for fp32), so in the
-// packed layout a row start is only 4-byte aligned; gfx950 serves dwordx4
-// accesses at 4-byte alignment, so the packed kernels read and write those
-// rows directly.
+// from the row's N LSE values and shared with 16-lane DPP reductions, so the
+// combine keeps no data in LDS (its tiled launches reserve LDS only to cap
+// occupancy). Packed rows are D + P elements wide (P = 2 for 16-bit elements,
+// 1 for fp32), so a packed row starts only 4-byte aligned; gfx950 serves
+// dwordx4 accesses at 4-byte alignment, so the receive side reads those rows
+// in place, and the pack assembles its spans of rows in LDS to write them
+// with aligned stores.
 //
 // Build with -Xclang -target-feature -Xclang -packed-fp32-ops and without
 // fast-math (the NaN / infinity tests must survive).
@@ -241,9 +248,10 @@ __device__ __forceinline__ void store_elem(void* out, int64_t idx, float v, int 
         static_cast<typename Elem<DT>::T*>(out)[idx] = Elem<DT>::enc1(v);
 }
 
-// ---------------------------------------------------------------- combine (fast path)
+// ---------------------------------------------------------------- combine (row kernel)
 //
-// Row r of plane n starts at element n * plane + r * stride of `src`.
+// For N = 1, N > 16, or D outside {128, 256, 512} (whole 16-byte chunks, at
+// most 256 lanes per row). Row r of plane n starts at element n * plane + r * stride of `src`.
 // Separate layout (lsec_combine): stride = D, plane >= rows * D (rows * D
 // when dense; more when the planes are the leading rows of longer ones), LSE
 // n of row r at lse[n * lse_plane + r]. Packed layout (lsec_unpack_combine):
