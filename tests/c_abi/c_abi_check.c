@@ -4,7 +4,7 @@
  * (synth/libsynth.so), expected values from the CPU oracle
  * (oracle/liblsec_oracle.so), comparisons with the tolerances of the GPU
  * parity tests. TEST INFRASTRUCTURE: built by __graft_entry__.build(), run by
- * tests/test_gpu_c_abi.py.
+ * tests/test_gpu_zz_c_abi.py.
  *
  * Cases: the combine (bf16, tiled path, base e, global LSE), the combine
  * (fp16, row path, base 2), an fp32 result from bf16 partials, pack_send
