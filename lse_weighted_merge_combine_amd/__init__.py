@@ -32,7 +32,8 @@ Entry points (same names as the C ABI):
   "vllm.v1.attention.ops.dcp" (``cp_lse_ag_out_rs`` / ``cp_lse_ag_out_ar``).
 
 ``lse_weighted_combine`` and ``merge_dcp_outputs`` keep the argument names of
-the pages' functions.
+the pages' functions; ``lse_combine``, ``pack_send`` and ``unpack_combine`` are
+the plain names of the three hot-path calls.
 
 Element dtypes: bfloat16, float16 and float32. The combining calls take
 ``out_dtype=torch.float32`` to return an fp32 result from 16-bit inputs (the
@@ -423,6 +424,26 @@ def lse_weighted_combine(outputs: torch.Tensor, lses: torch.Tensor, return_lse: 
                         out_dtype=torch.float32)
 
 
+def lse_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
+                return_lse: bool = False):
+    """The combine under its plain name: [N,B,H,D] + [N,B,H] -> [B,H,D] in the
+    input dtype (+ the [B,H] fp32 global LSE when ``return_lse``)."""
+    return lsec_combine(outputs, lses, base_e=base_e, return_lse=return_lse)
+
+
+def pack_send(out: torch.Tensor, lse: torch.Tensor, N: int) -> torch.Tensor:
+    """The pack under its plain name: [B,H,D] + [B,H] -> [N,B,H/N,D+P]."""
+    return lsec_pack_send(out, lse, N)
+
+
+def unpack_combine(recv: torch.Tensor, D: int, base_e: bool = True, return_lse: bool = False):
+    """The receive side under its plain name, with the head dimension D stated
+    (as the page's ``_dcp_a2a_unpack_combine`` takes it): recv [N,B,Hl,D+P]."""
+    if recv.dim() != 4 or recv.shape[-1] != D + lsec_pack_dim(recv.dtype):
+        raise ValueError(f"recv {tuple(recv.shape)} does not hold rows of D={D} plus the LSE")
+    return lsec_unpack_combine(recv, base_e=base_e, return_lse=return_lse)
+
+
 def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or \
             not t.is_contiguous():
@@ -433,6 +454,6 @@ def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
 __all__ = [
     "lsec_pack_dim", "lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
     "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
-    "lsec_combine_planes",
+    "lsec_combine_planes", "lse_combine", "pack_send", "unpack_combine",
     "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
 ]

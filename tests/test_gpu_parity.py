@@ -595,6 +595,30 @@ def test_side_stream_and_preallocated_outputs(lsec):
     assert_lse_close(out_lse, L_ref)
 
 
+def test_plain_name_wrappers(lsec):
+    """lse_combine / pack_send / unpack_combine: the hot path under its plain
+    names, on the packed workload's shapes scaled down."""
+    N, B, H, D = 4, 33, 8, 128
+    o, l = synth.custom_inputs(N, B, H, D, seed=55, special=SPECIALS)
+    y, L = lsec.lse_combine(to_dev(o, "bf16", DEV), f32_to_dev(l, DEV), base_e=False,
+                            return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.lse_combine(o, l, "bf16", base2=True)
+    assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"))
+    assert_lse_close(L, L_ref)
+    send = lsec.pack_send(to_dev(o[0], "bf16", DEV), f32_to_dev(l[0], DEV), N)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(send), oracle.pack_send(o[0], l[0], N))
+    y2, L2 = lsec.unpack_combine(send, D, return_lse=True)
+    torch.cuda.synchronize()
+    y2_ref, L2_ref = oracle.unpack_combine(bits_of(send), D, "bf16")
+    oo, _ = oracle.unpack(bits_of(send), D)
+    assert_output_close(y2, y2_ref, "bf16", max_abs_input(oo, "bf16"))
+    assert_lse_close(L2, L2_ref)
+    with pytest.raises(ValueError):
+        lsec.unpack_combine(send, D + 2)
+
+
 def test_page_signature_alias(lsec):
     """The page's function returns fp32 (bf16 outputs times fp32 weights)."""
     o, l = synth.custom_inputs(3, 4, 4, 64, seed=13)
