@@ -1,0 +1,88 @@
+"""The library's calls inside a captured HIP graph.
+
+The entry points allocate nothing and never synchronise, so a caller can
+capture them on its stream and replay them (what a serving loop does to drop
+the launch overhead of the small packed calls). The graph holds only this
+library's kernels (the buffers are allocated and filled before capture); it
+is replayed several times with eager work and synchronisations in between,
+and every replay is checked against the eager results and the oracle.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import assert_lse_close, assert_output_close, bits_of, f32_to_dev, max_abs_input, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def lsec():
+    import lse_weighted_merge_combine_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    m.load_library()
+    return m
+
+
+def test_pack_unpack_combine_and_combine_replayed_from_a_graph(lsec):
+    print("[case] graph capture and replay", flush=True)
+    N, B, H, D = 8, 64, 64, 128
+    Hl = H // N
+    a, l = synth.custom_inputs(1, B, H, D, seed=71)
+    o, ol = synth.custom_inputs(N, B, Hl, D, seed=72, special=((0.05, float("-inf")),))
+    attn, attn_lse = to_dev(a[0], "bf16", DEV), f32_to_dev(l[0], DEV)
+    planes, plane_lses = to_dev(o, "bf16", DEV), f32_to_dev(ol, DEV)
+    # every buffer exists before capture
+    send = torch.empty((N, B, Hl, D + 2), dtype=torch.bfloat16, device=DEV)
+    y_pk = torch.empty((B, Hl, D), dtype=torch.bfloat16, device=DEV)
+    L_pk = torch.empty((B, Hl), dtype=torch.float32, device=DEV)
+    y_c = torch.empty((B, Hl, D), dtype=torch.bfloat16, device=DEV)
+    L_c = torch.empty((B, Hl), dtype=torch.float32, device=DEV)
+
+    def step():
+        lsec.lsec_pack_send(attn, attn_lse, N, send=send)
+        lsec.lsec_unpack_combine(send, return_lse=True, out=y_pk, out_lse=L_pk)
+        lsec.lsec_combine(planes, plane_lses, return_lse=True, out=y_c, out_lse=L_c)
+
+    # eager reference (warm-up on a side stream, as graph capture requires)
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (send, y_pk, L_pk, y_c, L_c)]
+    # the eager results themselves match the oracle
+    assert np.array_equal(bits_of(ref[0]), oracle.pack_send(a[0], l[0], N))
+    yr, Lr = oracle.unpack_combine(bits_of(ref[0]), D, "bf16")
+    oo, _ = oracle.unpack(bits_of(ref[0]), D)
+    assert_output_close(ref[1], yr, "bf16", max_abs_input(oo, "bf16"))
+    assert_lse_close(ref[2], Lr)
+    yc, Lc = oracle.lse_combine(o, ol, "bf16")
+    assert_output_close(ref[3], yc, "bf16", max_abs_input(o, "bf16"))
+    assert_lse_close(ref[4], Lc)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for t in (send, y_pk, L_pk, y_c, L_c):
+            t.fill_(float("nan")) if t.dtype.is_floating_point else t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((send, y_pk, L_pk, y_c, L_c), ref):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want.view(torch.int32)), \
+                f"replay {i} differs from the eager result"
+        # eager work between replays
+        lsec.lsec_combine(planes, plane_lses)
+        torch.cuda.synchronize()
