@@ -51,7 +51,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 METRIC = "LSE-combine achieved HBM GB/s and (token·head) rows/s; % of peak HBM BW"
-KERNEL_SRC = os.path.join(ROOT, "lse_weighted_merge_combine_amd", "csrc", "lsec.hip")
+KERNEL_DIR = os.path.join(ROOT, "lse_weighted_merge_combine_amd", "csrc")
 
 
 def log(*a):
@@ -76,16 +76,20 @@ def pack_bytes(N, B, H, D, s=2):
 
 
 def source_sha() -> str:
-    """SHA-256 of the kernel source's code: comments, trailing blanks and empty
-    lines removed, so that only a change to the code (not to its comments)
-    invalidates counters taken on it."""
+    """SHA-256 of the kernel sources' code (every csrc/*.hip and *.h, in name
+    order): comments, trailing blanks and empty lines removed, so that only a
+    change to the code (not to its comments) invalidates counters taken on it."""
     import re
-    with open(KERNEL_SRC) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
-    code = "\n".join(ln for ln in lines if ln.strip())
-    return hashlib.sha256(code.encode()).hexdigest()
+    parts = []
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if not name.endswith((".hip", ".h")):
+            continue
+        with open(os.path.join(KERNEL_DIR, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        parts.append(name + "\n" + "\n".join(ln for ln in lines if ln.strip()))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
 
 def load_traffic(workload: str, kernel: str):

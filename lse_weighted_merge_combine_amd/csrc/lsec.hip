@@ -26,227 +26,10 @@
 // Build with -Xclang -target-feature -Xclang -packed-fp32-ops and without
 // fast-math (the NaN / infinity tests must survive).
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "lsec_device.h"
 
-#include "lsec.h"
-
+namespace lsec_detail {
 namespace {
-
-constexpr int kBlock = 256;  // a row's lanes (D / elements per chunk) must fit one block
-
-// ---------------------------------------------------------------- helpers
-
-// Unsigned 32-bit division by an invariant divisor d >= 1 (Granlund and
-// Montgomery, "Division by invariant integers using multiplication", 1994):
-// q = (umulhi(x, m) + x) >> l with l = ceil(log2 d), m = 2^32 (2^l - d) / d + 1.
-struct FastDiv {
-    uint32_t d, m, l;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-    uint32_t l = 0;
-    while ((uint64_t(1) << l) < d) ++l;
-    uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
-    return FastDiv{d, uint32_t(m), l};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f) {
-    return uint32_t((uint64_t(__umulhi(x, f.m)) + x) >> f.l);
-}
-
-// Output row order. Identity (a == 0), or the token-major transpose of the
-// Ascend SFA merge with its token in the second input dimension: input row
-// r = (x, t) of an [A, C] grid (x < A, t < C) is stored at output row t * A + x.
-struct OutMap {
-    uint32_t a;  // A, or 0 for the identity
-    FastDiv c;   // divides by C
-};
-
-__device__ __forceinline__ uint32_t out_row(uint32_t r, OutMap om) {
-    if (om.a == 0) return r;
-    const uint32_t x = fdiv(r, om.c);
-    return (r - x * om.c.d) * om.a + x;
-}
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// The same four (two) dwords at 4-byte alignment (packed rows start every
-// D + P elements, i.e. on 4-byte boundaries).
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
-
-// Every input byte is read once and every output byte written once, so all
-// streaming accesses are non-temporal (the `nt` cache policy); on MI355X plain
-// loads cost 12-15 % at 2 GB per call and up to 40 % on small cold calls.
-// 16-byte load / store at a 16-byte aligned address.
-__device__ __forceinline__ u32x4 ld16(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ void st16(void* p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
-// 16-byte load / store at a 4-byte aligned address (packed rows): gfx950
-// serves dwordx4 at dword alignment. Packed rows are written in pieces that
-// straddle cache lines, so those stores keep the default policy: L2 assembles
-// whole lines before they go to HBM (non-temporal stores here measured about
-// 10 % slower).
-__device__ __forceinline__ u32x4 ld16_a4(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(p));
-}
-__device__ __forceinline__ void st16_a4(void* p, u32x4 v) {
-    *reinterpret_cast<u32x4_a4*>(p) = static_cast<u32x4_a4>(v);
-}
-// The fp32 LSE in the tail of a packed row (same cache lines as the row).
-__device__ __forceinline__ float ld_tail(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
-}
-__device__ __forceinline__ void st_tail(void* p, float v) { *reinterpret_cast<float*>(p) = v; }
-
-// Element types. T is the storage word; kEpc elements make one 16-byte chunk;
-// kPack elements carry one fp32 LSE in a packed row. dec / enc convert to and
-// from fp32 (round to nearest even).
-template <int DT>
-struct Elem;
-
-template <>
-struct Elem<LSEC_BF16> {
-    using T = uint16_t;
-    static constexpr int kEpc = 8;
-    static constexpr int kPack = 2;
-    __device__ static __forceinline__ void dec2(uint32_t u, float& a, float& b) {
-        a = __uint_as_float(u << 16);
-        b = __uint_as_float(u & 0xffff0000u);
-    }
-    __device__ static __forceinline__ uint32_t enc2(float a, float b) {
-        bf16x2 p = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32: round to nearest even
-        return __builtin_bit_cast(uint32_t, p);
-    }
-    __device__ static __forceinline__ float dec1(uint16_t h) {
-        return __uint_as_float(uint32_t(h) << 16);
-    }
-    __device__ static __forceinline__ uint16_t enc1(float a) {
-        return __builtin_bit_cast(uint16_t, (__bf16)a);
-    }
-};
-
-template <>
-struct Elem<LSEC_FP16> {
-    using T = uint16_t;
-    static constexpr int kEpc = 8;
-    static constexpr int kPack = 2;
-    __device__ static __forceinline__ void dec2(uint32_t u, float& a, float& b) {
-        f16x2 h = __builtin_bit_cast(f16x2, u);
-        a = (float)h.x;
-        b = (float)h.y;
-    }
-    __device__ static __forceinline__ uint32_t enc2(float a, float b) {
-        f16x2 p = {(_Float16)a, (_Float16)b};  // v_cvt_f16_f32: round to nearest even
-        return __builtin_bit_cast(uint32_t, p);
-    }
-    __device__ static __forceinline__ float dec1(uint16_t h) {
-        return (float)__builtin_bit_cast(_Float16, h);
-    }
-    __device__ static __forceinline__ uint16_t enc1(float a) {
-        return __builtin_bit_cast(uint16_t, (_Float16)a);
-    }
-};
-
-template <>
-struct Elem<LSEC_FP32> {
-    using T = uint32_t;
-    static constexpr int kEpc = 4;
-    static constexpr int kPack = 1;
-    __device__ static __forceinline__ float dec1(uint32_t u) { return __uint_as_float(u); }
-    __device__ static __forceinline__ uint32_t enc1(float a) { return __float_as_uint(a); }
-};
-
-// NaN and +-inf shard LSEs count as -inf (exponent field all ones).
-__device__ __forceinline__ float sanitize(float l) {
-    return (__float_as_uint(l) & 0x7f800000u) == 0x7f800000u ? -__builtin_inff() : l;
-}
-
-// Weight of a shard: 2^(x * scale), x = l' - m <= 0 or -inf. scale = log2(e)
-// for base-e LSEs (e^x = 2^(x log2 e)) and 1 for base 2. v_exp_f32 maps -inf
-// to 0. A NaN weight (not reachable: x is never NaN) would become 0.
-__device__ __forceinline__ float weight(float x, float scale) {
-    float w = __builtin_amdgcn_exp2f(x * scale);
-    return w != w ? 0.0f : w;
-}
-
-// Global LSE: ln S + m = log2(S) ln 2 + m (base e), or log2(S) + m (base 2).
-// S = 0 (all shards non-finite) gives -inf.
-__device__ __forceinline__ float global_lse(float s, float m, float inv_scale) {
-    return log2f(s) * inv_scale + m;
-}
-
-// Accumulate one 16-byte chunk (kEpc elements) scaled by w into acc.
-template <int DT>
-__device__ __forceinline__ void fma_chunk(u32x4 v, float w, float (&acc)[Elem<DT>::kEpc]) {
-    if constexpr (DT == LSEC_FP32) {
-        acc[0] = fmaf(__uint_as_float(v.x), w, acc[0]);
-        acc[1] = fmaf(__uint_as_float(v.y), w, acc[1]);
-        acc[2] = fmaf(__uint_as_float(v.z), w, acc[2]);
-        acc[3] = fmaf(__uint_as_float(v.w), w, acc[3]);
-    } else {
-        float a, b;
-        Elem<DT>::dec2(v.x, a, b);
-        acc[0] = fmaf(a, w, acc[0]);
-        acc[1] = fmaf(b, w, acc[1]);
-        Elem<DT>::dec2(v.y, a, b);
-        acc[2] = fmaf(a, w, acc[2]);
-        acc[3] = fmaf(b, w, acc[3]);
-        Elem<DT>::dec2(v.z, a, b);
-        acc[4] = fmaf(a, w, acc[4]);
-        acc[5] = fmaf(b, w, acc[5]);
-        Elem<DT>::dec2(v.w, a, b);
-        acc[6] = fmaf(a, w, acc[6]);
-        acc[7] = fmaf(b, w, acc[7]);
-    }
-}
-
-__device__ __forceinline__ u32x4 f32_chunk(float a, float b, float c, float d) {
-    u32x4 r = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
-    return r;
-}
-
-// Store a lane's kEpc results at element `idx` of `out` (16-byte aligned): in
-// the input dtype, or as fp32 when `out_f32` (16-bit inputs then write two
-// 16-byte chunks). fp32 inputs always give fp32 results.
-// The two chunks of an fp32 result go out as two store instructions, each
-// covering every other 16 bytes of the wave's span, so every cache line is
-// written in two halves (non-temporal stores then write 17-18 % more than the
-// result holds; the default policy writes exactly the result but measured
-// slower). The tiled combine avoids this layout (split loads, below); the
-// row and element kernels keep it.
-template <int DT>
-__device__ __forceinline__ void store_chunk(void* out, uint64_t idx,
-                                            const float (&acc)[Elem<DT>::kEpc], int out_f32) {
-    if constexpr (DT == LSEC_FP32) {
-        st16(static_cast<float*>(out) + idx, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
-    } else {
-        if (out_f32) {
-            float* p = static_cast<float*>(out) + idx;
-            st16(p, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
-            st16(p + 4, f32_chunk(acc[4], acc[5], acc[6], acc[7]));
-        } else {
-            u32x4 r = {Elem<DT>::enc2(acc[0], acc[1]), Elem<DT>::enc2(acc[2], acc[3]),
-                       Elem<DT>::enc2(acc[4], acc[5]), Elem<DT>::enc2(acc[6], acc[7])};
-            st16(static_cast<uint16_t*>(out) + idx, r);
-        }
-    }
-}
-
-// One result element (general paths).
-template <int DT>
-__device__ __forceinline__ void store_elem(void* out, int64_t idx, float v, int out_f32) {
-    if (DT == LSEC_FP32 || out_f32)
-        static_cast<float*>(out)[idx] = v;
-    else
-        static_cast<typename Elem<DT>::T*>(out)[idx] = Elem<DT>::enc1(v);
-}
 
 // ---------------------------------------------------------------- combine (row kernel)
 //
@@ -342,204 +125,6 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     const uint32_t orow = out_row(row, om);
     store_chunk<DT>(out, uint64_t(orow) * D + lane * E, acc, out_f32);
     if (out_lse != nullptr && lane == 0) out_lse[orow] = global_lse(s, m, inv_scale);
-}
-
-// ---------------------------------------------------------------- combine (tiled path)
-//
-// For D in {128, 256, 512} and 2 <= N <= 16 (N = 2, 4, 8, 16 compiled in; other
-// N at run time, NT = 0, with the plane groups of N = 16 and the planes past N
-// skipped by a uniform branch). A row is owned by
-// G = D / kEpc lanes (16 bytes each). A block of 256 threads covers S slots of
-// 256/G consecutive rows, so per plane it reads one contiguous run of
-// S*256/G rows (32 KB at S = 8). The planes are walked in order, PG at a time:
-// each lane has PG*S 16-byte loads in flight and a block keeps few DRAM pages
-// open. On MI355X this streams markedly faster than issuing all N planes of
-// one row at once, which spreads every block over N distant pages.
-//
-// Weights: lane j of each 16-lane DPP row loads shard j's LSE for its row
-// (j < N; the 16-lane segments of a row group hold identical copies). Max and
-// sum are 16-lane DPP reductions; during the sweep the weight of plane n comes
-// from lane n of the segment (a lane shuffle, or readlane when a wave holds
-// one row or part of one). The global LSE is written before the sweep so
-// nothing but the weights stays live through it.
-//
-// Addresses: plane n starts at n * plane_bytes (uniform, scalar registers);
-// a lane's chunk sits at a 32-bit byte offset inside the plane; shard j's LSE
-// of row r is lse[j * lse_plane + r]. The host checks plane_bytes < 2^32 and
-// N * lse_plane < 2^32. Rows past the end of the last block are clamped to
-// the last row for loading and are not stored.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                                 0xF, 0xF, false));
-}
-
-// Reductions over the 16 lanes of each DPP row (every lane gets the result).
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
-    v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
-    v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm:[2,3,0,1]
-    v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm:[1,0,3,2]
-    return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp_mov<0x128>(v);
-    v += dpp_mov<0x124>(v);
-    v += dpp_mov<0x4E>(v);
-    v += dpp_mov<0xB1>(v);
-    return v;
-}
-
-// Value held by lane n of this lane's 16-lane segment (n uniform). With
-// G >= 64 every lane of a wave belongs to the same row, and each 16-lane
-// segment holds the same values, so lane n of the wave is lane n of the
-// segment.
-template <int G>
-__device__ __forceinline__ float lane_value(float v, int n) {
-    if constexpr (G >= 64)
-        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), n));
-    else
-        return __shfl(v, n, 16);
-}
-
-__device__ __forceinline__ u32x4 ld16_nt_at(const char* p) { return ld16(p); }
-__device__ __forceinline__ u32x4 ld16_a4_at(const char* p) { return ld16_a4(p); }
-
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
-// XCD i mod 8). Remap so that each XCD takes chunks of kXcdChunk consecutive
-// tiles: logical tile = (chunk * 8 + xcd) * kXcdChunk + index within chunk.
-// The remap is a permutation of [0, nblocks): the grid's tail that does not
-// fill a whole round of 8 chunks keeps the identity. Measured on MI355X: 4-8 %
-// more bandwidth for the streaming combine than plain round-robin order.
-constexpr uint32_t kXcdChunk = 16;
-
-__device__ __forceinline__ uint32_t xcd_chunked_block(uint32_t bid, uint32_t nblocks) {
-    const uint32_t full = nblocks / (8 * kXcdChunk) * (8 * kXcdChunk);
-    if (bid >= full) return bid;
-    const uint32_t xcd = bid % 8, i = bid / 8;
-    return ((i / kXcdChunk) * 8 + xcd) * kXcdChunk + i % kXcdChunk;
-}
-
-template <int S, int NT>
-constexpr int tiled_pg() {
-    return (S >= 4 ? 1 : (8 / S < NT ? 8 / S : NT));
-}
-
-// SPLIT (fp32 result from 16-bit partials): lane l of a row owns elements
-// [4l, 4l + 4) and [D/2 + 4l, D/2 + 4l + 4) instead of [8l, 8l + 8), read as
-// two 8-byte loads, so each of its two 16-byte fp32 stores belongs to an
-// instruction that writes one contiguous half of the row (whole cache
-// lines). Measured on MI355X: 6.6 % faster on N=16 D=128 2^19 rows, 4.5 % on
-// N=8 D=512 2^16 rows, than 16-byte loads with two interleaved stores.
-// Otherwise the result has the input dtype.
-template <int DT, int NT, int G, int S, bool PACKED, bool SPLIT>
-__global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
-    const void* src, const float* __restrict__ lse, int n_rt, uint32_t rows, uint32_t stride,
-    uint64_t plane_bytes, uint32_t lse_plane, float scale, float inv_scale,
-    void* __restrict__ out, float* __restrict__ out_lse, OutMap om) {
-    static_assert(!SPLIT || DT != LSEC_FP32, "fp32 partials already give fp32 results");
-    constexpr int E = Elem<DT>::kEpc;
-    constexpr uint32_t ES = sizeof(typename Elem<DT>::T);
-    constexpr int RPS = kBlock / G;  // rows per slot
-    constexpr int D = G * E;
-    constexpr int PG = tiled_pg<S, (NT > 0 ? NT : 16)>();
-    static_assert(NT == 0 || NT % PG == 0, "plane groups must tile N");
-    const int N = NT > 0 ? NT : n_rt;  // 2 <= n_rt <= 16
-    // Plane n0 + p exists (always for a compiled-in N).
-    auto has = [&](int n) { return NT > 0 || n < N; };
-    static_assert(RPS >= 1 && kBlock % G == 0, "a row's lanes must fit the block");
-    const uint32_t t = threadIdx.x;
-    const uint32_t rib = t / G;
-    const uint32_t lane = t % G;
-    const uint32_t j = t & 15u;
-    const uint32_t row0 = xcd_chunked_block(blockIdx.x, gridDim.x) * (RPS * S);
-    const char* base = reinterpret_cast<const char*>(src);
-
-    uint32_t row[S], off[S];
-    float lw[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        row[s] = row0 + s * RPS + rib;
-        const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
-        off[s] = (rc * stride + lane * (SPLIT ? E / 2 : E)) * ES;
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
-        float l = -__builtin_inff();
-        if (int(j) < N) {
-            if (PACKED)
-                l = ld_tail(base + j * plane_bytes + (rc * stride + D) * ES);
-            else
-                l = lse[j * lse_plane + rc];
-        }
-        lw[s] = l;
-    }
-    // The first plane group's loads go out right behind the LSE loads, so the
-    // LSE round trip overlaps the data instead of preceding it (small,
-    // latency-bound calls pay for exactly that) and the reductions below run
-    // while the data is in flight.
-    u32x4 v[PG][S];
-    auto load_group = [&](int n0) {
-#pragma unroll
-        for (int p = 0; p < PG; ++p) {
-            if (!has(n0 + p)) break;
-            const char* pb = base + uint64_t(n0 + p) * plane_bytes;
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
-                if constexpr (SPLIT) {
-                    const u32x2_a4 lo = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x2_a4*>(pb + off[s]));
-                    const u32x2_a4 hi = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x2_a4*>(pb + off[s] + D * ES / 2));
-                    v[p][s] = u32x4{lo.x, lo.y, hi.x, hi.y};
-                } else {
-                    v[p][s] = PACKED ? ld16_a4_at(pb + off[s]) : ld16_nt_at(pb + off[s]);
-                }
-            }
-        }
-    };
-    load_group(0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const float l = int(j) < N ? sanitize(lw[s]) : -__builtin_inff();
-        float m = row16_max(l);
-        if (m == -__builtin_inff()) m = 0.0f;
-        const float w = int(j) < N ? weight(l - m, scale) : 0.0f;
-        const float sum = row16_sum(w);
-        lw[s] = w * (1.0f / fmaxf(sum, 1e-10f));
-        if (out_lse != nullptr && lane == 0 && row[s] < rows)
-            out_lse[out_row(row[s], om)] = global_lse(sum, m, inv_scale);
-    }
-
-    float acc[S][E];
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int k = 0; k < E; ++k) acc[s][k] = 0.0f;
-#pragma unroll 1
-    for (int n0 = 0; n0 < N; n0 += PG) {
-        if (n0 > 0) load_group(n0);
-        __builtin_amdgcn_sched_barrier(0);  // all PG*S loads issued before the first is used
-#pragma unroll
-        for (int p = 0; p < PG; ++p) {
-            if (!has(n0 + p)) break;
-#pragma unroll
-            for (int s = 0; s < S; ++s) fma_chunk<DT>(v[p][s], lane_value<G>(lw[s], n0 + p), acc[s]);
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        if (row[s] >= rows) continue;
-        if constexpr (SPLIT) {
-            float* p = static_cast<float*>(out) + uint64_t(out_row(row[s], om)) * D + lane * 4;
-            st16(p, f32_chunk(acc[s][0], acc[s][1], acc[s][2], acc[s][3]));
-            st16(p + D / 2, f32_chunk(acc[s][4], acc[s][5], acc[s][6], acc[s][7]));
-        } else {
-            store_chunk<DT>(out, uint64_t(out_row(row[s], om)) * D + lane * E, acc[s], 0);
-        }
-    }
 }
 
 // ---------------------------------------------------------------- combine (general path)
@@ -953,86 +538,6 @@ void dispatch_n(const void* src, const float* lse, int N, uint32_t rows, int D, 
 constexpr uint64_t kTiledMinBlocks = 2048;
 constexpr uint64_t kTiledMinBlocksN16 = 1024;
 
-struct TiledArgs {
-    const void* src;
-    const float* lse;
-    int n;
-    uint32_t rows, stride;
-    uint64_t plane_bytes;
-    uint32_t lse_plane;
-    float scale, inv_scale;
-    void* out;
-    int out_f32;
-    float* out_lse;
-    OutMap om;
-    hipStream_t st;
-};
-
-// Occupancy cap for the tiled combine, as dynamic LDS that the kernel never
-// touches (a CU has 160 KB): S = 16 launches run at most 1 block per CU
-// (90 KB), S = 8 at most 2 (56 KB each), S = 4 at most 4 (36 KB each). HBM
-// streams better from fewer, deeper waves; measured on MI355X against the
-// occupancy the registers allow: fp32 N=8 D=512 2^16 rows (S = 16, 2 blocks)
-// 5.7 % faster, bf16 N=8 D=512 2^16 rows (S = 8, 3 blocks) 2.8 %, bf16 N=8
-// D=128 2^17 rows (S = 4, 7 blocks) 7.0 %. The 16-bit S = 16 kernels hold
-// one block per CU by their registers anyway. S <= 2 serves inputs too small
-// to fill the chip, and capping it (or the pack, or the corrected partial)
-// measured slower.
-constexpr size_t tiled_lds_cap(int S) {
-    return S == 16 ? 90000 : (S == 8 ? 56000 : (S == 4 ? 36000 : 0));
-}
-
-template <int DT, int NT, int G, bool PACKED, bool SPLIT>
-void launch_tiled_s(int S, const TiledArgs& a) {
-    constexpr uint32_t RPS = kBlock / G;
-    const unsigned blocks = (a.rows + RPS * S - 1) / (RPS * S);
-#define LSEC_TILED(SV)                                                                         \
-    combine_tiled_kernel<DT, NT, G, SV, PACKED, SPLIT><<<blocks, kBlock, tiled_lds_cap(SV), a.st>>>( \
-        a.src, a.lse, a.n, a.rows, a.stride, a.plane_bytes, a.lse_plane, a.scale, a.inv_scale,   \
-        a.out, a.out_lse, a.om)
-    switch (S) {
-        case 16: LSEC_TILED(16); break;
-        case 8: LSEC_TILED(8); break;
-        case 4: LSEC_TILED(4); break;
-        case 2: LSEC_TILED(2); break;
-        default: LSEC_TILED(1); break;
-    }
-#undef LSEC_TILED
-}
-
-template <int DT, int G, bool PACKED, bool SPLIT>
-void launch_tiled_n(int N, int S, const TiledArgs& a) {
-    switch (N) {
-        case 2: launch_tiled_s<DT, 2, G, PACKED, SPLIT>(S, a); break;
-        case 4: launch_tiled_s<DT, 4, G, PACKED, SPLIT>(S, a); break;
-        case 8: launch_tiled_s<DT, 8, G, PACKED, SPLIT>(S, a); break;
-        case 16: launch_tiled_s<DT, 16, G, PACKED, SPLIT>(S, a); break;
-        default: launch_tiled_s<DT, 0, G, PACKED, SPLIT>(S, a); break;  // 2 < N < 16, at run time
-    }
-}
-
-template <int DT, bool PACKED, bool SPLIT>
-void launch_tiled_d(int N, int S, int D, const TiledArgs& a) {
-    constexpr int E = Elem<DT>::kEpc;
-    switch (D) {
-        case 128: launch_tiled_n<DT, 128 / E, PACKED, SPLIT>(N, S, a); break;
-        case 256: launch_tiled_n<DT, 256 / E, PACKED, SPLIT>(N, S, a); break;
-        default: launch_tiled_n<DT, 512 / E, PACKED, SPLIT>(N, S, a); break;
-    }
-}
-
-// 16-bit partials with an fp32 result take the split-load variant.
-template <int DT, bool PACKED>
-void launch_tiled(int N, int S, int D, const TiledArgs& a) {
-    if constexpr (DT != LSEC_FP32) {
-        if (a.out_f32) {
-            launch_tiled_d<DT, PACKED, true>(N, S, D, a);
-            return;
-        }
-    }
-    launch_tiled_d<DT, PACKED, false>(N, S, D, a);
-}
-
 // Which combine kernel serves a call. `fast` = fast_d(D), rows < 2^31 and the
 // buffers meet the 16-byte (separate) or 4-byte (packed) alignment; otherwise
 // the element-wise kernel runs.
@@ -1236,6 +741,9 @@ int combine_entry(const void* outputs, int64_t plane_stride, const float* lses,
 }
 
 }  // namespace
+}  // namespace lsec_detail
+
+using namespace lsec_detail;
 
 // ---------------------------------------------------------------- C ABI
 

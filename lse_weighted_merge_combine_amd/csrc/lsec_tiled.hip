@@ -1,0 +1,237 @@
+// lsec_tiled.hip -- the tiled combine of liblsec.so for one element type,
+// compiled once per type (LSEC_TILED_DT = LSEC_BF16, LSEC_FP16, LSEC_FP32) so
+// that its many instantiations build in parallel. The host code in lsec.hip
+// calls launch_tiled<DT, PACKED>, instantiated at the end of this file.
+//
+// Build with -Xclang -target-feature -Xclang -packed-fp32-ops and without
+// fast-math (the NaN / infinity tests must survive).
+
+#include "lsec_device.h"
+
+#ifndef LSEC_TILED_DT
+#error "compile with -DLSEC_TILED_DT=<LSEC_BF16 | LSEC_FP16 | LSEC_FP32>"
+#endif
+
+namespace lsec_detail {
+namespace {
+
+// ---------------------------------------------------------------- combine (tiled path)
+//
+// For D in {128, 256, 512} and 2 <= N <= 16 (N = 2, 4, 8, 16 compiled in; other
+// N at run time, NT = 0, with the plane groups of N = 16 and the planes past N
+// skipped by a uniform branch). A row is owned by
+// G = D / kEpc lanes (16 bytes each). A block of 256 threads covers S slots of
+// 256/G consecutive rows, so per plane it reads one contiguous run of
+// S*256/G rows (32 KB at S = 8). The planes are walked in order, PG at a time:
+// each lane has PG*S 16-byte loads in flight and a block keeps few DRAM pages
+// open. On MI355X this streams markedly faster than issuing all N planes of
+// one row at once, which spreads every block over N distant pages.
+//
+// Weights: lane j of each 16-lane DPP row loads shard j's LSE for its row
+// (j < N; the 16-lane segments of a row group hold identical copies). Max and
+// sum are 16-lane DPP reductions; during the sweep the weight of plane n comes
+// from lane n of the segment (a lane shuffle, or readlane when a wave holds
+// one row or part of one). The global LSE is written before the sweep so
+// nothing but the weights stays live through it.
+//
+// Addresses: plane n starts at n * plane_bytes (uniform, scalar registers);
+// a lane's chunk sits at a 32-bit byte offset inside the plane; shard j's LSE
+// of row r is lse[j * lse_plane + r]. The host checks plane_bytes < 2^32 and
+// N * lse_plane < 2^32. Rows past the end of the last block are clamped to
+// the last row for loading and are not stored.
+__device__ __forceinline__ u32x4 ld16_nt_at(const char* p) { return ld16(p); }
+__device__ __forceinline__ u32x4 ld16_a4_at(const char* p) { return ld16_a4(p); }
+
+template <int S, int NT>
+constexpr int tiled_pg() {
+    return (S >= 4 ? 1 : (8 / S < NT ? 8 / S : NT));
+}
+
+// SPLIT (fp32 result from 16-bit partials): lane l of a row owns elements
+// [4l, 4l + 4) and [D/2 + 4l, D/2 + 4l + 4) instead of [8l, 8l + 8), read as
+// two 8-byte loads, so each of its two 16-byte fp32 stores belongs to an
+// instruction that writes one contiguous half of the row (whole cache
+// lines). Measured on MI355X: 6.6 % faster on N=16 D=128 2^19 rows, 4.5 % on
+// N=8 D=512 2^16 rows, than 16-byte loads with two interleaved stores.
+// Otherwise the result has the input dtype.
+template <int DT, int NT, int G, int S, bool PACKED, bool SPLIT>
+__global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
+    const void* src, const float* __restrict__ lse, int n_rt, uint32_t rows, uint32_t stride,
+    uint64_t plane_bytes, uint32_t lse_plane, float scale, float inv_scale,
+    void* __restrict__ out, float* __restrict__ out_lse, OutMap om) {
+    static_assert(!SPLIT || DT != LSEC_FP32, "fp32 partials already give fp32 results");
+    constexpr int E = Elem<DT>::kEpc;
+    constexpr uint32_t ES = sizeof(typename Elem<DT>::T);
+    constexpr int RPS = kBlock / G;  // rows per slot
+    constexpr int D = G * E;
+    constexpr int PG = tiled_pg<S, (NT > 0 ? NT : 16)>();
+    static_assert(NT == 0 || NT % PG == 0, "plane groups must tile N");
+    const int N = NT > 0 ? NT : n_rt;  // 2 <= n_rt <= 16
+    // Plane n0 + p exists (always for a compiled-in N).
+    auto has = [&](int n) { return NT > 0 || n < N; };
+    static_assert(RPS >= 1 && kBlock % G == 0, "a row's lanes must fit the block");
+    const uint32_t t = threadIdx.x;
+    const uint32_t rib = t / G;
+    const uint32_t lane = t % G;
+    const uint32_t j = t & 15u;
+    const uint32_t row0 = xcd_chunked_block(blockIdx.x, gridDim.x) * (RPS * S);
+    const char* base = reinterpret_cast<const char*>(src);
+
+    uint32_t row[S], off[S];
+    float lw[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        row[s] = row0 + s * RPS + rib;
+        const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
+        off[s] = (rc * stride + lane * (SPLIT ? E / 2 : E)) * ES;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const uint32_t rc = row[s] < rows ? row[s] : rows - 1;
+        float l = -__builtin_inff();
+        if (int(j) < N) {
+            if (PACKED)
+                l = ld_tail(base + j * plane_bytes + (rc * stride + D) * ES);
+            else
+                l = lse[j * lse_plane + rc];
+        }
+        lw[s] = l;
+    }
+    // The first plane group's loads go out right behind the LSE loads, so the
+    // LSE round trip overlaps the data instead of preceding it (small,
+    // latency-bound calls pay for exactly that) and the reductions below run
+    // while the data is in flight.
+    u32x4 v[PG][S];
+    auto load_group = [&](int n0) {
+#pragma unroll
+        for (int p = 0; p < PG; ++p) {
+            if (!has(n0 + p)) break;
+            const char* pb = base + uint64_t(n0 + p) * plane_bytes;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                if constexpr (SPLIT) {
+                    const u32x2_a4 lo = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x2_a4*>(pb + off[s]));
+                    const u32x2_a4 hi = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x2_a4*>(pb + off[s] + D * ES / 2));
+                    v[p][s] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                } else {
+                    v[p][s] = PACKED ? ld16_a4_at(pb + off[s]) : ld16_nt_at(pb + off[s]);
+                }
+            }
+        }
+    };
+    load_group(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float l = int(j) < N ? sanitize(lw[s]) : -__builtin_inff();
+        float m = row16_max(l);
+        if (m == -__builtin_inff()) m = 0.0f;
+        const float w = int(j) < N ? weight(l - m, scale) : 0.0f;
+        const float sum = row16_sum(w);
+        lw[s] = w * (1.0f / fmaxf(sum, 1e-10f));
+        if (out_lse != nullptr && lane == 0 && row[s] < rows)
+            out_lse[out_row(row[s], om)] = global_lse(sum, m, inv_scale);
+    }
+
+    float acc[S][E];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int k = 0; k < E; ++k) acc[s][k] = 0.0f;
+#pragma unroll 1
+    for (int n0 = 0; n0 < N; n0 += PG) {
+        if (n0 > 0) load_group(n0);
+        __builtin_amdgcn_sched_barrier(0);  // all PG*S loads issued before the first is used
+#pragma unroll
+        for (int p = 0; p < PG; ++p) {
+            if (!has(n0 + p)) break;
+#pragma unroll
+            for (int s = 0; s < S; ++s) fma_chunk<DT>(v[p][s], lane_value<G>(lw[s], n0 + p), acc[s]);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        if (row[s] >= rows) continue;
+        if constexpr (SPLIT) {
+            float* p = static_cast<float*>(out) + uint64_t(out_row(row[s], om)) * D + lane * 4;
+            st16(p, f32_chunk(acc[s][0], acc[s][1], acc[s][2], acc[s][3]));
+            st16(p + D / 2, f32_chunk(acc[s][4], acc[s][5], acc[s][6], acc[s][7]));
+        } else {
+            store_chunk<DT>(out, uint64_t(out_row(row[s], om)) * D + lane * E, acc[s], 0);
+        }
+    }
+}
+
+}  // namespace
+
+// Occupancy cap for the tiled combine, as dynamic LDS that the kernel never
+// touches (a CU has 160 KB): S = 16 launches run at most 1 block per CU
+// (90 KB), S = 8 at most 2 (56 KB each), S = 4 at most 4 (36 KB each). HBM
+// streams better from fewer, deeper waves; measured on MI355X against the
+// occupancy the registers allow: fp32 N=8 D=512 2^16 rows (S = 16, 2 blocks)
+// 5.7 % faster, bf16 N=8 D=512 2^16 rows (S = 8, 3 blocks) 2.8 %, bf16 N=8
+// D=128 2^17 rows (S = 4, 7 blocks) 7.0 %. The 16-bit S = 16 kernels hold
+// one block per CU by their registers anyway. S <= 2 serves inputs too small
+// to fill the chip, and capping it (or the pack, or the corrected partial)
+// measured slower.
+constexpr size_t tiled_lds_cap(int S) {
+    return S == 16 ? 90000 : (S == 8 ? 56000 : (S == 4 ? 36000 : 0));
+}
+
+template <int DT, int NT, int G, bool PACKED, bool SPLIT>
+void launch_tiled_s(int S, const TiledArgs& a) {
+    constexpr uint32_t RPS = kBlock / G;
+    const unsigned blocks = (a.rows + RPS * S - 1) / (RPS * S);
+#define LSEC_TILED(SV)                                                                         \
+    combine_tiled_kernel<DT, NT, G, SV, PACKED, SPLIT><<<blocks, kBlock, tiled_lds_cap(SV), a.st>>>( \
+        a.src, a.lse, a.n, a.rows, a.stride, a.plane_bytes, a.lse_plane, a.scale, a.inv_scale,   \
+        a.out, a.out_lse, a.om)
+    switch (S) {
+        case 16: LSEC_TILED(16); break;
+        case 8: LSEC_TILED(8); break;
+        case 4: LSEC_TILED(4); break;
+        case 2: LSEC_TILED(2); break;
+        default: LSEC_TILED(1); break;
+    }
+#undef LSEC_TILED
+}
+
+template <int DT, int G, bool PACKED, bool SPLIT>
+void launch_tiled_n(int N, int S, const TiledArgs& a) {
+    switch (N) {
+        case 2: launch_tiled_s<DT, 2, G, PACKED, SPLIT>(S, a); break;
+        case 4: launch_tiled_s<DT, 4, G, PACKED, SPLIT>(S, a); break;
+        case 8: launch_tiled_s<DT, 8, G, PACKED, SPLIT>(S, a); break;
+        case 16: launch_tiled_s<DT, 16, G, PACKED, SPLIT>(S, a); break;
+        default: launch_tiled_s<DT, 0, G, PACKED, SPLIT>(S, a); break;  // 2 < N < 16, at run time
+    }
+}
+
+template <int DT, bool PACKED, bool SPLIT>
+void launch_tiled_d(int N, int S, int D, const TiledArgs& a) {
+    constexpr int E = Elem<DT>::kEpc;
+    switch (D) {
+        case 128: launch_tiled_n<DT, 128 / E, PACKED, SPLIT>(N, S, a); break;
+        case 256: launch_tiled_n<DT, 256 / E, PACKED, SPLIT>(N, S, a); break;
+        default: launch_tiled_n<DT, 512 / E, PACKED, SPLIT>(N, S, a); break;
+    }
+}
+
+// 16-bit partials with an fp32 result take the split-load variant.
+template <int DT, bool PACKED>
+void launch_tiled(int N, int S, int D, const TiledArgs& a) {
+    if constexpr (DT != LSEC_FP32) {
+        if (a.out_f32) {
+            launch_tiled_d<DT, PACKED, true>(N, S, D, a);
+            return;
+        }
+    }
+    launch_tiled_d<DT, PACKED, false>(N, S, D, a);
+}
+
+template void launch_tiled<LSEC_TILED_DT, false>(int, int, int, const TiledArgs&);
+template void launch_tiled<LSEC_TILED_DT, true>(int, int, int, const TiledArgs&);
+
+}  // namespace lsec_detail
