@@ -128,6 +128,33 @@ int lsec_combine_planes(const void* outputs, int64_t plane_stride, const float* 
                         int dtype, int base, void* out, float* out_lse, void* stream);
 
 /*
+ * lsec_combine_planes_valid -- lsec_combine_planes whose count of valid tokens
+ * lives in device memory: the `query_start_loc` argument of the same page's
+ * `DirectDCPA2AWorkspace.lse_reduce` (that op's body is not given; the reading
+ * taken here is that its masking marks the tokens past the last request as
+ * padding). query_start_loc holds the num_reqs + 1 cumulative token offsets
+ * of the step's requests (int32, device memory); the kernels read
+ * Tv = query_start_loc[num_reqs], clamped to [0, T], and combine tokens
+ * [0, Tv) exactly as lsec_combine_planes does. Tokens [Tv, T) are padding:
+ * their rows of out and out_lse are not written and their planes are not
+ * read. T is the token capacity of out (a padded batch, e.g. a captured
+ * graph's size), so the host never has to read Tv. The per-request sequence
+ * lengths of that op are not needed: a shard with no keys for a request
+ * carries a NaN or infinite LSE, which the combine already drops.
+ *   query_start_loc : int32 [num_reqs + 1], device memory, 4-byte aligned;
+ *                     only element num_reqs is read
+ *   num_reqs        : >= 0
+ *   other arguments : as lsec_combine_planes (T = the capacity)
+ * Errors: as lsec_combine_planes; NULL also for a NULL query_start_loc when
+ * T * H > 0, SHAPE for num_reqs < 0 or H >= 2^32, ALIGNMENT for a misaligned
+ * query_start_loc.
+ */
+int lsec_combine_planes_valid(const void* outputs, int64_t plane_stride, const float* lses,
+                              int64_t lse_plane_stride, int64_t N, int64_t T, int64_t H,
+                              int64_t D, int dtype, int base, const int32_t* query_start_loc,
+                              int64_t num_reqs, void* out, float* out_lse, void* stream);
+
+/*
  * lsec_merge -- the merge of page "vllm_ascend/attention/context_parallel/
  * sfa_cp.py", `_merge_dcp_outputs_with_torch`: the combine of lsec_combine over
  * received planes whose token index is the first or the second of the two row

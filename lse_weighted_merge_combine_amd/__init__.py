@@ -25,7 +25,8 @@ Entry points (same names as the C ABI):
 * ``lsec_combine_planes(outputs, lses, num_tokens)`` -- the local combine of
   the fused direct all-to-all on the page "vllm.v1.attention.ops.dcp"
   (``DirectDCPA2AWorkspace.lse_reduce``): the first ``num_tokens`` tokens of
-  one ubatch slot's receive planes.
+  one ubatch slot's receive planes; with ``query_start_loc`` the valid count
+  is read on the device and ``num_tokens`` is the padded capacity.
 
 * ``lsec_correct_partial(lses, rank, partial)`` -- the local step of the LSE
   all-gather + output reduce-scatter strategies named on the page
@@ -107,6 +108,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_unpack.argtypes = [P, I64, I64, I64, I64, I, P, P, P]
     lib.lsec_combine_planes.restype = I
     lib.lsec_combine_planes.argtypes = [P, I64, P, I64, I64, I64, I64, I64, I, I, P, P, P]
+    lib.lsec_combine_planes_valid.restype = I
+    lib.lsec_combine_planes_valid.argtypes = [P, I64, P, I64, I64, I64, I64, I64, I, I, P, I64, P,
+                                              P, P]
     lib.lsec_merge.restype = I
     lib.lsec_merge.argtypes = [P, P, I64, I64, I64, I64, I, I, I, P, P, P]
     lib.lsec_correct_partial.restype = I
@@ -213,7 +217,7 @@ def lsec_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
 def lsec_combine_planes(outputs: torch.Tensor, lses: torch.Tensor, num_tokens: int,
                         base_e: bool = True, return_lse: bool = False,
                         out: torch.Tensor | None = None, out_lse: torch.Tensor | None = None,
-                        stream=None, out_dtype=None):
+                        stream=None, out_dtype=None, query_start_loc: torch.Tensor | None = None):
     """Combine the first ``num_tokens`` tokens of receive planes
     outputs [N,T_max,H,D] + lses [N,T_max,H] -> [num_tokens,H,D] (+ [num_tokens,H]).
 
@@ -221,6 +225,12 @@ def lsec_combine_planes(outputs: torch.Tensor, lses: torch.Tensor, num_tokens: i
     (``received_output[ubatch][slot]``). Each plane must be contiguous; the
     stride between planes may be anything at least a plane's size (so a view
     such as ``buf[u, s]`` or ``buf[u, s, :, :T]`` works as is).
+
+    ``query_start_loc`` (int32 [num_reqs + 1] on the same device, as passed to
+    ``DirectDCPA2AWorkspace.lse_reduce``) makes ``num_tokens`` a capacity: the
+    kernels read the valid count ``query_start_loc[-1]`` (clamped to
+    [0, num_tokens]) and leave the rows of later tokens (padding) unwritten,
+    as the page's ``new_empty`` output leaves them (lsec_combine_planes_valid).
     """
     lib = load_library()
     if outputs.dim() != 4 or lses.dim() != 3 or tuple(lses.shape) != tuple(outputs.shape[:3]):
@@ -248,11 +258,24 @@ def lsec_combine_planes(outputs: torch.Tensor, lses: torch.Tensor, num_tokens: i
     _check_out(out, (T, H, D), rdt, dev)
     if return_lse:
         _check_out(out_lse, (T, H), torch.float32, dev)
-    st = lib.lsec_combine_planes(_ptr(outputs), outputs.stride(0) if N > 1 else T * H * D,
-                                 _ptr(lses), lses.stride(0) if N > 1 else T * H, N, T, H, D, dt,
-                                 LSEC_BASE_E if base_e else LSEC_BASE_2, _ptr(out),
-                                 _ptr(out_lse) if return_lse else None, _stream(dev, stream))
-    _raise_on(st, "lsec_combine_planes")
+    pstride = outputs.stride(0) if N > 1 else T * H * D
+    lstride = lses.stride(0) if N > 1 else T * H
+    base = LSEC_BASE_E if base_e else LSEC_BASE_2
+    if query_start_loc is None:
+        st = lib.lsec_combine_planes(_ptr(outputs), pstride, _ptr(lses), lstride, N, T, H, D, dt,
+                                     base, _ptr(out), _ptr(out_lse) if return_lse else None,
+                                     _stream(dev, stream))
+        _raise_on(st, "lsec_combine_planes")
+    else:
+        q = query_start_loc
+        if q.dtype != torch.int32 or q.dim() != 1 or q.numel() < 1 or q.device != dev:
+            raise ValueError("query_start_loc must be a 1-D int32 tensor of num_reqs + 1 "
+                             f"offsets on {dev}, got {q.dtype} {tuple(q.shape)} on {q.device}")
+        st = lib.lsec_combine_planes_valid(_ptr(outputs), pstride, _ptr(lses), lstride, N, T, H, D,
+                                           dt, base, _ptr(q), q.numel() - 1, _ptr(out),
+                                           _ptr(out_lse) if return_lse else None,
+                                           _stream(dev, stream))
+        _raise_on(st, "lsec_combine_planes_valid")
     return (out, out_lse) if return_lse else out
 
 

@@ -55,6 +55,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     const uint32_t lane = t - rib * g.d;
     if (rib >= rows_per_block) return;
     const uint32_t row = blockIdx.x * rows_per_block + rib;
+    rows = valid_rows(rows, om);
     if (row >= rows) return;
     const int N = NT > 0 ? NT : n_rt;
     const typename Elem<DT>::T* rp = src + int64_t(row) * stride;
@@ -137,7 +138,12 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
     const typename Elem<DT>::T* __restrict__ src, const float* __restrict__ lse, int N,
     int64_t rows, int64_t stride, int64_t plane, int64_t lse_plane, int64_t D, float scale,
     float inv_scale, void* __restrict__ out, int out_f32, float* __restrict__ out_lse,
-    int64_t map_a, int64_t map_c) {
+    int64_t map_a, int64_t map_c, const int32_t* valid, int64_t rows_per_token) {
+    if (valid != nullptr) {  // only the rows of the first *valid tokens
+        const int32_t tv = *valid;
+        const int64_t vr = tv <= 0 ? 0 : int64_t(tv) * rows_per_token;
+        if (vr < rows) rows = vr;
+    }
     const int64_t total = rows * D;
     for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < total;
          i += int64_t(gridDim.x) * kBlock) {
@@ -588,7 +594,8 @@ void run_combine_dt(const void* src, const float* lse, int64_t N, int64_t rows, 
         const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
         combine_elems_kernel<DT, PACKED><<<general_grid(rows * D), kBlock, 0, st>>>(
             static_cast<const typename Elem<DT>::T*>(src), lse, int(N), rows, stride, pl.plane,
-            pl.lse_plane, D, scale, inv_scale, out, out_f32, out_lse, map_a, map_c);
+            pl.lse_plane, D, scale, inv_scale, out, out_f32, out_lse, map_a, map_c, om.valid,
+            int64_t(om.rows_per_token));
     }
 }
 
@@ -597,8 +604,10 @@ void run_combine_dt(const void* src, const float* lse, int64_t N, int64_t rows, 
 template <bool PACKED>
 int run_combine(const void* src, const float* lse, int64_t N, int64_t rows, int64_t D,
                 const Dtype& dt, int base, void* out, float* out_lse, bool fast, hipStream_t st,
-                Planes pl, int64_t map_a = 0, int64_t map_c = 1) {
-    const OutMap om{uint32_t(map_a), make_fastdiv(uint32_t(map_c))};
+                Planes pl, int64_t map_a = 0, int64_t map_c = 1, const int32_t* valid = nullptr,
+                int64_t rows_per_token = 0) {
+    const OutMap om{uint32_t(map_a), make_fastdiv(uint32_t(map_c)), valid,
+                    uint32_t(rows_per_token)};
     const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
     const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
     const CombinePlan plan = plan_combine(N, rows, D, dt.esize, PACKED, fast, pl);
@@ -709,13 +718,17 @@ void launch_unpack(bool fast, const void* recv, int64_t total_rows, int64_t D, i
     }
 }
 
-// Shared by lsec_combine, lsec_merge and lsec_combine_planes: rows (b, h) of a
-// [B, H] grid, stored in input order or, when `transposed`, at row h * B + b.
-// Plane n of the partial outputs starts at element n * plane_stride, its LSEs
-// at n * lse_plane_stride; the first B * H rows of each plane are combined.
+// Shared by lsec_combine, lsec_merge and lsec_combine_planes(_valid): rows
+// (b, h) of a [B, H] grid, stored in input order or, when `transposed`, at row
+// h * B + b. Plane n of the partial outputs starts at element n * plane_stride,
+// its LSEs at n * lse_plane_stride; the first B * H rows of each plane are
+// combined, or, when `masked`, those of the first query_start_loc[num_reqs]
+// tokens b (read by the kernels).
 int combine_entry(const void* outputs, int64_t plane_stride, const float* lses,
                   int64_t lse_plane_stride, int64_t N, int64_t B, int64_t H, int64_t D, int dtype,
-                  int base, void* out, float* out_lse, void* stream, bool transposed) {
+                  int base, void* out, float* out_lse, void* stream, bool transposed,
+                  bool masked = false, const int32_t* query_start_loc = nullptr,
+                  int64_t num_reqs = 0) {
     if (N < 1 || B < 0 || H < 1 || D < 1 || N > (int64_t(1) << 30)) return LSEC_ERR_SHAPE;
     Dtype dt;
     if (!parse_dtype(dtype, true, &dt)) return LSEC_ERR_DTYPE;
@@ -723,21 +736,24 @@ int combine_entry(const void* outputs, int64_t plane_stride, const float* lses,
     int64_t rows, rd, ob, span, lspan;
     if (!mul_ok(B, H, &rows) || !mul_ok(rows, D, &rd) || !mul_ok(rd, dt.out_esize, &ob))
         return LSEC_ERR_SHAPE;
-    if (plane_stride < rd || lse_plane_stride < rows) return LSEC_ERR_SHAPE;
+    if (plane_stride < rd || lse_plane_stride < rows || num_reqs < 0 ||
+        (masked && H > int64_t(UINT32_MAX)))
+        return LSEC_ERR_SHAPE;
     if (!mul_ok(N - 1, plane_stride, &span) || __builtin_add_overflow(span, rd, &span) ||
         !mul_ok(span, dt.esize, &span) || !mul_ok(N - 1, lse_plane_stride, &lspan) ||
         __builtin_add_overflow(lspan, rows, &lspan) || !mul_ok(lspan, 4, &lspan))
         return LSEC_ERR_SHAPE;
     if (rows == 0) return LSEC_OK;
-    if (!outputs || !lses || !out) return LSEC_ERR_NULL;
+    if (!outputs || !lses || !out || (masked && !query_start_loc)) return LSEC_ERR_NULL;
     if (!aligned(outputs, dt.esize) || !aligned(out, dt.out_esize) || !aligned(lses, 4) ||
-        (out_lse && !aligned(out_lse, 4)))
+        (out_lse && !aligned(out_lse, 4)) || (masked && !aligned(query_start_loc, 4)))
         return LSEC_ERR_ALIGNMENT;
     const bool fast = fast_d(D, dt.esize) && rows < (int64_t(1) << 31) && aligned(outputs, 16) &&
                       aligned(out, 16) && (plane_stride * dt.esize) % 16 == 0;
     return run_combine<false>(outputs, lses, N, rows, D, dt, base, out, out_lse, fast,
                               static_cast<hipStream_t>(stream), Planes{plane_stride, lse_plane_stride},
-                              transposed ? B : 0, transposed ? H : 1);
+                              transposed ? B : 0, transposed ? H : 1,
+                              masked ? query_start_loc + num_reqs : nullptr, H);
 }
 
 }  // namespace
@@ -813,6 +829,14 @@ int lsec_combine_planes(const void* outputs, int64_t plane_stride, const float* 
                         int dtype, int base, void* out, float* out_lse, void* stream) {
     return combine_entry(outputs, plane_stride, lses, lse_plane_stride, N, T, H, D, dtype, base,
                          out, out_lse, stream, false);
+}
+
+int lsec_combine_planes_valid(const void* outputs, int64_t plane_stride, const float* lses,
+                              int64_t lse_plane_stride, int64_t N, int64_t T, int64_t H,
+                              int64_t D, int dtype, int base, const int32_t* query_start_loc,
+                              int64_t num_reqs, void* out, float* out_lse, void* stream) {
+    return combine_entry(outputs, plane_stride, lses, lse_plane_stride, N, T, H, D, dtype, base,
+                         out, out_lse, stream, false, true, query_start_loc, num_reqs);
 }
 
 int lsec_merge(const void* outputs, const float* lses, int64_t N, int64_t A, int64_t C,

@@ -41,7 +41,21 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f) {
 struct OutMap {
     uint32_t a;  // A, or 0 for the identity
     FastDiv c;   // divides by C
+    // When set, only the rows of the first *valid tokens (rows_per_token rows
+    // each) are read and written; the count lives in device memory.
+    const int32_t* valid;
+    uint32_t rows_per_token;
 };
+
+// The rows a launch combines: all `rows`, or those of the first *om.valid
+// tokens (clamped to [0, rows]).
+__device__ __forceinline__ uint32_t valid_rows(uint32_t rows, const OutMap& om) {
+    if (om.valid == nullptr) return rows;
+    const int32_t t = *om.valid;
+    if (t <= 0) return 0;
+    const uint64_t r = uint64_t(uint32_t(t)) * om.rows_per_token;
+    return r < rows ? uint32_t(r) : rows;
+}
 
 __device__ __forceinline__ uint32_t out_row(uint32_t r, OutMap om) {
     if (om.a == 0) return r;

@@ -75,6 +75,10 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     const uint32_t lane = t % G;
     const uint32_t j = t & 15u;
     const uint32_t row0 = xcd_chunked_block(blockIdx.x, gridDim.x) * (RPS * S);
+    if (om.valid != nullptr) {
+        rows = valid_rows(rows, om);
+        if (row0 >= rows) return;  // every row of the block is padding
+    }
     const char* base = reinterpret_cast<const char*>(src);
 
     uint32_t row[S], off[S];

@@ -26,9 +26,12 @@ for 16-bit elements, 1 for fp32).
 Parity status: every function here is pinned by the CPU tests (closed forms,
 brute-force sharded attention, library log-sum-exp / softmax, the second
 formulation of the merge on the Ascend SFA context-parallel page, the simulated
-all-to-all). One reading is not pinned against any source: the order of the
+all-to-all). Two readings are not pinned against any source: the order of the
 LSE's bytes inside the two tail elements of a 16-bit packed row (memory order
-is taken); the round trip through pack and unpack is.
+is taken; the round trip through pack and unpack is pinned), and
+``valid_tokens``, the valid-token masking of the direct all-to-all's reduce
+(parity unpinned; ``lse_combine_valid`` applies it in front of the pinned
+``lse_combine``).
 """
 from __future__ import annotations
 
@@ -150,6 +153,28 @@ def lse_combine(outputs: np.ndarray, lses: np.ndarray, dtype: str, base2: bool =
     _check(_load().oracle_lse_combine(o.ctypes.data, _DT[dtype], l.ctypes.data, N, B, H, D,
                                       int(base2), y.ctypes.data, L.ctypes.data), "lse_combine")
     return y, L
+
+
+def valid_tokens(query_start_loc, capacity: int) -> int:
+    """The count of valid tokens of a padded step: the last of the requests'
+    cumulative token offsets, clamped to [0, capacity]. A reading of the
+    ``seq_lens`` / ``query_start_loc`` masking of
+    ``DirectDCPA2AWorkspace.lse_reduce`` (page "vllm.v1.attention.ops.dcp"),
+    whose body the page does not give: tokens past the last request are padding
+    with no result. Parity unpinned (no source fixes the reading)."""
+    t = int(np.asarray(query_start_loc).reshape(-1)[-1])
+    return min(max(t, 0), int(capacity))
+
+
+def lse_combine_valid(outputs: np.ndarray, lses: np.ndarray, query_start_loc, dtype: str,
+                      base2: bool = False):
+    """outputs [N,T,H,D], lses [N,T,H] of a step padded to T tokens ->
+    (y [Tv,H,D], L [Tv,H], Tv): ``lse_combine`` over the first Tv =
+    ``valid_tokens(query_start_loc, T)`` tokens; tokens [Tv, T) have no result."""
+    tv = valid_tokens(query_start_loc, outputs.shape[1])
+    y, L = lse_combine(np.ascontiguousarray(outputs[:, :tv]), np.ascontiguousarray(lses[:, :tv]),
+                       dtype, base2)
+    return y, L, tv
 
 
 def merge(outputs: np.ndarray, lses: np.ndarray, dtype: str, token_dim: int,

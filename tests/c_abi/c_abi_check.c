@@ -214,6 +214,59 @@ static void packed_case(void) {
     free(uo_ref), free(ul_ref), free(uo), free(ul);
 }
 
+/* Planes padded to T tokens; the valid count (query_start_loc[2] = 27) is in
+ * device memory. Tokens [0, 27) match the oracle; the padding rows keep the
+ * 0xff bytes the output was filled with. */
+static void valid_count_case(void) {
+    const int64_t N = 4, T = 40, Tv = 27, H = 4, D = 128, rows = T * H, n_out = N * rows * D;
+    const int32_t qsl[3] = {0, 10, (int32_t)Tv};
+    uint16_t* o = malloc(sizeof(uint16_t) * (size_t)n_out);
+    float* l = malloc(sizeof(float) * (size_t)(N * rows));
+    draw(35, OUT_BF16, n_out, N * rows, o, l, -5.0, 15.0);
+    void* d_o = dev_copy(o, sizeof(uint16_t) * (size_t)n_out);
+    void* d_l = dev_copy(l, sizeof(float) * (size_t)(N * rows));
+    void* d_q = dev_copy(qsl, sizeof(qsl));
+    void* d_y = NULL;
+    float* d_L = NULL;
+    HIP_OK(hipMalloc(&d_y, sizeof(uint16_t) * (size_t)(rows * D)));
+    HIP_OK(hipMalloc((void**)&d_L, sizeof(float) * (size_t)rows));
+    HIP_OK(hipMemset(d_y, 0xff, sizeof(uint16_t) * (size_t)(rows * D)));
+    HIP_OK(hipMemset(d_L, 0xff, sizeof(float) * (size_t)rows));
+    const int st = lsec_combine_planes_valid(d_o, rows * D, (const float*)d_l, rows, N, T, H, D,
+                                             LSEC_BF16, LSEC_BASE_E, (const int32_t*)d_q, 2, d_y,
+                                             d_L, NULL);
+    HIP_OK(hipDeviceSynchronize());
+    uint16_t* y = malloc(sizeof(uint16_t) * (size_t)(rows * D));
+    float* L = malloc(sizeof(float) * (size_t)rows);
+    HIP_OK(hipMemcpy(y, d_y, sizeof(uint16_t) * (size_t)(rows * D), hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(L, d_L, sizeof(float) * (size_t)rows, hipMemcpyDeviceToHost));
+    /* the first Tv tokens of each plane, gathered for the oracle */
+    const int64_t vrows = Tv * H;
+    uint16_t* ov = malloc(sizeof(uint16_t) * (size_t)(N * vrows * D));
+    float* lv = malloc(sizeof(float) * (size_t)(N * vrows));
+    for (int64_t n = 0; n < N; ++n) {
+        memcpy(ov + n * vrows * D, o + n * rows * D, sizeof(uint16_t) * (size_t)(vrows * D));
+        memcpy(lv + n * vrows, l + n * rows, sizeof(float) * (size_t)vrows);
+    }
+    double* y_ref = malloc(sizeof(double) * (size_t)(vrows * D));
+    double* L_ref = malloc(sizeof(double) * (size_t)vrows);
+    oracle_lse_combine(ov, LSEC_BF16, lv, N, Tv, H, D, 0, y_ref, L_ref);
+    int untouched = 1;
+    for (int64_t i = vrows * D; i < rows * D; ++i) untouched &= y[i] == 0xffff;
+    const unsigned char* Lb = (const unsigned char*)(L + vrows);
+    for (size_t i = 0; i < sizeof(float) * (size_t)(rows - vrows); ++i) untouched &= Lb[i] == 0xff;
+    check(st == LSEC_OK && untouched &&
+              close_enough(y, LSEC_BF16, y_ref, vrows * D, max_abs(ov, LSEC_BF16, N * vrows * D), L,
+                           L_ref, vrows),
+          "combine_planes_valid bf16 N=4 T=40 Tv=27 (count on device)");
+    HIP_OK(hipFree(d_o));
+    HIP_OK(hipFree(d_l));
+    HIP_OK(hipFree(d_q));
+    HIP_OK(hipFree(d_y));
+    HIP_OK(hipFree(d_L));
+    free(o), free(l), free(y), free(L), free(ov), free(lv), free(y_ref), free(L_ref);
+}
+
 static void error_cases(void) {
     void* d = NULL;
     HIP_OK(hipMalloc(&d, 4096));
@@ -247,6 +300,7 @@ int main(void) {
     combine_case("combine bf16 -> fp32 N=4 B=33 H=4 D=256 base e + LSE", 33, 4, 33, 4, 256,
                  LSEC_BF16, LSEC_BASE_E, 1);
     packed_case();
+    valid_count_case();
     error_cases();
     printf("c_abi_check: %s\n", failures ? "FAILED" : "ok");
     return failures ? 1 : 0;

@@ -32,7 +32,8 @@ def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ("lsec_combine", "lsec_merge", "lsec_pack_send", "lsec_unpack_combine",
               "lsec_unpack", "lsec_pack_dim", "lsec_status_string", "lsec_version",
-              "lsec_combine_planes", "lsec_correct_partial", "lsec_combine_path"):
+              "lsec_combine_planes", "lsec_combine_planes_valid", "lsec_correct_partial",
+              "lsec_combine_path"):
         assert n in names
 
 
@@ -205,6 +206,21 @@ def test_combine_planes_validation(lib):
     assert c(FAKE, 64, FAKE + 2, 8, 2, 2, 3, 8, 0, 0, FAKE, None, None) == 5
     assert c(None, 64, None, 8, 2, 0, 3, 8, 0, 0, None, None, None) == 0      # T = 0
     assert c(FAKE, 64, FAKE, 8, 0, 2, 3, 8, 0, 0, FAKE, None, None) == 2      # N < 1
+
+
+def test_combine_planes_valid_validation(lib):
+    c = lib.lsec_combine_planes_valid
+    # outputs, plane_stride, lses, lse_plane_stride, N, T, H, D, dtype, base,
+    # query_start_loc, num_reqs, out, out_lse, stream
+    assert c(FAKE, 64, FAKE, 8, 2, 2, 3, 8, 0, 0, None, 1, FAKE, None, None) == 1   # NULL offsets
+    assert c(FAKE, 64, FAKE, 8, 2, 2, 3, 8, 0, 0, FAKE + 2, 1, FAKE, None, None) == 5  # misaligned
+    assert c(FAKE, 64, FAKE, 8, 2, 2, 3, 8, 0, 0, FAKE, -1, FAKE, None, None) == 2  # num_reqs < 0
+    assert c(FAKE, 1 << 40, FAKE, 1 << 34, 2, 1, 1 << 32, 8, 0, 0, FAKE, 1, FAKE, None,
+             None) == 2                                                              # H >= 2^32
+    assert c(FAKE, 47, FAKE, 6, 2, 2, 3, 8, 0, 0, FAKE, 1, FAKE, None, None) == 2   # stride < plane
+    assert c(FAKE, 64, FAKE, 8, 2, 2, 3, 8, 9, 0, FAKE, 1, FAKE, None, None) == 4   # dtype
+    assert c(FAKE, 64, FAKE, 8, 2, 2, 3, 8, 0, 7, FAKE, 1, FAKE, None, None) == 6   # base
+    assert c(None, 64, None, 8, 2, 0, 3, 8, 0, 0, None, 1, None, None, None) == 0   # T = 0
 
 
 def test_header_and_c_consumer_compile_as_c99():

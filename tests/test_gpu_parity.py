@@ -458,6 +458,75 @@ def test_combine_planes_padded_stride(lsec):
                                  lview, T)
 
 
+# ---------------------------------------------------------------- valid-token count in device memory
+
+PLANES_VALID = [
+    # W, T (capacity), Tv (query_start_loc[-1]), H, D, dtype, base2, out_f32, path
+    (8, 16384, 10001, 32, 128, "bf16", False, False, "combine_tiled_kernel S=16"),  # 16 slots
+    (8, 4096, 2500, 16, 512, "bf16", True, False, "combine_tiled_kernel S=8"),     # a wave per row
+    (8, 4096, 3001, 16, 128, "bf16", False, False, "combine_tiled_kernel S=2"),    # mid-block
+    (8, 4096, 4096, 16, 128, "bf16", False, False, "combine_tiled_kernel S=2"),    # all valid
+    (8, 4096, 5000, 16, 128, "bf16", False, False, "combine_tiled_kernel S=2"),    # clamped to T
+    (8, 4096, 0, 16, 128, "bf16", False, False, "combine_tiled_kernel S=2"),       # all padding
+    (8, 4096, -3, 16, 128, "bf16", False, False, "combine_tiled_kernel S=2"),      # negative: none
+    (4, 777, 500, 8, 512, "f16", True, False, "combine_tiled_kernel S=1"),
+    (8, 2051, 1, 8, 128, "f32", False, False, "combine_tiled_kernel S=1"),         # one token
+    (8, 1024, 700, 8, 128, "bf16", False, True, "combine_tiled_kernel S=1"),       # fp32 result
+    (5, 300, 171, 4, 256, "bf16", True, False, "combine_tiled_kernel S=1"),        # N at run time
+    (1, 64, 40, 4, 128, "bf16", False, False, "combine_rows_kernel"),              # N = 1
+    (20, 40, 23, 4, 128, "bf16", True, False, "combine_rows_kernel"),              # N > 16
+    (2, 16, 9, 4, 12, "bf16", False, False, "combine_elems_kernel"),               # D % 8 != 0
+]
+
+
+def _offsets(tv: int, seed: int) -> np.ndarray:
+    """Cumulative token offsets of a few requests whose last entry is tv."""
+    rng = np.random.default_rng(seed)
+    if tv <= 0:
+        return np.array([0, tv], dtype=np.int32)
+    cuts = np.sort(rng.integers(0, tv + 1, size=min(tv, 6)))
+    return np.concatenate([[0], cuts, [tv]]).astype(np.int32)
+
+
+@pytest.mark.parametrize("W,T,Tv,H,D,dtype,base2,out_f32,path", PLANES_VALID)
+def test_combine_planes_valid_count_on_device(lsec, W, T, Tv, H, D, dtype, base2, out_f32, path):
+    """The count of valid tokens comes from query_start_loc[num_reqs] in
+    device memory: the first Tv tokens match the oracle, and the rows of the
+    padding tokens past Tv keep what the output held before (bit for bit)."""
+    _announce(f"combine_planes_valid W={W} T={T} Tv={Tv} H={H} D={D} {dtype} out_f32={out_f32}")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    assert lsec.lsec_combine_path(W, T, H, D, dtype=tdt) == path
+    o, l = synth.custom_inputs(W, T, H, D, dtype=dtype, seed=3 * T + D + W, special=SPECIALS)
+    rdt = torch.float32 if out_f32 else tdt
+    planes, lplanes = to_dev(o, dtype, DEV), f32_to_dev(l, DEV)
+    qsl = _offsets(Tv, seed=T + Tv)
+    out = torch.full((T, H, D), -7.0, dtype=rdt, device=DEV)
+    out_lse = torch.full((T, H), -7.0, device=DEV)
+    lsec.lsec_combine_planes(planes, lplanes, T, base_e=not base2, return_lse=True, out=out,
+                             out_lse=out_lse, out_dtype=rdt,
+                             query_start_loc=torch.from_numpy(qsl).to(DEV))
+    torch.cuda.synchronize()
+    y_ref, L_ref, tv = oracle.lse_combine_valid(o, l, qsl, dtype, base2)
+    assert tv == min(max(Tv, 0), T)
+    if tv:
+        oT = o[:, :tv]
+        assert_output_close(out[:tv], y_ref, "f32" if out_f32 else dtype, max_abs_input(oT, dtype))
+        assert_lse_close(out_lse[:tv], L_ref)
+    assert bool(torch.all(out[tv:] == -7.0)), "a padding token's output row was written"
+    assert bool(torch.all(out_lse[tv:] == -7.0)), "a padding token's LSE was written"
+
+
+def test_combine_planes_valid_rejects_bad_offsets(lsec):
+    o = torch.zeros((2, 4, 2, 128), dtype=torch.bfloat16, device=DEV)
+    l = torch.zeros((2, 4, 2), device=DEV)
+    for bad in (torch.tensor([0, 4], dtype=torch.int64, device=DEV),    # int64
+                torch.tensor([[0, 4]], dtype=torch.int32, device=DEV),  # 2-D
+                torch.zeros(0, dtype=torch.int32, device=DEV),          # empty
+                torch.tensor([0, 4], dtype=torch.int32)):               # host memory
+        with pytest.raises(ValueError):
+            lsec.lsec_combine_planes(o, l, 4, query_start_loc=bad)
+
+
 # ---------------------------------------------------------------- all-gather + reduce-scatter local step
 
 CORRECT = [

@@ -86,3 +86,47 @@ def test_pack_unpack_combine_and_combine_replayed_from_a_graph(lsec):
         # eager work between replays
         lsec.lsec_combine(planes, plane_lses)
         torch.cuda.synchronize()
+
+
+def test_valid_count_changes_between_replays_of_one_graph(lsec):
+    """A captured combine of receive planes padded to T tokens, replayed after
+    the step's query_start_loc changes in device memory (written by an eager
+    copy, outside the graph): each replay combines exactly the valid tokens and
+    leaves the padding rows as they were."""
+    print("[case] graph replay with a changing valid-token count", flush=True)
+    W, T, H, D = 8, 512, 16, 128
+    o, l = synth.custom_inputs(W, T, H, D, seed=73, special=((0.02, float("nan")),))
+    planes, lplanes = to_dev(o, "bf16", DEV), f32_to_dev(l, DEV)
+    qsl = torch.zeros(3, dtype=torch.int32, device=DEV)
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=DEV)
+    out_lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+
+    def step():
+        lsec.lsec_combine_planes(planes, lplanes, T, return_lse=True, out=out, out_lse=out_lse,
+                                 query_start_loc=qsl)
+
+    qsl.copy_(torch.tensor([0, 100, 200], dtype=torch.int32))
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    M = max_abs_input(o, "bf16")
+    for offsets in ([0, 300, 511], [0, 7, 9], [0, 0, 0], [0, 256, 512], [0, 400, 700]):
+        q = np.array(offsets, dtype=np.int32)
+        qsl.copy_(torch.from_numpy(q))
+        out.fill_(-7.0)
+        out_lse.fill_(-7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y_ref, L_ref, tv = oracle.lse_combine_valid(o, l, q, "bf16")
+        if tv:
+            assert_output_close(out[:tv], y_ref, "bf16", M, f"offsets {offsets}")
+            assert_lse_close(out_lse[:tv], L_ref, f"offsets {offsets}")
+        assert bool(torch.all(out[tv:] == -7.0)) and bool(torch.all(out_lse[tv:] == -7.0)), \
+            f"offsets {offsets}: a padding row was written"
