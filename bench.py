@@ -245,10 +245,13 @@ def build_workload(name: str, dev, out_f32: bool = False):
 
 # ---------------------------------------------------------------- timing
 
-def time_steps(kernels, steps, warmup, flush_bytes, dev):
+def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
+    """Time `steps` steps after `warmup`. With flush_bytes, a buffer of that
+    size is rewritten (or, with flush_read, summed) before each step, outside
+    the timed events, so the step's inputs come from HBM."""
     import torch
 
-    flush = torch.empty(max(flush_bytes // 4, 1), dtype=torch.float32, device=dev) \
+    flush = torch.ones(max(flush_bytes // 4, 1), dtype=torch.float32, device=dev) \
         if flush_bytes else None
     for i in range(warmup):
         for _, _, fn in kernels:
@@ -260,7 +263,10 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev):
     t0 = time.perf_counter()
     for i in range(steps):
         if flush is not None:
-            flush.fill_(float(i))
+            if flush_read:
+                flush.sum()
+            else:
+                flush.fill_(float(i))
         ev[i][0].record()
         for k, (_, _, fn) in enumerate(kernels):
             fn()
@@ -342,6 +348,9 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=-1,
                     help="cache flush before each step (default: 1024 MiB if the step's "
                          "working set is under 1 GiB, else none)")
+    ap.add_argument("--flush-read", action="store_true",
+                    help="flush by reading the buffer instead of rewriting it (leaves no "
+                         "dirty lines in the caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -370,8 +379,9 @@ def main():
     step_bytes = sum(b for _, b, _ in kernels)
     flush_mib = args.flush_mib if args.flush_mib >= 0 else (1024 if step_bytes < (1 << 30) else 0)
     log(f"[bench] {args.workload}: {step_bytes / 1e6:.1f} MB per step, warmup {args.warmup}, "
-        f"steps {args.steps}, flush {flush_mib} MiB")
-    wall, per_kernel_ms = time_steps(kernels, args.steps, args.warmup, flush_mib << 20, dev)
+        f"steps {args.steps}, flush {flush_mib} MiB{' (read)' if args.flush_read else ''}")
+    wall, per_kernel_ms = time_steps(kernels, args.steps, args.warmup, flush_mib << 20, dev,
+                                     args.flush_read)
     gpu_ms = sum(per_kernel_ms)
     ms_per_step = gpu_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -414,6 +424,7 @@ def main():
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "step_bytes": step_bytes, "cache_flush_mib": flush_mib,
+        "cache_flush_kind": ("read" if args.flush_read else "write") if flush_mib else "none",
         "wall_s": round(wall, 4), "kernels": kernel_detail,
         "roofline": roofline, "cpu_baseline": cpu,
     }

@@ -141,7 +141,10 @@ def test_python_binding_rejects_bad_tensors():
     ((16, 16384, 32, 128, 0, 0, 1), "combine_tiled_kernel S=16"),
     ((8, 4096, 16, 512, 0, 0, 1), "combine_tiled_kernel S=8"),
     ((4, 256, 32, 128, 0, 0, 1), "combine_tiled_kernel S=1"),
-    ((8, 2048, 8, 128, 0, 1, 1), "combine_tiled_kernel S=1"),
+    ((8, 2048, 8, 128, 0, 1, 1), "combine_tiled_kernel S=1"),    # packed
+    ((8, 2048, 8, 128, 256, 1, 1), "combine_tiled_kernel S=1"),  # packed, fp32 result
+    ((8, 2048, 8, 128, 2, 1, 1), "combine_tiled_kernel S=1"),    # fp32 packed rows
+    ((17, 2048, 8, 128, 0, 1, 1), "combine_rows_kernel"),        # packed, N > 16
     ((16, 16384, 32, 128, 0, 0, 0), "combine_elems_kernel"),   # buffers not 16-byte aligned
     ((1, 50, 3, 512, 0, 0, 1), "combine_rows_kernel"),          # N = 1
     ((32, 6, 4, 128, 0, 0, 1), "combine_rows_kernel"),          # N > 16

@@ -275,6 +275,31 @@ def test_tiled_unpack_combine_ragged(lsec, N, B, H, D, dtype, slots):
     assert_lse_close(L, L_ref)
 
 
+def test_unpack_combine_receive_buffer_off_16_byte_alignment(lsec):
+    """The same receive buffer 4 bytes past a 16-byte boundary (packed rows are
+    only 4-byte aligned anyway) gives the same results as an aligned one."""
+    N, B, H, D = 8, 64, 16, 128
+    _announce("unpack_combine, receive buffer 4 bytes off 16-byte alignment")
+    outs, lses = [], []
+    for r in range(N):
+        a, b = synth.custom_inputs(1, B, H, D, seed=760 + r, special=SPECIALS)
+        outs.append(a[0])
+        lses.append(b[0])
+    recv_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N) for r in range(N)])[1]
+    flat = torch.empty(recv_h.size + 8, dtype=torch.bfloat16, device=DEV)
+    shifted = flat[2:2 + recv_h.size].view(recv_h.shape)
+    shifted.copy_(to_dev(recv_h, "bf16", DEV))
+    assert shifted.data_ptr() % 16 == 4
+    y1, L1 = lsec.lsec_unpack_combine(shifted, return_lse=True)
+    y2, L2 = lsec.lsec_unpack_combine(to_dev(recv_h, "bf16", DEV), return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.unpack_combine(recv_h, D, "bf16")
+    oo, _ = oracle.unpack(recv_h, D)
+    for y, L in ((y1, L1), (y2, L2)):
+        assert_output_close(y, y_ref, "bf16", max_abs_input(oo, "bf16"))
+        assert_lse_close(L, L_ref)
+
+
 @pytest.mark.parametrize("N,B,H,D,dtype", [
     (4, 9, 8, 128, "bf16"), (2, 7, 6, 64, "f16"), (8, 3, 16, 512, "bf16"),
     (4, 5, 8, 6, "bf16"),    # general path: D % 8 != 0
