@@ -268,9 +268,11 @@ def lsec_combine_planes(outputs: torch.Tensor, lses: torch.Tensor, num_tokens: i
         _raise_on(st, "lsec_combine_planes")
     else:
         q = query_start_loc
-        if q.dtype != torch.int32 or q.dim() != 1 or q.numel() < 1 or q.device != dev:
-            raise ValueError("query_start_loc must be a 1-D int32 tensor of num_reqs + 1 "
-                             f"offsets on {dev}, got {q.dtype} {tuple(q.shape)} on {q.device}")
+        if (q.dtype != torch.int32 or q.dim() != 1 or q.numel() < 1 or q.device != dev
+                or not q.is_contiguous()):
+            raise ValueError("query_start_loc must be a contiguous 1-D int32 tensor of "
+                             f"num_reqs + 1 offsets on {dev}, got {q.dtype} {tuple(q.shape)} "
+                             f"stride {tuple(q.stride())} on {q.device}")
         st = lib.lsec_combine_planes_valid(_ptr(outputs), pstride, _ptr(lses), lstride, N, T, H, D,
                                            dt, base, _ptr(q), q.numel() - 1, _ptr(out),
                                            _ptr(out_lse) if return_lse else None,

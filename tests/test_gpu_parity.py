@@ -547,6 +547,7 @@ def test_combine_planes_valid_rejects_bad_offsets(lsec):
     for bad in (torch.tensor([0, 4], dtype=torch.int64, device=DEV),    # int64
                 torch.tensor([[0, 4]], dtype=torch.int32, device=DEV),  # 2-D
                 torch.zeros(0, dtype=torch.int32, device=DEV),          # empty
+                torch.arange(6, dtype=torch.int32, device=DEV)[::2],    # strided
                 torch.tensor([0, 4], dtype=torch.int32)):               # host memory
         with pytest.raises(ValueError):
             lsec.lsec_combine_planes(o, l, 4, query_start_loc=bad)
