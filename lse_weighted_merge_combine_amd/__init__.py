@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
 * ``lsec_unpack_combine(recv, ...)`` -- ``_dcp_a2a_unpack_combine``.
 * ``lsec_unpack(recv)`` -- the layout half of the receive step.
 * ``lsec_pack_dim(dtype)`` -- ``_dcp_a2a_lse_pack_dim``.
+* ``dcp_a2a_lse_reduce(out, lse, world_size, exchange)`` -- the page's
+  ``dcp_a2a_lse_reduce``: pack, the caller's all-to-all, unpack + combine.
 
 * ``lsec_merge(outputs, lses, token_dim)`` -- ``_merge_dcp_outputs_with_torch``
   of the page "vllm_ascend/attention/context_parallel/sfa_cp.py": the same
@@ -449,6 +451,39 @@ def lse_weighted_combine(outputs: torch.Tensor, lses: torch.Tensor, return_lse: 
                         out_dtype=torch.float32)
 
 
+def dcp_a2a_lse_reduce(cp_attn_out: torch.Tensor, cp_attn_lse: torch.Tensor, world_size: int,
+                       exchange=None, return_lse: bool = False, is_lse_base_on_e: bool = True,
+                       send: torch.Tensor | None = None, recv: torch.Tensor | None = None):
+    """The page's ``dcp_a2a_lse_reduce`` with the all-to-all left to the caller.
+
+    cp_attn_out [B,H,D] and cp_attn_lse [B,H] (fp32) are this rank's partial
+    attention over all H heads. They are packed into send [N,B,H/N,D+P]
+    (``lsec_pack_send``), ``exchange(send, recv)`` must fill recv so that
+    plane n holds what rank n packed for this rank (the chunk order of
+    ``all_to_all_single``; with torch.distributed:
+    ``lambda s, r: dist.all_to_all_single(r.view(-1), s.view(-1), group=g)``),
+    and recv is combined (``lsec_unpack_combine``) into this rank's [B,H/N,D]
+    heads (+ their [B,H/N] global LSE). As on the page, world_size 1 returns
+    the inputs unchanged and H must be divisible by world_size (ValueError).
+    ``send`` / ``recv`` may be preallocated buffers of the packed shape.
+    """
+    if world_size == 1:
+        return (cp_attn_out, cp_attn_lse) if return_lse else cp_attn_out
+    if cp_attn_out.dim() != 3:
+        raise ValueError(f"expected cp_attn_out [B,H,D], got {tuple(cp_attn_out.shape)}")
+    H = cp_attn_out.shape[1]
+    if world_size < 1 or H % world_size != 0:
+        raise ValueError(f"H={H} must be divisible by DCP world size {world_size}.")
+    if exchange is None:
+        raise ValueError("world_size > 1 needs an exchange(send, recv) function")
+    send = lsec_pack_send(cp_attn_out, cp_attn_lse, world_size, send=send)
+    if recv is None:
+        recv = torch.empty_like(send)
+    _check_out(recv, tuple(send.shape), send.dtype, send.device)
+    exchange(send, recv)
+    return lsec_unpack_combine(recv, base_e=is_lse_base_on_e, return_lse=return_lse)
+
+
 def lse_combine(outputs: torch.Tensor, lses: torch.Tensor, base_e: bool = True,
                 return_lse: bool = False):
     """The combine under its plain name: [N,B,H,D] + [N,B,H] -> [B,H,D] in the
@@ -479,6 +514,6 @@ def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
 __all__ = [
     "lsec_pack_dim", "lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
     "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
-    "lsec_combine_planes", "lse_combine", "pack_send", "unpack_combine",
+    "lsec_combine_planes", "lse_combine", "pack_send", "unpack_combine", "dcp_a2a_lse_reduce",
     "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
 ]

@@ -236,3 +236,21 @@ def test_header_and_c_consumer_compile_as_c99():
            "-I", "/opt/rocm/include", src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_dcp_a2a_lse_reduce_host_contract():
+    """The page's dcp_a2a_lse_reduce contract before any kernel runs: world
+    size 1 returns the inputs themselves, H % world_size != 0 raises
+    ValueError, and a multi-rank call needs an exchange."""
+    import torch
+
+    import lse_weighted_merge_combine_amd as lsec
+    out = torch.zeros((3, 8, 16), dtype=torch.bfloat16)
+    lse = torch.zeros((3, 8), dtype=torch.float32)
+    assert lsec.dcp_a2a_lse_reduce(out, lse, 1) is out
+    o2, l2 = lsec.dcp_a2a_lse_reduce(out, lse, 1, return_lse=True)
+    assert o2 is out and l2 is lse
+    with pytest.raises(ValueError, match="divisible"):
+        lsec.dcp_a2a_lse_reduce(out, lse, 3)
+    with pytest.raises(ValueError, match="exchange"):
+        lsec.dcp_a2a_lse_reduce(out, lse, 4)

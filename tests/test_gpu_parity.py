@@ -275,6 +275,39 @@ def test_tiled_unpack_combine_ragged(lsec, N, B, H, D, dtype, slots):
     assert_lse_close(L, L_ref)
 
 
+@pytest.mark.parametrize("N,base2", [(4, False), (8, True), (2, False)])
+def test_dcp_a2a_lse_reduce_simulated_ranks(lsec, N, base2):
+    """N ranks on one GPU: each rank's reduce packs its [B,H,D] partial, the
+    exchange copies plane `rank` of every rank's send buffer into its receive
+    buffer (the all-to-all's chunk order), and the combine returns the rank's
+    H/N heads; each rank matches the oracle's pack, exchange and combine."""
+    B, H, D = 33, 16, 128
+    _announce(f"dcp_a2a_lse_reduce N={N} base2={base2}")
+    outs, lses = [], []
+    for r in range(N):
+        a, b = synth.custom_inputs(1, B, H, D, seed=800 + 10 * N + r, special=SPECIALS)
+        outs.append(a[0])
+        lses.append(b[0])
+    dev_o = [to_dev(o, "bf16", DEV) for o in outs]
+    dev_l = [f32_to_dev(l, DEV) for l in lses]
+    sends = [lsec.lsec_pack_send(dev_o[r], dev_l[r], N) for r in range(N)]
+    recvs_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N) for r in range(N)])
+    for rank in range(N):
+        def exchange(send, recv, rank=rank):
+            assert torch.equal(send.view(torch.int16), sends[rank].view(torch.int16))
+            for n in range(N):
+                recv[n].copy_(sends[n][rank])
+
+        y, L = lsec.dcp_a2a_lse_reduce(dev_o[rank], dev_l[rank], N, exchange, return_lse=True,
+                                       is_lse_base_on_e=not base2)
+        torch.cuda.synchronize()
+        assert tuple(y.shape) == (B, H // N, D)
+        y_ref, L_ref = oracle.unpack_combine(recvs_h[rank], D, "bf16", base2)
+        oo, _ = oracle.unpack(recvs_h[rank], D)
+        assert_output_close(y, y_ref, "bf16", max_abs_input(oo, "bf16"), f"rank {rank}")
+        assert_lse_close(L, L_ref, f"rank {rank}")
+
+
 def test_unpack_combine_receive_buffer_off_16_byte_alignment(lsec):
     """The same receive buffer 4 bytes past a 16-byte boundary (packed rows are
     only 4-byte aligned anyway) gives the same results as an aligned one."""
