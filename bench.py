@@ -110,8 +110,11 @@ def load_traffic(workload: str, kernel: str):
 
 # ---------------------------------------------------------------- workloads
 
-def build_workload(name: str, dev, out_f32: bool = False):
-    """Inputs on the device, preallocated outputs and the step's kernels."""
+def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
+    """Inputs on the device, preallocated outputs and the step's kernels.
+    valid_tokens (direct_planes only): the count of valid tokens is read by the
+    kernels from a query_start_loc array in device memory; the other tokens of
+    the padded step are neither read nor written."""
     import numpy as np
     import torch
 
@@ -123,6 +126,8 @@ def build_workload(name: str, dev, out_f32: bool = False):
     s = 4 if w.dtype == "f32" else 2
     if out_f32 and w.kind not in ("combine", "correct"):
         raise SystemExit("--out-f32 applies to the combine and correct workloads only")
+    if valid_tokens is not None and w.kind != "planes":
+        raise SystemExit("--valid-tokens applies to the direct_planes workload only")
     odt = torch.float32 if out_f32 else tdt
     os_ = 4 if odt == torch.float32 else 2
 
@@ -164,17 +169,25 @@ def build_workload(name: str, dev, out_f32: bool = False):
         lbuf[:, :w.B] = torch.from_numpy(l).to(dev)
         out = torch.empty((w.B, w.H, w.D), dtype=tdt, device=dev)
         out_lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
-        nbytes = combine_bytes(w.N, w.B, w.H, w.D, s, True)
         kname = f"{lsec.lsec_combine_path(w.N, w.B, w.H, w.D, dtype=tdt)} ({w.dtype}, N={w.N}, " \
-                f"D={w.D}, {w.B} of {T_max} tokens per plane)"
+                f"D={w.D}, {w.B} of {T_max} tokens per plane"
+        if valid_tokens is None:
+            K, qsl = w.B, None
+            kname += ")"
+        else:  # the step is padded to B tokens; K of them are valid
+            K = min(max(int(valid_tokens), 0), w.B)
+            qsl = torch.tensor([0, K], dtype=torch.int32, device=dev)
+            kname += f", {K} valid by query_start_loc)"
+            info["valid_tokens"] = K
+        nbytes = combine_bytes(w.N, K, w.H, w.D, s, True) + (4 if qsl is not None else 0)
 
         def step():
             lsec.lsec_combine_planes(buf, lbuf, w.B, base_e=not w.base2, return_lse=True, out=out,
-                                     out_lse=out_lse)
+                                     out_lse=out_lse, query_start_loc=qsl)
 
         kernels = [(kname, nbytes, step)]
-        host = (o, l)
-        rows = w.B * w.H
+        host = (np.ascontiguousarray(o[:, :K]), np.ascontiguousarray(l[:, :K]))
+        rows = K * w.H
         info["T_max"] = T_max
     elif w.kind == "merge":
         o, l = synth.combine_inputs(w)
@@ -290,7 +303,9 @@ def cpu_baseline(w, host, threads: int):
     import oracle
 
     o, l = host
-    B = w.B
+    B = o.shape[1]  # the tokens timed on the GPU (fewer than w.B with --valid-tokens)
+    if B == 0:
+        return None
     threads = max(1, min(threads, B))
     bounds = np.linspace(0, B, threads + 1).astype(int)
     parts = [(np.ascontiguousarray(o[:, a:b]), np.ascontiguousarray(l[:, a:b]))
@@ -313,11 +328,11 @@ def cpu_baseline(w, host, threads: int):
     dt = time.perf_counter() - t0
     if errs:
         raise errs[0]
-    nbytes = combine_bytes(w.N, w.B, w.H, w.D, 4 if w.dtype == "f32" else 2, w.return_lse)
+    nbytes = combine_bytes(w.N, B, w.H, w.D, 4 if w.dtype == "f32" else 2, w.return_lse)
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
-            "rows_per_s": round(w.B * w.H / dt, 1),
-            "sample": f"the whole workload ({w.B * w.H} rows, N={w.N}, D={w.D}) through the fp64 "
+            "rows_per_s": round(B * w.H / dt, 1),
+            "sample": f"the whole workload ({B * w.H} rows, N={w.N}, D={w.D}) through the fp64 "
                       f"C oracle, token ranges split over {threads} threads"}
 
 
@@ -348,6 +363,9 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=-1,
                     help="cache flush before each step (default: 1024 MiB if the step's "
                          "working set is under 1 GiB, else none)")
+    ap.add_argument("--valid-tokens", type=int, default=None,
+                    help="direct_planes: combine only this many tokens, the count read by "
+                         "the kernels from query_start_loc in device memory")
     ap.add_argument("--flush-read", action="store_true",
                     help="flush by reading the buffer instead of rewriting it (leaves no "
                          "dirty lines in the caches)")
@@ -375,7 +393,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
 
-    w, info, kernels, host, rows = build_workload(args.workload, dev, args.out_f32)
+    w, info, kernels, host, rows = build_workload(args.workload, dev, args.out_f32,
+                                                  args.valid_tokens)
     step_bytes = sum(b for _, b, _ in kernels)
     flush_mib = args.flush_mib if args.flush_mib >= 0 else (1024 if step_bytes < (1 << 30) else 0)
     log(f"[bench] {args.workload}: {step_bytes / 1e6:.1f} MB per step, warmup {args.warmup}, "
@@ -405,8 +424,9 @@ def main():
     if not args.no_cpu_baseline and host is not None:
         log("[bench] timing the CPU oracle ...")
         cpu = cpu_baseline(w, host, args.cpu_threads)
-        cpu["cpu_model"] = cpu_info()
-        log(f"[bench] oracle {cpu['seconds']}s on {cpu['cores']} threads")
+        if cpu is not None:
+            cpu["cpu_model"] = cpu_info()
+            log(f"[bench] oracle {cpu['seconds']}s on {cpu['cores']} threads")
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)

@@ -97,6 +97,19 @@ def test_sweep_merge_and_planes(lsec, case):
                                             np.ascontiguousarray(l[:, :T]), dtype, base2)
         assert_output_close(y2, y2_ref, rdt, M, "planes")
         assert_lse_close(L2, L2_ref, "planes")
+    # the same planes with the valid count in device memory (capacity A)
+    Tv = (7 * i) % (A + 2) - 1  # -1 .. A
+    qsl = np.array([0, max(Tv, 0) // 2, Tv], dtype=np.int32)
+    y3 = torch.full((A, C, D), -3.0, dtype=TDT[rdt], device=DEV)
+    L3 = torch.full((A, C), -3.0, device=DEV)
+    lsec.lsec_combine_planes(buf, lbuf, A, base_e=not base2, return_lse=True, out=y3,
+                             out_lse=L3, out_dtype=odt, query_start_loc=torch.from_numpy(qsl).to(DEV))
+    torch.cuda.synchronize()
+    y3_ref, L3_ref, tv = oracle.lse_combine_valid(o, l, qsl, dtype, base2)
+    if tv:
+        assert_output_close(y3[:tv], y3_ref, rdt, M, "planes_valid")
+        assert_lse_close(L3[:tv], L3_ref, "planes_valid")
+    assert bool(torch.all(y3[tv:] == -3.0)) and bool(torch.all(L3[tv:] == -3.0)), "padding written"
 
 
 @pytest.mark.parametrize("case", _cases("packed", 40, 555), ids=lambda c: f"p{c[0]}")
