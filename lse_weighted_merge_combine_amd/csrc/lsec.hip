@@ -43,7 +43,12 @@ namespace {
 // Launch: a lane group of g = D / kEpc lanes owns a row; rows_per_block =
 // kBlock / g. Every lane loads the row's N LSE values itself (broadcasts
 // within the group) and issues all N chunk loads before it uses the first.
-template <int DT, int NT, bool PACKED>
+// SPLIT (an fp32 result from 16-bit partials): lane l owns elements
+// [4l, 4l + 4) and [D/2 + 4l, D/2 + 4l + 4), read as two 8-byte loads, so each
+// of its two 16-byte fp32 stores belongs to an instruction that writes one
+// contiguous half of the row (D is a multiple of 8 here, so D/2 keeps every
+// offset 8-byte aligned).
+template <int DT, int NT, bool PACKED, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     const typename Elem<DT>::T* __restrict__ src, const float* __restrict__ lse, int n_rt,
     uint32_t rows, FastDiv g, uint32_t rows_per_block, int64_t stride, int64_t plane,
@@ -58,16 +63,25 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
     rows = valid_rows(rows, om);
     if (row >= rows) return;
     const int N = NT > 0 ? NT : n_rt;
+    static_assert(!SPLIT || DT != LSEC_FP32, "fp32 partials already give fp32 results");
     const typename Elem<DT>::T* rp = src + int64_t(row) * stride;
-    const typename Elem<DT>::T* cp = rp + lane * E;
+    const typename Elem<DT>::T* cp = rp + lane * (SPLIT ? E / 2 : E);
 
     auto load_lse = [&](int n) -> float {
         if (PACKED) return ld_tail(rp + n * plane + D);
         return lse[int64_t(n) * lse_plane + row];
     };
     auto load_chunk = [&](int n) -> u32x4 {
-        if (PACKED) return ld16_a4(cp + n * plane);
-        return ld16(cp + n * plane);
+        if constexpr (SPLIT) {
+            const u32x2_a4 lo = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2_a4*>(cp + n * plane));
+            const u32x2_a4 hi = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2_a4*>(cp + n * plane + D / 2));
+            return u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+            if (PACKED) return ld16_a4(cp + n * plane);
+            return ld16(cp + n * plane);
+        }
     };
 
     float acc[E];
@@ -124,7 +138,13 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
         }
     }
     const uint32_t orow = out_row(row, om);
-    store_chunk<DT>(out, uint64_t(orow) * D + lane * E, acc, out_f32);
+    if constexpr (SPLIT) {
+        float* p = static_cast<float*>(out) + uint64_t(orow) * D + lane * 4;
+        st16(p, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
+        st16(p + D / 2, f32_chunk(acc[4], acc[5], acc[6], acc[7]));
+    } else {
+        store_chunk<DT>(out, uint64_t(orow) * D + lane * E, acc);
+    }
     if (out_lse != nullptr && lane == 0) out_lse[orow] = global_lse(s, m, inv_scale);
 }
 
@@ -242,7 +262,7 @@ __global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
                 st16(p, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
                 st16(p + D / 2, f32_chunk(acc[4], acc[5], acc[6], acc[7]));
             } else {
-                store_chunk<DT>(out, uint64_t(row[s]) * D + lane * E, acc, 0);
+                store_chunk<DT>(out, uint64_t(row[s]) * D + lane * E, acc);
             }
             if (out_lse != nullptr && lane == 0) out_lse[row[s]] = global_lse(sum, m, inv_scale);
         }
@@ -512,9 +532,18 @@ void launch_combine_rows(const void* src, const float* lse, int N, uint32_t rows
     const uint32_t rpb = kBlock / g;
     const unsigned blocks = (rows + rpb - 1) / rpb;
     const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
-    combine_rows_kernel<DT, NT, PACKED><<<blocks, kBlock, 0, st>>>(
-        static_cast<const typename Elem<DT>::T*>(src), lse, N, rows, make_fastdiv(g), rpb, stride,
-        pl.plane, pl.lse_plane, D, scale, inv_scale, out, out_f32, out_lse, om);
+    const auto* s = static_cast<const typename Elem<DT>::T*>(src);
+    if constexpr (DT != LSEC_FP32) {
+        if (out_f32) {
+            combine_rows_kernel<DT, NT, PACKED, true><<<blocks, kBlock, 0, st>>>(
+                s, lse, N, rows, make_fastdiv(g), rpb, stride, pl.plane, pl.lse_plane, D, scale,
+                inv_scale, out, out_f32, out_lse, om);
+            return;
+        }
+    }
+    combine_rows_kernel<DT, NT, PACKED, false><<<blocks, kBlock, 0, st>>>(
+        s, lse, N, rows, make_fastdiv(g), rpb, stride, pl.plane, pl.lse_plane, D, scale,
+        inv_scale, out, out_f32, out_lse, om);
 }
 
 template <int DT, bool PACKED>

@@ -206,30 +206,22 @@ __device__ __forceinline__ u32x4 f32_chunk(float a, float b, float c, float d) {
     return r;
 }
 
-// Store a lane's kEpc results at element `idx` of `out` (16-byte aligned): in
-// the input dtype, or as fp32 when `out_f32` (16-bit inputs then write two
-// 16-byte chunks). fp32 inputs always give fp32 results.
-// The two chunks of an fp32 result go out as two store instructions, each
-// covering every other 16 bytes of the wave's span, so every cache line is
-// written in two halves (non-temporal stores then write 17-18 % more than the
-// result holds; the default policy writes exactly the result but measured
-// slower). The tiled combine avoids this layout (split loads, below); the
-// row and element kernels keep it.
+// Store a lane's kEpc results at element `idx` of `out` (16-byte aligned) in
+// the input dtype (fp32 inputs: fp32). An fp32 result from 16-bit partials
+// does not come through here: those kernels read split halves of the row so
+// that each of a lane's two 16-byte fp32 stores belongs to an instruction
+// writing one contiguous half of the row (two stores covering every other 16
+// bytes of a wave's span had L2 write 17-18 % more than the result holds with
+// non-temporal stores, and ran slower with the default policy).
 template <int DT>
 __device__ __forceinline__ void store_chunk(void* out, uint64_t idx,
-                                            const float (&acc)[Elem<DT>::kEpc], int out_f32) {
+                                            const float (&acc)[Elem<DT>::kEpc]) {
     if constexpr (DT == LSEC_FP32) {
         st16(static_cast<float*>(out) + idx, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
     } else {
-        if (out_f32) {
-            float* p = static_cast<float*>(out) + idx;
-            st16(p, f32_chunk(acc[0], acc[1], acc[2], acc[3]));
-            st16(p + 4, f32_chunk(acc[4], acc[5], acc[6], acc[7]));
-        } else {
-            u32x4 r = {Elem<DT>::enc2(acc[0], acc[1]), Elem<DT>::enc2(acc[2], acc[3]),
-                       Elem<DT>::enc2(acc[4], acc[5]), Elem<DT>::enc2(acc[6], acc[7])};
-            st16(static_cast<uint16_t*>(out) + idx, r);
-        }
+        u32x4 r = {Elem<DT>::enc2(acc[0], acc[1]), Elem<DT>::enc2(acc[2], acc[3]),
+                   Elem<DT>::enc2(acc[4], acc[5]), Elem<DT>::enc2(acc[6], acc[7])};
+        st16(static_cast<uint16_t*>(out) + idx, r);
     }
 }
 

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
             st16(p, f32_chunk(acc[s][0], acc[s][1], acc[s][2], acc[s][3]));
             st16(p + D / 2, f32_chunk(acc[s][4], acc[s][5], acc[s][6], acc[s][7]));
         } else {
-            store_chunk<DT>(out, uint64_t(out_row(row[s], om)) * D + lane * E, acc[s], 0);
+            store_chunk<DT>(out, uint64_t(out_row(row[s], om)) * D + lane * E, acc[s]);
         }
     }
 }

@@ -113,6 +113,10 @@ OUT_F32 = [
     (3, 11, 7, 128, "f16", True, "combine_tiled_kernel S=1"),   # N at run time
     (20, 11, 7, 128, "f16", True, "combine_rows_kernel"),       # N > 16
     (9, 20, 2, 24, "bf16", False, "combine_rows_kernel"),
+    (1, 37, 5, 128, "bf16", False, "combine_rows_kernel"),      # N = 1
+    (5, 19, 3, 64, "f16", True, "combine_rows_kernel"),         # N at run time, D = 64
+    (16, 9, 4, 1024, "bf16", False, "combine_rows_kernel"),     # 128 lanes per row
+    (2, 5, 3, 2048, "bf16", True, "combine_rows_kernel"),       # 256 lanes per row
     (4, 10, 3, 1004, "bf16", True, "combine_elems_kernel"),
 ]
 
@@ -143,6 +147,42 @@ def test_fp32_result_is_the_unrounded_16bit_result(lsec):
     y32 = lsec.lsec_combine(og, lg, out_dtype=F32)
     torch.cuda.synchronize()
     assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), y16.view(torch.int16))
+
+
+@pytest.mark.parametrize("N,D", [(20, 128), (1, 64), (3, 24)])
+def test_row_kernel_fp32_result_rounds_to_its_16bit_result(lsec, N, D):
+    """The row kernel's fp32 result (split loads: a lane owns two quarter-rows)
+    rounded to bf16 equals its bf16 result bit for bit: each element is
+    accumulated over the planes in the same order either way."""
+    B, H = 33, 6
+    _announce(f"row kernel bf16 == round(f32) N={N} D={D}")
+    assert lsec.lsec_combine_path(N, B, H, D, out_dtype=F32) == "combine_rows_kernel"
+    o, l = _inputs(N, B, H, D, "bf16", 31 + N + D)
+    og, lg = to_dev(o, "bf16", DEV), f32_to_dev(l, DEV)
+    y16 = lsec.lsec_combine(og, lg)
+    y32 = lsec.lsec_combine(og, lg, out_dtype=F32)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), y16.view(torch.int16))
+
+
+@pytest.mark.parametrize("N,B,H,D", [(20, 9, 40, 128), (4, 7, 8, 64)])
+def test_row_kernel_unpack_combine_fp32_result(lsec, N, B, H, D):
+    """Packed rows (4-byte aligned) through the row kernel with an fp32 result."""
+    _announce(f"row kernel unpack_combine bf16 -> f32 N={N} B={B} H={H} D={D}")
+    assert lsec.lsec_combine_path(N, B, H // N, D, packed=True, out_dtype=F32) == \
+        "combine_rows_kernel"
+    outs, lses = [], []
+    for r in range(N):
+        a, b = _inputs(1, B, H, D, "bf16", 950 + r)
+        outs.append(a[0])
+        lses.append(b[0])
+    recv_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N) for r in range(N)])[0]
+    y, L = lsec.lsec_unpack_combine(to_dev(recv_h, "bf16", DEV), return_lse=True, out_dtype=F32)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.unpack_combine(recv_h, D, "bf16")
+    oo, _ = oracle.unpack(recv_h, D)
+    assert_output_close(y, y_ref, "f32", max_abs_input(oo, "bf16"))
+    assert_lse_close(L, L_ref)
 
 
 def test_page_alias_returns_promoted_fp32(lsec):
