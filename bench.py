@@ -29,6 +29,12 @@ already resident in HBM:
 result from 16-bit partials (the promoted dtype of the page's CPU combine)
 instead of a result in the input dtype.
 
+``--floor`` also times, under the same protocol, the library's two measurement
+aids (include/lsec_floor.h): a launch of one wave that does nothing, and for
+each kernel of the step a plain streaming read of as many bytes as that kernel
+moves. They bound what any kernel can reach on the same box, process and cache
+state.
+
 Workloads under 1 GiB are timed cold: a 1 GiB buffer is rewritten before each
 step, outside the timed events. Kernel time comes from HIP events recorded on
 the stream the kernels run on (torch's current stream). The JSON line also
@@ -77,12 +83,14 @@ def pack_bytes(N, B, H, D, s=2):
 
 def source_sha() -> str:
     """SHA-256 of the kernel sources' code (every csrc/*.hip and *.h, in name
-    order): comments, trailing blanks and empty lines removed, so that only a
-    change to the code (not to its comments) invalidates counters taken on it."""
+    order, except lsec_floor.hip: the measurement aids, which share no code
+    with the combining kernels): comments, trailing blanks and empty lines
+    removed, so that only a change to the code (not to its comments)
+    invalidates counters taken on it."""
     import re
     parts = []
     for name in sorted(os.listdir(KERNEL_DIR)):
-        if not name.endswith((".hip", ".h")):
+        if not name.endswith((".hip", ".h")) or name == "lsec_floor.hip":
             continue
         with open(os.path.join(KERNEL_DIR, name)) as f:
             text = f.read()
@@ -293,6 +301,36 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
     return wall, per_kernel_ms
 
 
+def time_floor(kernels, per_kernel_ms, steps, warmup, flush_bytes, dev, flush_read=False):
+    """Time the measurement aids under the protocol of the workload's steps:
+    an empty launch (one wave), and for each of the step's kernels a plain
+    streaming read of as many bytes as that kernel moves (rounded down to 16),
+    from a buffer of its own. Each kernel's time per launch is reported as a
+    multiple of its read's."""
+    import torch
+
+    import lse_weighted_merge_combine_amd as lsec
+
+    _, e_ms = time_steps([("empty", 0, lambda: lsec.lsec_floor_empty(dev))], steps, warmup,
+                         flush_bytes, dev, flush_read)
+    reads = []
+    for k, (name, nbytes, _) in enumerate(kernels):
+        nbytes -= nbytes % 16
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        sink = torch.empty(max(lsec.load_library().lsec_floor_read_blocks(nbytes), 1),
+                           dtype=torch.int32, device=dev)
+        _, r_ms = time_steps([("read", nbytes, lambda: lsec.lsec_floor_read(buf, sink))], steps,
+                             warmup, flush_bytes, dev, flush_read)
+        read_ms = r_ms[0] / steps
+        reads.append({"kernel": name, "bytes": nbytes, "read_us": round(read_ms * 1e3, 3),
+                      "read_GBps": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
+                      "kernel_over_read": round(per_kernel_ms[k] / steps / read_ms, 3)})
+        del buf, sink
+    return {"empty_launch_us": round(e_ms[0] / steps * 1e3, 3), "reads": reads,
+            "kernels": ["floor_empty_kernel", "floor_read_kernel"],
+            "timing": "HIP events, same flush protocol as the steps"}
+
+
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, host, threads: int):
@@ -369,6 +407,9 @@ def main():
     ap.add_argument("--flush-read", action="store_true",
                     help="flush by reading the buffer instead of rewriting it (leaves no "
                          "dirty lines in the caches)")
+    ap.add_argument("--floor", action="store_true",
+                    help="also time an empty launch and, per kernel, a plain read of its "
+                         "bytes (the floor any kernel is measured against)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -420,6 +461,14 @@ def main():
                       "GB/s": round(b / (per_kernel_ms[i] / args.steps * 1e-3) / 1e9, 1)}
                      for i, (n, b, _) in enumerate(kernels)]
 
+    floor = None
+    if args.floor:
+        floor = time_floor(kernels, per_kernel_ms, args.steps, args.warmup, flush_mib << 20,
+                           dev, args.flush_read)
+        log(f"[bench] floor: empty launch {floor['empty_launch_us']} us; " + "; ".join(
+            f"plain read of {r['bytes'] / 1e6:.1f} MB {r['read_us']} us ({r['read_GBps']} GB/s)"
+            for r in floor["reads"]))
+
     cpu = None
     if not args.no_cpu_baseline and host is not None:
         log("[bench] timing the CPU oracle ...")
@@ -448,6 +497,8 @@ def main():
         "wall_s": round(wall, 4), "kernels": kernel_detail,
         "roofline": roofline, "cpu_baseline": cpu,
     }
+    if floor is not None:
+        line["floor"] = floor
     print(json.dumps(line), flush=True)
 
 

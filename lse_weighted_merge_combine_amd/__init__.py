@@ -119,6 +119,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_correct_partial.argtypes = [P, I64, I64, P, I64, I64, I64, I, I, P, P, P]
     lib.lsec_combine_path.restype = ctypes.c_char_p
     lib.lsec_combine_path.argtypes = [I64, I64, I64, I64, I, I, I]
+    lib.lsec_floor_empty.restype = I
+    lib.lsec_floor_empty.argtypes = [P]
+    lib.lsec_floor_read_blocks.restype = I64
+    lib.lsec_floor_read_blocks.argtypes = [I64]
+    lib.lsec_floor_read.restype = I
+    lib.lsec_floor_read.argtypes = [P, I64, P, P]
     _lib = lib
     return lib
 
@@ -504,6 +510,38 @@ def unpack_combine(recv: torch.Tensor, D: int, base_e: bool = True, return_lse: 
     return lsec_unpack_combine(recv, base_e=base_e, return_lse=return_lse)
 
 
+# ---------------------------------------------------------------- measurement aids
+# (include/lsec_floor.h: not operations of the combine; the reference points
+# its kernels are timed against)
+
+def lsec_floor_empty(device=None, stream=None) -> None:
+    """Launch one wave that does nothing (the duration no launch goes below)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    _raise_on(load_library().lsec_floor_empty(_stream(dev, stream)), "lsec_floor_empty")
+
+
+def lsec_floor_read(src: torch.Tensor, sink: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Read every byte of ``src`` once with the combine's 16-byte non-temporal
+    loads (a plain streaming read). Returns the int32 ``sink``: one word per
+    16 KiB of ``src``, the XOR of its 32-bit words."""
+    lib = load_library()
+    dev = _check_dev(src)
+    nbytes = src.numel() * src.element_size()
+    words = lib.lsec_floor_read_blocks(nbytes)
+    if words < 0:
+        raise ValueError(f"src holds {nbytes} bytes: a multiple of 16 is required")
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=dev)
+    elif sink.dtype != torch.int32 or sink.numel() < words or sink.device != dev or \
+            not sink.is_contiguous():
+        raise ValueError(f"sink must be a contiguous int32 tensor of >= {words} words on {dev}")
+    _raise_on(lib.lsec_floor_read(_ptr(src), nbytes, _ptr(sink), _stream(dev, stream)),
+              "lsec_floor_read")
+    return sink
+
+
 def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or \
             not t.is_contiguous():
@@ -516,4 +554,5 @@ __all__ = [
     "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
     "lsec_combine_planes", "lse_combine", "pack_send", "unpack_combine", "dcp_a2a_lse_reduce",
     "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
+    "lsec_floor_empty", "lsec_floor_read",
 ]

@@ -20,10 +20,12 @@ def hipcc() -> str:
 
 
 # Translation units: the main one (row / element / corrected-partial / pack /
-# unpack kernels, the host code and the C ABI) and the tiled combine once per
-# element type (it holds most of the kernel instantiations). They compile in
+# unpack kernels, the host code and the C ABI), the measurement aids of
+# lsec_floor.h, and the tiled combine once per element type (it holds most of
+# the kernel instantiations). They compile in
 # parallel and link into one shared library.
-UNITS = [("lsec", os.path.join(PKG, "csrc", "lsec.hip"), [])] + [
+UNITS = [("lsec", os.path.join(PKG, "csrc", "lsec.hip"), []),
+         ("lsec_floor", os.path.join(PKG, "csrc", "lsec_floor.hip"), [])] + [
     (f"lsec_tiled_{name}", os.path.join(PKG, "csrc", "lsec_tiled.hip"), [f"-DLSEC_TILED_DT={dt}"])
     for name, dt in (("bf16", 0), ("fp16", 1), ("fp32", 2))
 ]

@@ -1,16 +1,20 @@
 """Host-side checks of the C ABI (no GPU needed, nothing is launched).
 
-The library must load, export every function ``include/lsec.h`` declares, and
-reject bad arguments with the documented status before touching the GPU.
+The library must load, export every function ``include/*.h`` declares (the
+combine's ABI in lsec.h, the measurement aids in lsec_floor.h), and reject bad
+arguments with the documented status before touching the GPU.
 """
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lsec.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -22,10 +26,12 @@ def lib():
     return lsec.load_library()
 
 
-def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lsec_[a-z_0-9]+)\s*\(", src)))
+def _declared(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(lsec_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_expected_entry_points():
@@ -34,12 +40,14 @@ def test_header_declares_expected_entry_points():
               "lsec_unpack", "lsec_pack_dim", "lsec_status_string", "lsec_version",
               "lsec_combine_planes", "lsec_combine_planes_valid", "lsec_correct_partial",
               "lsec_combine_path"):
+        assert n in _declared([HEADER])
+    for n in ("lsec_floor_empty", "lsec_floor_read", "lsec_floor_read_blocks"):
         assert n in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
-        assert hasattr(lib, name), f"{name} declared in lsec.h but not exported"
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
 
 
 def test_constants_match_header(lib):
@@ -229,7 +237,6 @@ def test_combine_planes_valid_validation(lib):
 def test_header_and_c_consumer_compile_as_c99():
     """include/lsec.h is a plain C header: the C consumer of the library
     compiles as C99 with warnings as errors (nothing is linked or run)."""
-    import subprocess
     src = os.path.join(ROOT, "tests", "c_abi", "c_abi_check.c")
     cmd = ["gcc", "-std=c99", "-fsyntax-only", "-Wall", "-Wextra", "-Werror",
            "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
@@ -254,3 +261,31 @@ def test_dcp_a2a_lse_reduce_host_contract():
         lsec.dcp_a2a_lse_reduce(out, lse, 3)
     with pytest.raises(ValueError, match="exchange"):
         lsec.dcp_a2a_lse_reduce(out, lse, 4)
+
+
+def test_floor_read_validation(lib):
+    """The measurement aids check their arguments before launching."""
+    assert lib.lsec_floor_read_blocks(0) == 0
+    assert lib.lsec_floor_read_blocks(16) == 1
+    assert lib.lsec_floor_read_blocks(16384) == 1
+    assert lib.lsec_floor_read_blocks(16400) == 2
+    assert lib.lsec_floor_read_blocks(-16) == -1
+    assert lib.lsec_floor_read_blocks(24) == -1
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.lsec_floor_read(fake, 24, fake, None) == 2       # SHAPE: not a multiple of 16
+    assert lib.lsec_floor_read(fake, -16, fake, None) == 2      # SHAPE
+    assert lib.lsec_floor_read(None, 0, None, None) == 0        # nothing to read, nothing launched
+    assert lib.lsec_floor_read(None, 32, fake, None) == 1       # NULL
+    assert lib.lsec_floor_read(fake, 32, None, None) == 1       # NULL
+    assert lib.lsec_floor_read(ctypes.c_void_p((1 << 20) + 4), 32, fake, None) == 5  # ALIGNMENT
+    assert lib.lsec_floor_read(fake, 32, ctypes.c_void_p((1 << 20) + 2), None) == 5  # ALIGNMENT
+
+
+def test_floor_header_compiles_as_c99(tmp_path):
+    src = tmp_path / "use_floor.c"
+    src.write_text('#include "lsec_floor.h"\n#include "lsec.h"\n'
+                   'int main(void) { return lsec_floor_read_blocks(16) == 1 ? 0 : 1; }\n')
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                          "-I", os.path.join(ROOT, "include"), str(src)],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr

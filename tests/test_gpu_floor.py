@@ -1,0 +1,65 @@
+"""The measurement aids of include/lsec_floor.h on the GPU: the plain read
+touches every byte once (its per-block XORs match numpy's), and the empty
+launch runs. They are not part of the combine; bench.py times the combining
+kernels against them."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+BLOCK_BYTES = 16384  # one sink word per 16 KiB of input
+
+
+@pytest.fixture(scope="module")
+def lsec():
+    import lse_weighted_merge_combine_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    m.load_library()
+    return m
+
+
+def _xor_words(a: np.ndarray) -> int:
+    return int(np.bitwise_xor.reduce(a.view(np.uint32))) if a.size else 0
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, BLOCK_BYTES, 3 * BLOCK_BYTES + 48,
+                                    (1 << 20) + 16 * 37, 64 << 20])
+def test_floor_read_touches_every_byte(lsec, nbytes):
+    print(f"[case] floor_read {nbytes} bytes", flush=True)
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).to(DEV)
+    sink = lsec.lsec_floor_read(src)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    nblk = -(-nbytes // BLOCK_BYTES)
+    assert got.size == nblk
+    for b in range(nblk):
+        want = _xor_words(host[b * BLOCK_BYTES // 4:(b + 1) * BLOCK_BYTES // 4])
+        assert int(got[b]) == want, f"block {b}"
+
+
+def test_floor_read_rejects_ragged_bytes(lsec):
+    with pytest.raises(ValueError):
+        lsec.lsec_floor_read(torch.zeros(3, dtype=torch.int32, device=DEV))
+
+
+def test_floor_read_empty_input(lsec):
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    lsec.lsec_floor_read(torch.zeros(0, dtype=torch.int32, device=DEV), sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7  # nothing launched, nothing written
+
+
+def test_floor_empty_launch(lsec):
+    s = torch.cuda.Stream(DEV)
+    for _ in range(3):
+        lsec.lsec_floor_empty(DEV)
+        lsec.lsec_floor_empty(DEV, stream=s)
+    torch.cuda.synchronize()
