@@ -116,6 +116,74 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def traffic_record(bench_log: str, fetch_dir: str, write_dir: str, commit: str) -> dict:
+    """Build profiles/traffic_<workload>.json from two rocprofv3 PMC runs of the
+    same bench command with --copy-calibration (FETCH_SIZE, then WRITE_SIZE,
+    in KiB per dispatch) and that command's JSON line. The counters are scaled
+    by what they read for the run's own 1 GiB device copies (the last three
+    __amd_rocclr_copyBuffer dispatches), and averaged over the dominant
+    kernel's dispatches (matched on the first word of its bench name)."""
+    import csv
+    import glob
+
+    with open(bench_log) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    workload = line["config"]["workload"] + \
+        ("_f32out" if line["config"].get("result_dtype") == "f32" else "")
+    kernel = line["roofline"]["kernel"]
+    symbol = kernel.split()[0]
+
+    def counters(d, symbol):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if len(files) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {d}, found {len(files)}")
+        with open(files[0]) as f:
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+        mine = [float(r["Counter_Value"]) for r in rows
+                if symbol + "<" in r["Kernel_Name"] or symbol + "(" in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")][-3:]
+        if not mine or len(copies) != 3:
+            raise SystemExit(f"{d}: {len(mine)} dispatches of {symbol}, {len(copies)} copies")
+        return mine, sum(copies) / 3
+
+    fetch, fetch_copy = counters(fetch_dir, symbol)
+    write, write_copy = counters(write_dir, symbol)
+    gib_kib = float(1 << 20)
+    ff, wf = fetch_copy / gib_kib, write_copy / gib_kib
+    f_kib, w_kib = sum(fetch) / len(fetch), sum(write) / len(write)
+    traffic = int(round((f_kib / ff + w_kib / wf) * 1024))
+    alg = line["roofline"]["bytes_per_launch"]
+    per_kernel = []
+    for k in line["kernels"]:
+        kf, _ = counters(fetch_dir, k["kernel"].split()[0])
+        kw, _ = counters(write_dir, k["kernel"].split()[0])
+        t = int(round((sum(kf) / len(kf) / ff + sum(kw) / len(kw) / wf) * 1024))
+        per_kernel.append({"kernel": k["kernel"], "traffic_bytes_per_launch": t,
+                           "algorithmic_bytes_per_launch": k["bytes"],
+                           "traffic_over_algorithmic": round(t / k["bytes"], 4)})
+    return {
+        "workload": workload, "kernel": kernel, "source_sha256": source_sha(),
+        "source_sha256_of": "every csrc/*.hip and *.h except lsec_floor.hip, in name order, "
+                            "with comments and blank lines removed (bench.source_sha)",
+        "counters_taken_at_commit": commit,
+        "fetch_size_kib_per_dispatch": f_kib, "write_size_kib_per_dispatch": w_kib,
+        "dispatches": min(len(fetch), len(write)),
+        "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                             "fetch_size_kib": fetch_copy, "write_size_kib": write_copy,
+                             "fetch_factor": ff, "write_factor": wf},
+        "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": round(traffic / alg, 4),
+        "per_kernel": per_kernel,
+        "commands": [
+            f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d "
+            f"<repo>/gpurun_out/pmc/{c}_{workload} -o pmc -- python3 <repo>/bench.py --workload "
+            f"{line['config']['workload']}{' --out-f32' if workload.endswith('_f32out') else ''} "
+            "--steps 3 --warmup 1 --no-cpu-baseline --copy-calibration"
+            for c in ("FETCH_SIZE", "WRITE_SIZE")],
+    }
+
+
 # ---------------------------------------------------------------- workloads
 
 def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
@@ -414,7 +482,21 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a 1 GiB device copy (PMC calibration)")
+    ap.add_argument("--traffic-record", nargs=3, metavar=("BENCH_LOG", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: write profiles/traffic_<workload>.json from a bench JSON line "
+                         "and the FETCH_SIZE / WRITE_SIZE PMC runs of the same command")
+    ap.add_argument("--commit", default="unknown",
+                    help="with --traffic-record: the commit the counters were taken on")
     args = ap.parse_args()
+
+    if args.traffic_record:
+        rec = traffic_record(*args.traffic_record, commit=args.commit)
+        path = os.path.join(ROOT, "profiles", f"traffic_{rec['workload']}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(f"{path}: {rec['traffic_over_algorithmic']} x the algorithmic bytes")
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
