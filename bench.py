@@ -29,11 +29,12 @@ already resident in HBM:
 result from 16-bit partials (the promoted dtype of the page's CPU combine)
 instead of a result in the input dtype.
 
-``--floor`` also times, under the same protocol, the library's two measurement
-aids (include/lsec_floor.h): a launch of one wave that does nothing, and for
-each kernel of the step a plain streaming read of as many bytes as that kernel
-moves. They bound what any kernel can reach on the same box, process and cache
-state.
+The library's two measurement aids (include/lsec_floor.h) are timed under the
+same protocol after the steps (``--no-floor`` skips them): a launch of one
+wave that does nothing, and for each kernel of the step a plain streaming read
+of as many bytes as that kernel moves. They bound what any kernel can reach on
+the same box, process and cache state, and appear in the JSON line as
+``floor``.
 
 Workloads under 1 GiB are timed cold: a 1 GiB buffer is rewritten before each
 step, outside the timed events. Kernel time comes from HIP events recorded on
@@ -475,9 +476,11 @@ def main():
     ap.add_argument("--flush-read", action="store_true",
                     help="flush by reading the buffer instead of rewriting it (leaves no "
                          "dirty lines in the caches)")
-    ap.add_argument("--floor", action="store_true",
+    ap.add_argument("--floor", dest="floor", action="store_true", default=True,
                     help="also time an empty launch and, per kernel, a plain read of its "
-                         "bytes (the floor any kernel is measured against)")
+                         "bytes (the floor any kernel is measured against; on by default)")
+    ap.add_argument("--no-floor", dest="floor", action="store_false",
+                    help="skip the floor measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--copy-calibration", action="store_true",
