@@ -29,10 +29,10 @@ already resident in HBM:
 result from 16-bit partials (the promoted dtype of the page's CPU combine)
 instead of a result in the input dtype.
 
-The library's two measurement aids (include/lsec_floor.h) are timed under the
+The library's measurement aids (include/lsec_floor.h) are timed under the
 same protocol after the steps (``--no-floor`` skips them): a launch of one
 wave that does nothing, and for each kernel of the step a plain streaming read
-of as many bytes as that kernel moves. They bound what any kernel can reach on
+of as many bytes as that kernel moves and a plain copy of half of them. They bound what any kernel can reach on
 the same box, process and cache state, and appear in the JSON line as
 ``floor``.
 
@@ -373,9 +373,11 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
 def time_floor(kernels, per_kernel_ms, steps, warmup, flush_bytes, dev, flush_read=False):
     """Time the measurement aids under the protocol of the workload's steps:
     an empty launch (one wave), and for each of the step's kernels a plain
-    streaming read of as many bytes as that kernel moves (rounded down to 16),
-    from a buffer of its own. Each kernel's time per launch is reported as a
-    multiple of its read's."""
+    streaming read of as many bytes as that kernel moves (rounded down to 16)
+    and a plain copy of half of them (as many bytes read as written), from
+    buffers of their own. Each kernel's time per launch is reported as a
+    multiple of both: the read bounds the combining kernels, the copy the pack
+    and the corrected partial."""
     import torch
 
     import lse_weighted_merge_combine_amd as lsec
@@ -390,13 +392,23 @@ def time_floor(kernels, per_kernel_ms, steps, warmup, flush_bytes, dev, flush_re
                            dtype=torch.int32, device=dev)
         _, r_ms = time_steps([("read", nbytes, lambda: lsec.lsec_floor_read(buf, sink))], steps,
                              warmup, flush_bytes, dev, flush_read)
-        read_ms = r_ms[0] / steps
+        del buf, sink
+        half = (nbytes // 2) - (nbytes // 2) % 16
+        csrc = torch.ones(half // 4, dtype=torch.int32, device=dev)
+        cdst = torch.empty_like(csrc)
+        _, c_ms = time_steps([("copy", 2 * half, lambda: lsec.lsec_floor_copy(csrc, cdst))],
+                             steps, warmup, flush_bytes, dev, flush_read)
+        del csrc, cdst
+        read_ms, copy_ms = r_ms[0] / steps, c_ms[0] / steps
+        kernel_ms_k = per_kernel_ms[k] / steps
         reads.append({"kernel": name, "bytes": nbytes, "read_us": round(read_ms * 1e3, 3),
                       "read_GBps": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
-                      "kernel_over_read": round(per_kernel_ms[k] / steps / read_ms, 3)})
-        del buf, sink
+                      "kernel_over_read": round(kernel_ms_k / read_ms, 3),
+                      "copy_us": round(copy_ms * 1e3, 3),
+                      "copy_GBps": round(2 * half / (copy_ms * 1e-3) / 1e9, 1),
+                      "kernel_over_copy": round(kernel_ms_k / copy_ms, 3)})
     return {"empty_launch_us": round(e_ms[0] / steps * 1e3, 3), "reads": reads,
-            "kernels": ["floor_empty_kernel", "floor_read_kernel"],
+            "kernels": ["floor_empty_kernel", "floor_read_kernel", "floor_copy_kernel"],
             "timing": "HIP events, same flush protocol as the steps"}
 
 

@@ -1,17 +1,21 @@
 /*
  * lsec_floor.h -- measurement aids of liblsec.so (gfx950). They are not
- * operations of the LSE-weighted combine: they give the two reference points
- * that the combining kernels are timed against on the same device, in the
+ * operations of the LSE-weighted combine: they give the reference points
+ * that the library's kernels are timed against on the same device, in the
  * same process and cache state:
  *  - lsec_floor_empty : a launch that does no work (one 64-lane wave), i.e.
  *                       the duration no kernel launch can go below;
  *  - lsec_floor_read  : a plain streaming read of a buffer with the same
  *                       16-byte non-temporal loads the combine uses, i.e. the
  *                       rate the device reaches for those bytes with no
- *                       arithmetic, no layout and (almost) no writes.
+ *                       arithmetic, no layout and (almost) no writes;
+ *  - lsec_floor_copy  : a plain copy with those loads and 16-byte
+ *                       non-temporal stores, the same for calls that write as
+ *                       much as they read (pack, unpack, corrected partial).
  * A combining call that moves b bytes cannot finish faster than a plain read
- * of b bytes, and no call finishes faster than an empty launch; for calls of
- * a few tens of MB the two are close to each other.
+ * of b bytes, a call that reads and writes b / 2 bytes each not faster than
+ * a plain copy of b / 2 bytes, and no call faster than an empty launch; for
+ * calls of a few tens of MB these are close to each other.
  *
  * Conventions are those of lsec.h: device pointers, the caller allocates,
  * work is enqueued on `stream` (NULL = the null stream), arguments are checked
@@ -54,6 +58,18 @@ int64_t lsec_floor_read_blocks(int64_t bytes);
  * (src not 16-byte aligned, sink not 4-byte aligned), LAUNCH.
  */
 int lsec_floor_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * lsec_floor_copy -- copy `bytes` bytes from `src` to `dst` once.
+ *   src, dst : bytes / 16 chunks of 16 bytes each, 16-byte aligned (device
+ *              memory); the two must not overlap
+ *   bytes    : >= 0, a multiple of 16
+ * A lane keeps four 16-byte loads in flight, then stores them; a 256-lane
+ * block copies one contiguous 16 KiB run.
+ * Errors: SHAPE (bytes negative or not a multiple of 16), NULL, ALIGNMENT
+ * (src or dst not 16-byte aligned), LAUNCH.
+ */
+int lsec_floor_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

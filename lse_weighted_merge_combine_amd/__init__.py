@@ -125,6 +125,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_floor_read_blocks.argtypes = [I64]
     lib.lsec_floor_read.restype = I
     lib.lsec_floor_read.argtypes = [P, I64, P, P]
+    lib.lsec_floor_copy.restype = I
+    lib.lsec_floor_copy.argtypes = [P, P, I64, P]
     _lib = lib
     return lib
 
@@ -542,6 +544,19 @@ def lsec_floor_read(src: torch.Tensor, sink: torch.Tensor | None = None,
     return sink
 
 
+def lsec_floor_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Copy every byte of ``src`` into ``dst`` (same byte size, no overlap) once,
+    with the combine's 16-byte non-temporal loads and stores (a plain copy)."""
+    dev = _check_dev(src, dst)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must hold the same number of bytes")
+    if nbytes % 16:
+        raise ValueError(f"src holds {nbytes} bytes: a multiple of 16 is required")
+    _raise_on(load_library().lsec_floor_copy(_ptr(src), _ptr(dst), nbytes, _stream(dev, stream)),
+              "lsec_floor_copy")
+
+
 def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or \
             not t.is_contiguous():
@@ -554,5 +569,5 @@ __all__ = [
     "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
     "lsec_combine_planes", "lse_combine", "pack_send", "unpack_combine", "dcp_a2a_lse_reduce",
     "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
-    "lsec_floor_empty", "lsec_floor_read",
+    "lsec_floor_empty", "lsec_floor_read", "lsec_floor_copy",
 ]

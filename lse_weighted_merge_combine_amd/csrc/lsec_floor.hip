@@ -1,6 +1,6 @@
 // lsec_floor.hip -- measurement aids of liblsec.so (include/lsec_floor.h): an
-// empty launch and a plain streaming read, the reference points the
-// combining kernels are timed against. Not part of the combine.
+// empty launch, a plain streaming read and a plain copy, the reference points
+// the library's kernels are timed against. Not part of the combine.
 //
 // Build with -Xclang -target-feature -Xclang -packed-fp32-ops (as every unit
 // of the library).
@@ -46,6 +46,25 @@ __global__ __launch_bounds__(kBlock) void floor_read_kernel(const u32x4* __restr
     }
 }
 
+// Block b copies chunks [b * 1024, (b + 1) * 1024) (the last block stops at
+// n16); lane t moves chunks b * 1024 + t + 256 k, k < 4, all four loads issued
+// before the first store.
+__global__ __launch_bounds__(kBlock) void floor_copy_kernel(const u32x4* __restrict__ src,
+                                                            u32x4* __restrict__ dst, uint64_t n16) {
+    const uint64_t base = uint64_t(blockIdx.x) * kFloorChunksPerBlock + threadIdx.x;
+    u32x4 v[kFloorLoads];
+#pragma unroll
+    for (int k = 0; k < kFloorLoads; ++k) {
+        const uint64_t i = base + uint64_t(k) * kBlock;
+        v[k] = i < n16 ? ld16(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kFloorLoads; ++k) {
+        const uint64_t i = base + uint64_t(k) * kBlock;
+        if (i < n16) st16(dst + i, v[k]);
+    }
+}
+
 }  // namespace
 }  // namespace lsec_detail
 
@@ -75,6 +94,19 @@ int lsec_floor_read(const void* src, int64_t bytes, uint32_t* sink, void* stream
     (void)hipGetLastError();
     floor_read_kernel<<<unsigned(blocks), kBlock, 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<const u32x4*>(src), uint64_t(bytes) / 16, sink);
+    return hipGetLastError() == hipSuccess ? LSEC_OK : LSEC_ERR_LAUNCH;
+}
+
+int lsec_floor_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    const int64_t blocks = lsec_floor_read_blocks(bytes);
+    if (blocks < 0 || blocks > int64_t(UINT32_MAX)) return LSEC_ERR_SHAPE;
+    if (blocks == 0) return LSEC_OK;
+    if (!src || !dst) return LSEC_ERR_NULL;
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0)
+        return LSEC_ERR_ALIGNMENT;
+    (void)hipGetLastError();
+    floor_copy_kernel<<<unsigned(blocks), kBlock, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), uint64_t(bytes) / 16);
     return hipGetLastError() == hipSuccess ? LSEC_OK : LSEC_ERR_LAUNCH;
 }
 

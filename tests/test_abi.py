@@ -41,7 +41,7 @@ def test_header_declares_expected_entry_points():
               "lsec_combine_planes", "lsec_combine_planes_valid", "lsec_correct_partial",
               "lsec_combine_path"):
         assert n in _declared([HEADER])
-    for n in ("lsec_floor_empty", "lsec_floor_read", "lsec_floor_read_blocks"):
+    for n in ("lsec_floor_empty", "lsec_floor_read", "lsec_floor_read_blocks", "lsec_floor_copy"):
         assert n in names
 
 
@@ -279,6 +279,12 @@ def test_floor_read_validation(lib):
     assert lib.lsec_floor_read(fake, 32, None, None) == 1       # NULL
     assert lib.lsec_floor_read(ctypes.c_void_p((1 << 20) + 4), 32, fake, None) == 5  # ALIGNMENT
     assert lib.lsec_floor_read(fake, 32, ctypes.c_void_p((1 << 20) + 2), None) == 5  # ALIGNMENT
+    other = ctypes.c_void_p(1 << 21)
+    assert lib.lsec_floor_copy(fake, other, 24, None) == 2      # SHAPE
+    assert lib.lsec_floor_copy(None, None, 0, None) == 0        # nothing to copy
+    assert lib.lsec_floor_copy(None, other, 32, None) == 1      # NULL
+    assert lib.lsec_floor_copy(fake, None, 32, None) == 1       # NULL
+    assert lib.lsec_floor_copy(fake, ctypes.c_void_p((1 << 21) + 8), 32, None) == 5  # ALIGNMENT
 
 
 def test_floor_header_compiles_as_c99(tmp_path):

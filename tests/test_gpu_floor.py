@@ -1,5 +1,6 @@
 """The measurement aids of include/lsec_floor.h on the GPU: the plain read
-touches every byte once (its per-block XORs match numpy's), and the empty
+touches every byte once (its per-block XORs match numpy's), the plain copy
+reproduces its source bit for bit and writes nothing past it, and the empty
 launch runs. They are not part of the combine; bench.py times the combining
 kernels against them."""
 import os
@@ -63,3 +64,26 @@ def test_floor_empty_launch(lsec):
         lsec.lsec_floor_empty(DEV)
         lsec.lsec_floor_empty(DEV, stream=s)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 3 * BLOCK_BYTES + 48, (1 << 20) + 16 * 37])
+def test_floor_copy_is_exact(lsec, nbytes):
+    print(f"[case] floor_copy {nbytes} bytes", flush=True)
+    rng = np.random.default_rng(nbytes + 1)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).to(DEV)
+    guard = torch.full((nbytes // 4 + 64,), -7, dtype=torch.int32, device=DEV)
+    dst = guard[:nbytes // 4]
+    lsec.lsec_floor_copy(src, dst)
+    torch.cuda.synchronize()
+    got = guard.cpu().numpy()
+    assert np.array_equal(got[:nbytes // 4].view(np.uint32), host)
+    assert np.all(got[nbytes // 4:] == -7)  # nothing written past the end
+
+
+def test_floor_copy_rejects_bad_sizes(lsec):
+    a = torch.zeros(8, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        lsec.lsec_floor_copy(a, torch.zeros(4, dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError):
+        lsec.lsec_floor_copy(a[:3], torch.zeros(3, dtype=torch.int32, device=DEV))
