@@ -563,8 +563,8 @@ def main():
         floor = time_floor(kernels, per_kernel_ms, args.steps, args.warmup, flush_mib << 20,
                            dev, args.flush_read)
         log(f"[bench] floor: empty launch {floor['empty_launch_us']} us; " + "; ".join(
-            f"plain read of {r['bytes'] / 1e6:.1f} MB {r['read_us']} us ({r['read_GBps']} GB/s)"
-            for r in floor["reads"]))
+            f"plain read of {r['bytes'] / 1e6:.1f} MB {r['read_us']} us ({r['read_GBps']} GB/s), "
+            f"copy of half {r['copy_us']} us ({r['copy_GBps']} GB/s)" for r in floor["reads"]))
 
     cpu = None
     if not args.no_cpu_baseline and host is not None:
