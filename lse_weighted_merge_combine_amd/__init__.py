@@ -18,7 +18,8 @@ Entry points (same names as the C ABI):
 * ``lsec_unpack(recv)`` -- the layout half of the receive step.
 * ``lsec_pack_dim(dtype)`` -- ``_dcp_a2a_lse_pack_dim``.
 * ``dcp_a2a_lse_reduce(out, lse, world_size, exchange)`` -- the page's
-  ``dcp_a2a_lse_reduce``: pack, the caller's all-to-all, unpack + combine.
+  ``dcp_a2a_lse_reduce``: pack, the caller's all-to-all, unpack + combine;
+  ``dcp_a2a_send_recv_buffers(shape, device, dtype)`` keeps its buffers.
 
 * ``lsec_merge(outputs, lses, token_dim)`` -- ``_merge_dcp_outputs_with_torch``
   of the page "vllm_ascend/attention/context_parallel/sfa_cp.py": the same
@@ -459,6 +460,33 @@ def lse_weighted_combine(outputs: torch.Tensor, lses: torch.Tensor, return_lse: 
                         out_dtype=torch.float32)
 
 
+_A2A_BUFFERS: dict = {}
+
+
+def dcp_a2a_send_recv_buffers(shape, device, dtype: torch.dtype):
+    """Send and receive buffers of one packed shape [N, B, H/N, D + P] for the
+    exchange (the page's ``_dcp_a2a_send_recv_buffers``, whose body is not
+    shown). They are kept per (shape, device, dtype), so that repeated steps,
+    and a captured HIP graph, reuse the same memory: pass them to
+    ``dcp_a2a_lse_reduce(..., send=, recv=)``. Calls that overlap in time (on
+    different streams) must not share them."""
+    shape = tuple(int(x) for x in shape)
+    if len(shape) != 4 or any(x < 0 for x in shape):
+        raise ValueError(f"expected a packed shape [N, B, H/N, D + P], got {shape}")
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}: bfloat16, float16 or float32 only")
+    device = torch.device(device)
+    if device.type == "cuda" and device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    key = (shape, device, dtype)
+    bufs = _A2A_BUFFERS.get(key)
+    if bufs is None:
+        bufs = (torch.empty(shape, dtype=dtype, device=device),
+                torch.empty(shape, dtype=dtype, device=device))
+        _A2A_BUFFERS[key] = bufs
+    return bufs
+
+
 def dcp_a2a_lse_reduce(cp_attn_out: torch.Tensor, cp_attn_lse: torch.Tensor, world_size: int,
                        exchange=None, return_lse: bool = False, is_lse_base_on_e: bool = True,
                        send: torch.Tensor | None = None, recv: torch.Tensor | None = None):
@@ -569,5 +597,5 @@ __all__ = [
     "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
     "lsec_combine_planes", "lse_combine", "pack_send", "unpack_combine", "dcp_a2a_lse_reduce",
     "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
-    "lsec_floor_empty", "lsec_floor_read", "lsec_floor_copy",
+    "lsec_floor_empty", "lsec_floor_read", "lsec_floor_copy", "dcp_a2a_send_recv_buffers",
 ]

@@ -263,6 +263,27 @@ def test_dcp_a2a_lse_reduce_host_contract():
         lsec.dcp_a2a_lse_reduce(out, lse, 4)
 
 
+def test_send_recv_buffers_are_kept_per_shape():
+    """dcp_a2a_send_recv_buffers hands out one send and one receive buffer
+    per (shape, device, dtype) and the same ones on every later call."""
+    import torch
+
+    import lse_weighted_merge_combine_amd as lsec
+    s1, r1 = lsec.dcp_a2a_send_recv_buffers((4, 3, 2, 130), "cpu", torch.bfloat16)
+    assert tuple(s1.shape) == (4, 3, 2, 130) and s1.dtype == torch.bfloat16
+    assert s1.data_ptr() != r1.data_ptr()
+    s2, r2 = lsec.dcp_a2a_send_recv_buffers([4, 3, 2, 130], torch.device("cpu"), torch.bfloat16)
+    assert s2 is s1 and r2 is r1
+    s3, _ = lsec.dcp_a2a_send_recv_buffers((4, 3, 2, 130), "cpu", torch.float16)
+    assert s3 is not s1
+    s4, _ = lsec.dcp_a2a_send_recv_buffers((4, 3, 4, 130), "cpu", torch.bfloat16)
+    assert s4 is not s1
+    with pytest.raises(ValueError):
+        lsec.dcp_a2a_send_recv_buffers((4, 3, 130), "cpu", torch.bfloat16)
+    with pytest.raises(ValueError):
+        lsec.dcp_a2a_send_recv_buffers((4, 3, 2, 130), "cpu", torch.int8)
+
+
 def test_floor_read_validation(lib):
     """The measurement aids check their arguments before launching."""
     assert lib.lsec_floor_read_blocks(0) == 0

@@ -308,6 +308,33 @@ def test_dcp_a2a_lse_reduce_simulated_ranks(lsec, N, base2):
         assert_lse_close(L, L_ref, f"rank {rank}")
 
 
+def test_dcp_a2a_lse_reduce_on_kept_buffers(lsec):
+    """The same reduce through the kept send / receive buffers of
+    dcp_a2a_send_recv_buffers, twice in a row: bit for bit the result of
+    freshly allocated buffers, and the buffers are the same memory both times."""
+    N, B, H, D = 4, 21, 16, 128
+    _announce(f"dcp_a2a_lse_reduce kept buffers N={N}")
+    a, b = synth.custom_inputs(1, B, H, D, seed=871, special=SPECIALS)
+    o, l = to_dev(a[0], "bf16", DEV), f32_to_dev(b[0], DEV)
+
+    def exchange(send, recv):  # every rank sends what this rank sent (a stand-in)
+        for n in range(N):
+            recv[n].copy_(send[n])
+
+    y0, L0 = lsec.dcp_a2a_lse_reduce(o, l, N, exchange, return_lse=True)
+    shape = (N, B, H // N, D + lsec.lsec_pack_dim(torch.bfloat16))
+    ptrs = None
+    for _ in range(2):
+        send, recv = lsec.dcp_a2a_send_recv_buffers(shape, DEV, torch.bfloat16)
+        y, L = lsec.dcp_a2a_lse_reduce(o, l, N, exchange, return_lse=True, send=send, recv=recv)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+        assert torch.equal(L.view(torch.int32), L0.view(torch.int32))
+        if ptrs is not None:
+            assert (send.data_ptr(), recv.data_ptr()) == ptrs
+        ptrs = (send.data_ptr(), recv.data_ptr())
+
+
 def test_unpack_combine_receive_buffer_off_16_byte_alignment(lsec):
     """The same receive buffer 4 bytes past a 16-byte boundary (packed rows are
     only 4-byte aligned anyway) gives the same results as an aligned one."""
