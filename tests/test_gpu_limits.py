@@ -2,7 +2,9 @@
 
 The tiled combine addresses a lane's chunk by a 32-bit byte offset inside its
 plane, so it serves planes below 4 GiB; larger planes take the row kernel,
-which uses 64-bit offsets. These tests run a plane just below and just above
+which uses 64-bit offsets. The row kernel counts rows in 32 bits, so 2^31
+rows and more take the element-wise kernel (64-bit throughout); the last test
+runs just below and just above that line. These tests run a plane just below and just above
 4 GiB (8.6 GB of partial outputs each) and check sampled token ranges at the
 start, the middle and the very end of the planes against the oracle (rows are
 independent, so the oracle's result on a token slice of the inputs is exactly
@@ -106,4 +108,37 @@ def test_unpack_combine_around_4gib_planes(lsec, B, path):
         assert_output_close(y[s:e], y_ref, "bf16", max_abs_input(oo, "bf16"), f"tokens {s}:{e}")
         assert_lse_close(L[s:e], L_ref, f"tokens {s}:{e}")
     del recv, y, L
+    _release()
+
+
+@pytest.mark.parametrize("rows,path", [
+    (2**31 - 4096, "combine_rows_kernel"),
+    (2**31 + 4096, "combine_elems_kernel"),
+])
+def test_combine_around_2g_rows(lsec, rows, path):
+    """N=2 planes of `rows` rows of D=8 bf16 (68.7 GB of partial outputs, about
+    129 GB with LSEs and results). The inputs repeat one seeded 4096-row block
+    (tiled on the device), so every row's oracle result is that of its row in
+    the block; rows are checked at the start, across 2^31 and at the end."""
+    N, D, K = 2, 8, 4096
+    _announce(f"combine N={N} rows={rows} D={D} bf16 ({path})")
+    assert lsec.lsec_combine_path(N, rows, 1, D) == path
+    o, l = synth.custom_inputs(N, K, 1, D, seed=2031, lse_dist=("uniform", -10.0, 30.0),
+                               special=SPECIALS)
+    y_ref, L_ref = oracle.lse_combine(o, l, "bf16")
+    M = max_abs_input(o, "bf16")
+    og = torch.empty((N, rows, 1, D), dtype=torch.bfloat16, device=DEV)
+    lg = torch.empty((N, rows, 1), dtype=torch.float32, device=DEV)
+    og.view(N, rows // K, K, D).copy_(to_dev(o, "bf16", DEV).view(N, 1, K, D).expand(N, rows // K, K, D))
+    lg.view(N, rows // K, K).copy_(f32_to_dev(l, DEV).view(N, 1, K).expand(N, rows // K, K))
+    y, L = lsec.lsec_combine(og, lg, base_e=True, return_lse=True)
+    torch.cuda.synchronize()
+    del og, lg
+    _release()
+    for s in (0, 2**31 - K, 2**31, rows - K):
+        if s + K > rows:
+            continue
+        assert_output_close(y[s:s + K], y_ref, "bf16", M, f"rows {s}:{s + K}")
+        assert_lse_close(L[s:s + K], L_ref, f"rows {s}:{s + K}")
+    del y, L
     _release()
