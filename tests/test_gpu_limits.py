@@ -2,9 +2,9 @@
 
 The tiled combine addresses a lane's chunk by a 32-bit byte offset inside its
 plane, so it serves planes below 4 GiB; larger planes take the row kernel,
-which uses 64-bit offsets. The row kernel counts rows in 32 bits, so 2^31
-rows and more take the element-wise kernel (64-bit throughout); the last test
-runs just below and just above that line. These tests run a plane just below and just above
+which uses 64-bit offsets. The row kernels (combine, pack, unpack) count rows
+in 32 bits, so 2^31 rows and more take the element-wise kernels (64-bit
+throughout); the last tests run each call just below and just above that line. These tests run a plane just below and just above
 4 GiB (8.6 GB of partial outputs each) and check sampled token ranges at the
 start, the middle and the very end of the planes against the oracle (rows are
 independent, so the oracle's result on a token slice of the inputs is exactly
@@ -140,5 +140,75 @@ def test_combine_around_2g_rows(lsec, rows, path):
             continue
         assert_output_close(y[s:s + K], y_ref, "bf16", M, f"rows {s}:{s + K}")
         assert_lse_close(L[s:s + K], L_ref, f"rows {s}:{s + K}")
+    del y, L
+    _release()
+
+
+@pytest.mark.parametrize("B", [2**30 - 4096, 2**30 + 4096])
+def test_pack_and_unpack_around_2g_rows(lsec, B):
+    """pack_send of [B, H=2, D=8] bf16 (2 * B rows: 2^31 -+ 8192, fast kernel
+    below, element kernel above) and lsec_unpack of the result (N * B * Hl rows,
+    the same count), bit for bit. The input repeats one seeded 4096-token
+    block, so the send planes repeat the oracle's pack of that block."""
+    N, H, D, K = 2, 2, 8, 4096
+    _announce(f"pack_send + unpack N={N} B={B} H={H} D={D} bf16 ({B * H} rows)")
+    o, l = synth.custom_inputs(1, K, H, D, seed=2032, special=SPECIALS)
+    send_ref = oracle.pack_send(o[0], l[0], N)                # [N, K, 1, D + 2]
+    og = torch.empty((B, H, D), dtype=torch.bfloat16, device=DEV)
+    lg = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    og.view(B // K, K, H, D).copy_(to_dev(o[0], "bf16", DEV).view(1, K, H, D).expand(B // K, K, H, D))
+    lg.view(B // K, K, H).copy_(f32_to_dev(l[0], DEV).view(1, K, H).expand(B // K, K, H))
+    send = lsec.lsec_pack_send(og, lg, N)
+    torch.cuda.synchronize()
+    del og, lg
+    _release()
+    starts = [s for s in (0, 2**30 - K, 2**30, B - K) if s + K <= B]
+    for s in starts:
+        got = send[:, s:s + K].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, send_ref), f"send tokens {s}:{s + K}"
+    outs, lses = lsec.lsec_unpack(send)
+    torch.cuda.synchronize()
+    del send
+    _release()
+    for s in starts:
+        got_o = outs[:, s:s + K].view(torch.int16).cpu().numpy().view(np.uint16)
+        got_l = lses[:, s:s + K].view(torch.int32).cpu().numpy().view(np.uint32)
+        assert np.array_equal(got_o, o[0].transpose(1, 0, 2).reshape(N, K, 1, D)), f"outputs {s}"
+        assert np.array_equal(got_l, l[0].view(np.uint32).T.reshape(N, K, 1)), f"lses {s}"
+    del outs, lses
+    _release()
+
+
+@pytest.mark.parametrize("B,path", [
+    (2**31 - 4096, "combine_rows_kernel"),
+    (2**31 + 4096, "combine_elems_kernel"),
+])
+def test_unpack_combine_around_2g_rows(lsec, B, path):
+    """unpack_combine of receive planes [2, B, 1, 10] bf16 (86 GB) that repeat
+    one packed 4096-token block, checked at the start, across 2^31 and at the
+    end against the oracle's unpack + combine of the block."""
+    N, Hl, D, K = 2, 1, 8, 4096
+    _announce(f"unpack_combine N={N} B={B} Hl={Hl} D={D} bf16 ({path})")
+    assert lsec.lsec_combine_path(N, B, Hl, D, packed=True) == path
+    o, l = synth.custom_inputs(N, K, Hl, D, seed=2033, lse_dist=("uniform", -10.0, 30.0),
+                               special=SPECIALS)
+    blk = np.empty((N, K, Hl, D + 2), dtype=np.uint16)
+    blk[..., :D] = o
+    blk[..., D:] = l.view(np.uint16).reshape(N, K, Hl, 2)
+    y_ref, L_ref = oracle.unpack_combine(blk, D, "bf16")
+    oo, _ = oracle.unpack(blk, D)
+    M = max_abs_input(oo, "bf16")
+    rg = torch.empty((N, B, Hl, D + 2), dtype=torch.bfloat16, device=DEV)
+    rg.view(N, B // K, K, Hl, D + 2).copy_(
+        to_dev(blk, "bf16", DEV).view(N, 1, K, Hl, D + 2).expand(N, B // K, K, Hl, D + 2))
+    y, L = lsec.lsec_unpack_combine(rg, base_e=True, return_lse=True)
+    torch.cuda.synchronize()
+    del rg
+    _release()
+    for s in (0, 2**31 - K, 2**31, B - K):
+        if s + K > B:
+            continue
+        assert_output_close(y[s:s + K], y_ref, "bf16", M, f"tokens {s}:{s + K}")
+        assert_lse_close(L[s:s + K], L_ref, f"tokens {s}:{s + K}")
     del y, L
     _release()
