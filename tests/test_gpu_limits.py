@@ -4,7 +4,9 @@ The tiled combine addresses a lane's chunk by a 32-bit byte offset inside its
 plane, so it serves planes below 4 GiB; larger planes take the row kernel,
 which uses 64-bit offsets. The row kernels (combine, pack, unpack) count rows
 in 32 bits, so 2^31 rows and more take the element-wise kernels (64-bit
-throughout); the last tests run each call just below and just above that line. These tests run a plane just below and just above
+throughout); those tests run each call just below and just above that line.
+The corrected partial's tiled kernel addresses the gathered LSEs with 32-bit
+offsets (N * rows < 2^32); the last test runs just below and above that. These tests run a plane just below and just above
 4 GiB (8.6 GB of partial outputs each) and check sampled token ranges at the
 start, the middle and the very end of the planes against the oracle (rows are
 independent, so the oracle's result on a token slice of the inputs is exactly
@@ -210,5 +212,35 @@ def test_unpack_combine_around_2g_rows(lsec, B, path):
             continue
         assert_output_close(y[s:s + K], y_ref, "bf16", M, f"tokens {s}:{s + K}")
         assert_lse_close(L[s:s + K], L_ref, f"tokens {s}:{s + K}")
+    del y, L
+    _release()
+
+
+@pytest.mark.parametrize("B", [2**28 - 4096, 2**28 + 4096])
+def test_correct_partial_around_2_32_lse_entries(lsec, B):
+    """lsec_correct_partial with N=16 gathered LSEs of B rows (D=128 bf16): the
+    tiled kernel addresses the LSEs with 32-bit offsets, so it serves
+    N * B < 2^32 and the element kernel the rest (about 155 GB in all here).
+    The inputs repeat one seeded 4096-row block; rows are checked at the start,
+    across 2^28 and at the end against the oracle's result on the block."""
+    N, D, K, rank = 16, 128, 4096, 5
+    _announce(f"correct_partial N={N} B={B} D={D} bf16 rank {rank} ({N * B} LSE entries)")
+    o, l = synth.custom_inputs(N, K, 1, D, seed=2034, lse_dist=("uniform", -10.0, 30.0),
+                               special=SPECIALS)
+    y_ref, L_ref = oracle.correct_partial(l, rank, o[rank], "bf16")
+    M = max_abs_input(o[rank], "bf16")
+    pg = torch.empty((B, 1, D), dtype=torch.bfloat16, device=DEV)
+    lg = torch.empty((N, B, 1), dtype=torch.float32, device=DEV)
+    pg.view(B // K, K, D).copy_(to_dev(o[rank], "bf16", DEV).view(1, K, D).expand(B // K, K, D))
+    lg.view(N, B // K, K).copy_(f32_to_dev(l, DEV).view(N, 1, K).expand(N, B // K, K))
+    y, L = lsec.lsec_correct_partial(lg, rank, pg, return_lse=True)
+    torch.cuda.synchronize()
+    del pg, lg
+    _release()
+    for s in (0, 2**28 - K, 2**28, B - K):
+        if s + K > B:
+            continue
+        assert_output_close(y[s:s + K], y_ref, "bf16", M, f"rows {s}:{s + K}")
+        assert_lse_close(L[s:s + K], L_ref, f"rows {s}:{s + K}")
     del y, L
     _release()
