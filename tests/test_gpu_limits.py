@@ -5,8 +5,9 @@ plane, so it serves planes below 4 GiB; larger planes take the row kernel,
 which uses 64-bit offsets. The row kernels (combine, pack, unpack) count rows
 in 32 bits, so 2^31 rows and more take the element-wise kernels (64-bit
 throughout); those tests run each call just below and just above that line.
-The corrected partial's tiled kernel addresses the gathered LSEs with 32-bit
-offsets (N * rows < 2^32); the last test runs just below and above that. These tests run a plane just below and just above
+The corrected partial's and the combine's tiled kernels address the LSEs with
+32-bit offsets (N * rows, N * LSE plane stride < 2^32); the last tests run
+just below and above that. These tests run a plane just below and just above
 4 GiB (8.6 GB of partial outputs each) and check sampled token ranges at the
 start, the middle and the very end of the planes against the oracle (rows are
 independent, so the oracle's result on a token slice of the inputs is exactly
@@ -242,5 +243,30 @@ def test_correct_partial_around_2_32_lse_entries(lsec, B):
             continue
         assert_output_close(y[s:s + K], y_ref, "bf16", M, f"rows {s}:{s + K}")
         assert_lse_close(L[s:s + K], L_ref, f"rows {s}:{s + K}")
+    del y, L
+    _release()
+
+
+@pytest.mark.parametrize("lse_stride", [2**29 - 1, 2**29])
+def test_combine_planes_around_2_32_lse_offsets(lsec, lse_stride):
+    """lsec_combine_planes whose LSE planes sit lse_stride floats apart (N=8):
+    the tiled kernel addresses the LSEs with 32-bit offsets, so it serves
+    N * lse_stride < 2^32 (the first case) and the row kernel the second. Only
+    each plane's first T * H floats are written; the gaps (17 GB in all) are
+    never read."""
+    N, T, H, D = 8, 2048, 8, 128
+    _announce(f"combine_planes N={N} T={T} H={H} D={D} bf16, LSE plane stride {lse_stride}")
+    o, l = synth.custom_inputs(N, T, H, D, seed=2035, lse_dist=("uniform", -10.0, 30.0),
+                               special=SPECIALS)
+    y_ref, L_ref = oracle.lse_combine(o, l, "bf16")
+    big = torch.empty((N, lse_stride), dtype=torch.float32, device=DEV)
+    lses = big[:, :T * H].view(N, T, H)
+    assert lses.stride(0) == lse_stride
+    lses.copy_(f32_to_dev(l, DEV))
+    y, L = lsec.lsec_combine_planes(to_dev(o, "bf16", DEV), lses, T, return_lse=True)
+    torch.cuda.synchronize()
+    del big, lses
+    assert_output_close(y, y_ref, "bf16", max_abs_input(o, "bf16"), f"LSE stride {lse_stride}")
+    assert_lse_close(L, L_ref, f"LSE stride {lse_stride}")
     del y, L
     _release()
