@@ -338,19 +338,30 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
 def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
     """Time `steps` steps after `warmup`. With flush_bytes, a buffer of that
     size is rewritten (or, with flush_read, summed) before each step, outside
-    the timed events, so the step's inputs come from HBM."""
+    the timed events, so the step's inputs come from HBM. `kernels` is one
+    step's list of (name, bytes, fn), or a list of such lists (input sets that
+    hold the same work in different memory): step i then runs set i mod the
+    number of sets."""
     import torch
 
+    sets = kernels if kernels and isinstance(kernels[0], list) else [kernels]
     flush = torch.ones(max(flush_bytes // 4, 1), dtype=torch.float32, device=dev) \
         if flush_bytes else None
     for i in range(warmup):
-        for _, _, fn in kernels:
+        for _, _, fn in sets[i % len(sets)]:
             fn()
     torch.cuda.synchronize()
-    nk = len(kernels)
+    nk = len(sets[0])
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if flush is None and sum(b for _, b, _ in sets[0]) < (1 << 30):
+        # Small steps back to back: without a backlog the GPU would wait for
+        # the host to enqueue each launch, and the events around a launch
+        # would time that gap. A spin of ~20 ms + 0.1 ms per launch (about
+        # 2.4e6 cycles per ms on MI355X) lets the host enqueue every step
+        # before the first one runs; wall_s then includes the spin.
+        torch.cuda._sleep(int(2.4e6 * (20 + 0.1 * steps * nk)))
     for i in range(steps):
         if flush is not None:
             if flush_read:
@@ -358,7 +369,7 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
             else:
                 flush.fill_(float(i))
         ev[i][0].record()
-        for k, (_, _, fn) in enumerate(kernels):
+        for k, (_, _, fn) in enumerate(sets[i % len(sets)]):
             fn()
             ev[i][k + 1].record()
     torch.cuda.synchronize()
@@ -370,14 +381,16 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
     return wall, per_kernel_ms
 
 
-def time_floor(kernels, per_kernel_ms, steps, warmup, flush_bytes, dev, flush_read=False):
+def time_floor(kernels, per_kernel_ms, steps, warmup, flush_bytes, dev, flush_read=False,
+               rotate=0):
     """Time the measurement aids under the protocol of the workload's steps:
     an empty launch (one wave), and for each of the step's kernels a plain
     streaming read of as many bytes as that kernel moves (rounded down to 16)
     and a plain copy of half of them (as many bytes read as written), from
     buffers of their own. Each kernel's time per launch is reported as a
     multiple of both: the read bounds the combining kernels, the copy the pack
-    and the corrected partial."""
+    and the corrected partial. With `rotate` the reads and copies cycle
+    through that many buffers, as the steps cycle through their input sets."""
     import torch
 
     import lse_weighted_merge_combine_amd as lsec
@@ -385,20 +398,21 @@ def time_floor(kernels, per_kernel_ms, steps, warmup, flush_bytes, dev, flush_re
     _, e_ms = time_steps([("empty", 0, lambda: lsec.lsec_floor_empty(dev))], steps, warmup,
                          flush_bytes, dev, flush_read)
     reads = []
+    n_sets = max(rotate, 1)
     for k, (name, nbytes, _) in enumerate(kernels):
         nbytes -= nbytes % 16
-        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(n_sets)]
         sink = torch.empty(max(lsec.load_library().lsec_floor_read_blocks(nbytes), 1),
                            dtype=torch.int32, device=dev)
-        _, r_ms = time_steps([("read", nbytes, lambda: lsec.lsec_floor_read(buf, sink))], steps,
-                             warmup, flush_bytes, dev, flush_read)
-        del buf, sink
+        _, r_ms = time_steps([[("read", nbytes, lambda b=b: lsec.lsec_floor_read(b, sink))]
+                              for b in bufs], steps, warmup, flush_bytes, dev, flush_read)
+        del bufs, sink
         half = (nbytes // 2) - (nbytes // 2) % 16
-        csrc = torch.ones(half // 4, dtype=torch.int32, device=dev)
-        cdst = torch.empty_like(csrc)
-        _, c_ms = time_steps([("copy", 2 * half, lambda: lsec.lsec_floor_copy(csrc, cdst))],
-                             steps, warmup, flush_bytes, dev, flush_read)
-        del csrc, cdst
+        pairs = [(torch.ones(half // 4, dtype=torch.int32, device=dev),
+                  torch.empty(half // 4, dtype=torch.int32, device=dev)) for _ in range(n_sets)]
+        _, c_ms = time_steps([[("copy", 2 * half, lambda a=a, c=c: lsec.lsec_floor_copy(a, c))]
+                              for a, c in pairs], steps, warmup, flush_bytes, dev, flush_read)
+        del pairs
         read_ms, copy_ms = r_ms[0] / steps, c_ms[0] / steps
         kernel_ms_k = per_kernel_ms[k] / steps
         reads.append({"kernel": name, "bytes": nbytes, "read_us": round(read_ms * 1e3, 3),
@@ -485,6 +499,12 @@ def main():
     ap.add_argument("--valid-tokens", type=int, default=None,
                     help="direct_planes: combine only this many tokens, the count read by "
                          "the kernels from query_start_loc in device memory")
+    ap.add_argument("--rotate", type=int, default=0, metavar="K",
+                    help="workloads under 1 GiB: instead of a flush, cycle through K input "
+                         "sets of the step (different memory), so each step's inputs were last "
+                         "touched K - 1 steps before; pick K with K x the step's bytes well "
+                         "above the 256 MB Infinity Cache (the steps then run back to back "
+                         "behind a GPU spin that lets the host enqueue them all)")
     ap.add_argument("--flush-read", action="store_true",
                     help="flush by reading the buffer instead of rewriting it (leaves no "
                          "dirty lines in the caches)")
@@ -534,10 +554,20 @@ def main():
     w, info, kernels, host, rows = build_workload(args.workload, dev, args.out_f32,
                                                   args.valid_tokens)
     step_bytes = sum(b for _, b, _ in kernels)
-    flush_mib = args.flush_mib if args.flush_mib >= 0 else (1024 if step_bytes < (1 << 30) else 0)
+    sets = [kernels]
+    if args.rotate:
+        if args.rotate < 2 or step_bytes >= (1 << 30) or args.flush_mib > 0:
+            raise SystemExit("--rotate K needs K >= 2, a step under 1 GiB and no --flush-mib")
+        sets += [build_workload(args.workload, dev, args.out_f32, args.valid_tokens)[2]
+                 for _ in range(args.rotate - 1)]
+        flush_mib = 0
+    else:
+        flush_mib = args.flush_mib if args.flush_mib >= 0 else \
+            (1024 if step_bytes < (1 << 30) else 0)
     log(f"[bench] {args.workload}: {step_bytes / 1e6:.1f} MB per step, warmup {args.warmup}, "
-        f"steps {args.steps}, flush {flush_mib} MiB{' (read)' if args.flush_read else ''}")
-    wall, per_kernel_ms = time_steps(kernels, args.steps, args.warmup, flush_mib << 20, dev,
+        f"steps {args.steps}, " + (f"{args.rotate} input sets in rotation" if args.rotate else
+                                   f"flush {flush_mib} MiB{' (read)' if args.flush_read else ''}"))
+    wall, per_kernel_ms = time_steps(sets, args.steps, args.warmup, flush_mib << 20, dev,
                                      args.flush_read)
     gpu_ms = sum(per_kernel_ms)
     ms_per_step = gpu_ms / args.steps
@@ -561,7 +591,7 @@ def main():
     floor = None
     if args.floor:
         floor = time_floor(kernels, per_kernel_ms, args.steps, args.warmup, flush_mib << 20,
-                           dev, args.flush_read)
+                           dev, args.flush_read, args.rotate)
         log(f"[bench] floor: empty launch {floor['empty_launch_us']} us; " + "; ".join(
             f"plain read of {r['bytes'] / 1e6:.1f} MB {r['read_us']} us ({r['read_GBps']} GB/s), "
             f"copy of half {r['copy_us']} us ({r['copy_GBps']} GB/s)" for r in floor["reads"]))
@@ -590,7 +620,8 @@ def main():
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "step_bytes": step_bytes, "cache_flush_mib": flush_mib,
-        "cache_flush_kind": ("read" if args.flush_read else "write") if flush_mib else "none",
+        "cache_flush_kind": (f"rotation over {args.rotate} input sets" if args.rotate else
+                             ("read" if args.flush_read else "write") if flush_mib else "none"),
         "wall_s": round(wall, 4), "kernels": kernel_detail,
         "roofline": roofline, "cpu_baseline": cpu,
     }
