@@ -576,16 +576,19 @@ constexpr uint64_t kTiledMinBlocksN16 = 1024;
 // Which combine kernel serves a call. `fast` = fast_d(D), rows < 2^31 and the
 // buffers meet the 16-byte (separate) or 4-byte (packed) alignment; otherwise
 // the element-wise kernel runs.
-enum { kPathTiled = 0, kPathRows = 1, kPathElems = 2 };
+enum { kPathTiled = 0, kPathRows = 1, kPathElems = 2, kPathSpan = 3 };
 struct CombinePlan {
     int kind;
     int S;  // row slots per lane (tiled path)
 };
 
 // `pl` gives the plane geometry of the separate layout (packed planes are
-// always dense).
+// always dense). `span_ok`: packed 16-bit rows, a result in the input dtype,
+// planes 16-byte aligned, identity output order and no valid count -- then
+// the calls that would run the tiled kernel with S = 1 on rows of 128 values
+// with N = 2, 4, 8 or 16 run the span kernel when the rows are a multiple of 4.
 CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, int64_t esize, bool packed,
-                         bool fast, Planes pl) {
+                         bool fast, Planes pl, bool span_ok = false) {
     if (!fast) return {kPathElems, 0};
     const bool tiled_shape = (D == 128 || D == 256 || D == 512) && N >= 2 && N <= 16;
     if (tiled_shape) {
@@ -599,6 +602,9 @@ CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, int64_t esize, bool
             const uint64_t min_blocks = N >= 16 ? kTiledMinBlocksN16 : kTiledMinBlocks;
             int S = 16;
             while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < min_blocks) S /= 2;
+            if (S == 1 && span_ok && packed && esize == 2 && D == 128 && rows % 4 == 0 &&
+                (N == 2 || N == 4 || N == 8 || N == 16))
+                return {kPathSpan, 1};
             return {kPathTiled, S};
         }
     }
@@ -610,11 +616,17 @@ void run_combine_dt(const void* src, const float* lse, int64_t N, int64_t rows, 
                     Planes pl, float scale, float inv_scale, void* out, int out_f32,
                     float* out_lse, const CombinePlan& plan, OutMap om, int64_t map_a,
                     int64_t map_c, hipStream_t st) {
-    if (plan.kind == kPathTiled) {
+    if (plan.kind == kPathTiled || plan.kind == kPathSpan) {
         const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
         const TiledArgs a{src, lse, int(N), uint32_t(rows), uint32_t(stride),
                           uint64_t(pl.plane) * sizeof(typename Elem<DT>::T), uint32_t(pl.lse_plane),
                           scale, inv_scale, out, out_f32, out_lse, om, st};
+        if constexpr (PACKED && DT != LSEC_FP32) {
+            if (plan.kind == kPathSpan) {
+                launch_span<DT>(int(N), a);
+                return;
+            }
+        }
         launch_tiled<DT, PACKED>(int(N), plan.S, int(D), a);
     } else if (plan.kind == kPathRows) {
         dispatch_n<DT, PACKED>(src, lse, int(N), uint32_t(rows), int(D), pl, scale, inv_scale,
@@ -639,7 +651,9 @@ int run_combine(const void* src, const float* lse, int64_t N, int64_t rows, int6
                     uint32_t(rows_per_token)};
     const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
     const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
-    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, PACKED, fast, pl);
+    const bool span_ok = PACKED && dt.esize == 2 && !dt.out_f32 && aligned(src, 16) &&
+                         map_a == 0 && valid == nullptr;
+    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, PACKED, fast, pl, span_ok);
     (void)hipGetLastError();
 #define LSEC_RUN(DTV)                                                                        \
     run_combine_dt<DTV, PACKED>(src, lse, N, rows, D, pl, scale, inv_scale, out, dt.out_f32, \
@@ -827,8 +841,11 @@ const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int dt
     const bool fast = aligned_buffers && fast_d(D, dt.esize) && rows < (int64_t(1) << 31);
     int64_t rd;
     if (!mul_ok(rows, D, &rd)) return "none";
-    const CombinePlan plan = plan_combine(N, rows, D, dt.esize, packed != 0, fast, Planes{rd, rows});
+    const bool span_ok = packed && aligned_buffers && dt.esize == 2 && !dt.out_f32;
+    const CombinePlan plan =
+        plan_combine(N, rows, D, dt.esize, packed != 0, fast, Planes{rd, rows}, span_ok);
     if (plan.kind == kPathElems) return "combine_elems_kernel";
+    if (plan.kind == kPathSpan) return "combine_span_kernel";
     if (plan.kind == kPathRows) return "combine_rows_kernel";
     switch (plan.S) {
         case 16: return "combine_tiled_kernel S=16";

@@ -1,7 +1,8 @@
 // lsec_tiled.hip -- the tiled combine of liblsec.so for one element type,
 // compiled once per type (LSEC_TILED_DT = LSEC_BF16, LSEC_FP16, LSEC_FP32) so
 // that its many instantiations build in parallel. The host code in lsec.hip
-// calls launch_tiled<DT, PACKED>, instantiated at the end of this file.
+// calls launch_tiled<DT, PACKED> and, for packed rows of 128 16-bit values,
+// launch_span<DT>, instantiated at the end of this file.
 //
 // Build with -Xclang -target-feature -Xclang -packed-fp32-ops and without
 // fast-math (the NaN / infinity tests must survive).
@@ -168,6 +169,125 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------- combine (packed spans)
+//
+// Packed rows of 128 16-bit values (260 bytes with the fp32 LSE tail) when the
+// rows are a multiple of 4 and the planes 16-byte aligned, N = 2, 4, 8 or 16.
+// A wave owns four consecutive rows of every plane: a 1040-byte span, 65
+// aligned 16-byte chunks. Lane i loads chunk i of each plane and every lane
+// chunk 64 (one address per wave), so all loads are aligned and no separate
+// LSE loads go out: the tails of rows 0, 1, 2 are dword k of the chunks of
+// lanes 16, 32, 48, row 3's the last dword of chunk 64. Lane 16 k + j takes
+// shard j's LSE of row k by a lane shuffle; the weights then follow the
+// slotted kernel exactly (16-lane DPP max and sum, the same normalisation),
+// and every element is accumulated in plane order, so the results are those
+// of the slotted kernel bit for bit. Each dword of a chunk belongs to one row
+// (rows start on dwords) and is weighted by that row's weight. Result chunk q
+// of row k is span dwords 4 (16 k + q) + k .. + 3: this lane's accumulators
+// from dword k on, then the next lane's first k dwords (lane 63: chunk 64's),
+// fetched by one shuffle, so every store is a whole aligned 16-byte chunk.
+// Measured on MI355X (N = 8, 16384 packed rows of 128 bf16): 1.5 % faster cold
+// and 4 % faster warm than the slotted kernel with S = 1.
+template <int DT, int NT>
+__global__ __launch_bounds__(kBlock) void combine_span_kernel(
+    const void* src, uint32_t spans, uint64_t plane_bytes, float scale, float inv_scale,
+    void* __restrict__ out, float* __restrict__ out_lse) {
+    static_assert(DT != LSEC_FP32 && NT >= 2 && NT <= 16, "16-bit rows, N compiled in");
+    constexpr uint32_t kSpanIn = 1040, kSpanOut = 1024;  // 4 rows, with and without tails
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t k = lane >> 4;  // the row of most of this lane's chunk
+    const uint32_t j = lane & 15u;
+    const uint32_t span = xcd_chunked_block(blockIdx.x, gridDim.x) * (kBlock / 64) + threadIdx.x / 64;
+    if (span >= spans) return;  // uniform per wave; no block-wide synchronisation follows
+    const char* base = reinterpret_cast<const char*>(src) + uint64_t(span) * kSpanIn;
+    u32x4 c[NT], e[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const char* pb = base + uint64_t(n) * plane_bytes;
+        c[n] = ld16(pb + 16u * lane);
+        e[n] = ld16(pb + 1024u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Lanes 16, 32, 48 offer dword k - 1 of their chunks (the tails of rows
+    // 0, 1, 2); lane 16 k + j keeps plane j's offer of row k's source lane.
+    float l = -__builtin_inff();
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const uint32_t offer = lane == 16u ? c[n].x : (lane == 32u ? c[n].y : c[n].z);
+        const uint32_t got = uint32_t(__shfl(int(offer), int((k + 1u) * 16u) & 63));
+        const uint32_t mine = k == 3u ? e[n].w : got;
+        if (j == uint32_t(n)) l = __uint_as_float(mine);
+    }
+    l = j < uint32_t(NT) ? sanitize(l) : -__builtin_inff();
+    float m = row16_max(l);
+    if (m == -__builtin_inff()) m = 0.0f;
+    const float w = j < uint32_t(NT) ? weight(l - m, scale) : 0.0f;
+    const float sum = row16_sum(w);
+    const float wn = w * (1.0f / fmaxf(sum, 1e-10f));
+    if (out_lse != nullptr && j == 0u) out_lse[uint64_t(span) * 4u + k] = global_lse(sum, m, inv_scale);
+    // Dword 0 of lanes 32 and 48 and dword 1 of lane 48 belong to the row
+    // before the lane's own; dword k - 1 of lanes 16, 32, 48 is a tail, whose
+    // accumulator is never stored. Chunk 64's first three dwords are row 3's.
+    const bool prev0 = lane == 32u || lane == 48u;
+    const bool prev1 = lane == 48u;
+    float acc[8], acce[6];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 6; ++q) acce[q] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const float w_own = __shfl(wn, n, 16);
+        const float w_prev = __shfl(wn, int((lane & ~15u) - 16u + uint32_t(n)) & 63);
+        const float w3 = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wn), 48 + n));
+        const float w0 = prev0 ? w_prev : w_own;
+        const float w1 = prev1 ? w_prev : w_own;
+        float a, b;
+        Elem<DT>::dec2(c[n].x, a, b);
+        acc[0] = fmaf(a, w0, acc[0]);
+        acc[1] = fmaf(b, w0, acc[1]);
+        Elem<DT>::dec2(c[n].y, a, b);
+        acc[2] = fmaf(a, w1, acc[2]);
+        acc[3] = fmaf(b, w1, acc[3]);
+        Elem<DT>::dec2(c[n].z, a, b);
+        acc[4] = fmaf(a, w_own, acc[4]);
+        acc[5] = fmaf(b, w_own, acc[5]);
+        Elem<DT>::dec2(c[n].w, a, b);
+        acc[6] = fmaf(a, w_own, acc[6]);
+        acc[7] = fmaf(b, w_own, acc[7]);
+        Elem<DT>::dec2(e[n].x, a, b);
+        acce[0] = fmaf(a, w3, acce[0]);
+        acce[1] = fmaf(b, w3, acce[1]);
+        Elem<DT>::dec2(e[n].y, a, b);
+        acce[2] = fmaf(a, w3, acce[2]);
+        acce[3] = fmaf(b, w3, acce[3]);
+        Elem<DT>::dec2(e[n].z, a, b);
+        acce[4] = fmaf(a, w3, acce[4]);
+        acce[5] = fmaf(b, w3, acce[5]);
+    }
+    // The next lane's first three dwords (six values), or chunk 64's for lane 63.
+    float nx[6];
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+        const float down = __shfl_down(acc[q], 1);
+        nx[q] = lane == 63u ? acce[q] : down;
+    }
+    // Element q of the result chunk is value q + 2 k of (acc, nx).
+    float r[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float r1 = q + 2 < 8 ? acc[(q + 2) & 7] : nx[(q + 2 - 8) & 7];
+        const float r2 = q + 4 < 8 ? acc[(q + 4) & 7] : nx[(q + 4 - 8) & 7];
+        const float r3 = q + 6 < 8 ? acc[(q + 6) & 7] : nx[(q + 6 - 8) & 7];
+        r[q] = k == 0u ? acc[q] : (k == 1u ? r1 : (k == 2u ? r2 : r3));
+    }
+    const u32x4 res = {Elem<DT>::enc2(r[0], r[1]), Elem<DT>::enc2(r[2], r[3]),
+                       Elem<DT>::enc2(r[4], r[5]), Elem<DT>::enc2(r[6], r[7])};
+    st16(static_cast<char*>(out) + uint64_t(span) * kSpanOut + 16u * lane, res);
+}
+
 }  // namespace
 
 // Occupancy cap for the tiled combine, as dynamic LDS that the kernel never
@@ -237,5 +357,27 @@ void launch_tiled(int N, int S, int D, const TiledArgs& a) {
 
 template void launch_tiled<LSEC_TILED_DT, false>(int, int, int, const TiledArgs&);
 template void launch_tiled<LSEC_TILED_DT, true>(int, int, int, const TiledArgs&);
+
+// 16-bit elements only; the fp32 unit instantiates an empty launcher that the
+// host never calls (it routes only 16-bit packed rows here).
+template <int DT>
+void launch_span(int N, const TiledArgs& a) {
+    if constexpr (DT != LSEC_FP32) {
+        const uint32_t spans = a.rows / 4;
+        const unsigned blocks = (spans + kBlock / 64 - 1) / (kBlock / 64);
+#define LSEC_SPAN(NV)                                                                       \
+    combine_span_kernel<DT, NV><<<blocks, kBlock, 0, a.st>>>(a.src, spans, a.plane_bytes,   \
+                                                             a.scale, a.inv_scale, a.out, a.out_lse)
+        switch (N) {
+            case 2: LSEC_SPAN(2); break;
+            case 4: LSEC_SPAN(4); break;
+            case 8: LSEC_SPAN(8); break;
+            default: LSEC_SPAN(16); break;
+        }
+#undef LSEC_SPAN
+    }
+}
+
+template void launch_span<LSEC_TILED_DT>(int, const TiledArgs&);
 
 }  // namespace lsec_detail

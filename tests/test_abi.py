@@ -149,7 +149,12 @@ def test_python_binding_rejects_bad_tensors():
     ((16, 16384, 32, 128, 0, 0, 1), "combine_tiled_kernel S=16"),
     ((8, 4096, 16, 512, 0, 0, 1), "combine_tiled_kernel S=8"),
     ((4, 256, 32, 128, 0, 0, 1), "combine_tiled_kernel S=1"),
-    ((8, 2048, 8, 128, 0, 1, 1), "combine_tiled_kernel S=1"),    # packed
+    ((8, 2048, 8, 128, 0, 1, 1), "combine_span_kernel"),          # packed, 16-bit, rows % 4 == 0
+    ((16, 64, 4, 128, 1, 1, 1), "combine_span_kernel"),           # packed fp16, N = 16
+    ((8, 2047, 1, 128, 0, 1, 1), "combine_tiled_kernel S=1"),    # packed, rows % 4 != 0
+    ((5, 2048, 8, 128, 0, 1, 1), "combine_tiled_kernel S=1"),    # packed, N at run time
+    ((8, 2048, 8, 256, 0, 1, 1), "combine_tiled_kernel S=1"),    # packed, D != 128
+    ((8, 2048, 8, 128, 0, 1, 0), "combine_elems_kernel"),        # packed, unaligned buffers
     ((8, 2048, 8, 128, 256, 1, 1), "combine_tiled_kernel S=1"),  # packed, fp32 result
     ((8, 2048, 8, 128, 2, 1, 1), "combine_tiled_kernel S=1"),    # fp32 packed rows
     ((17, 2048, 8, 128, 0, 1, 1), "combine_rows_kernel"),        # packed, N > 16

@@ -18,6 +18,7 @@ from gpu_helpers import (assert_lse_close, assert_output_close, bits_of, f32_bit
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
+TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 @pytest.fixture(scope="module")
@@ -251,8 +252,8 @@ def test_tiled_n16_relaxed_block_count_sampled(lsec):
 
 
 @pytest.mark.parametrize("N,B,H,D,dtype,slots", [
-    (4, 8193, 16, 128, "bf16", 1),   # 32772 rows of the packed layout, ragged
-    (8, 4099, 64, 128, "bf16", 1),   # 32792 rows
+    (4, 8193, 4, 128, "bf16", 1),    # 8193 rows of the packed layout, ragged (not whole spans)
+    (8, 4099, 8, 128, "bf16", 1),    # 4099 rows
     (2, 4097, 32, 512, "f16", 8),    # 65552 rows
     (2, 16389, 64, 128, "bf16", 16),  # 524448 rows
     (5, 8193, 15, 128, "bf16", 1),    # 24579 rows, N at run time
@@ -273,6 +274,38 @@ def test_tiled_unpack_combine_ragged(lsec, N, B, H, D, dtype, slots):
     oo, _ = oracle.unpack(recv_h, D)
     assert_output_close(y, y_ref, dtype, max_abs_input(oo, dtype))
     assert_lse_close(L, L_ref)
+
+
+@pytest.mark.parametrize("N,B,Hl,dtype,base2,return_lse", [
+    (2, 6, 2, "bf16", False, True),      # 12 rows: three spans, one partial block
+    (4, 1027, 4, "f16", True, True),     # 4108 rows: 1027 spans, the last block partial
+    (8, 2048, 8, "bf16", False, True),   # the packed workload's receive side
+    (8, 4101, 4, "f16", False, False),   # 16404 rows, no global LSE
+    (16, 257, 4, "bf16", True, True),    # N = 16
+])
+def test_span_unpack_combine(lsec, N, B, Hl, dtype, base2, return_lse):
+    """Packed rows of 128 16-bit values in whole spans of four: the span kernel
+    (aligned chunk loads, the LSE tails taken from them, realigned stores)."""
+    D, H = 128, N * Hl
+    _announce(f"span unpack_combine N={N} B={B} Hl={Hl} {dtype} base2={base2}")
+    assert lsec.lsec_combine_path(N, B, Hl, D, packed=True, dtype=TDT[dtype]) == \
+        "combine_span_kernel"
+    outs, lses = [], []
+    for r in range(N):
+        a, b = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=900 + 31 * N + r,
+                                   special=SPECIALS)
+        outs.append(a[0])
+        lses.append(b[0])
+    recv_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N, dtype) for r in range(N)])[N - 1]
+    res = lsec.lsec_unpack_combine(to_dev(recv_h, dtype, DEV), base_e=not base2,
+                                   return_lse=return_lse)
+    torch.cuda.synchronize()
+    y, L = res if return_lse else (res, None)
+    y_ref, L_ref = oracle.unpack_combine(recv_h, D, dtype, base2)
+    oo, _ = oracle.unpack(recv_h, D, dtype)
+    assert_output_close(y, y_ref, dtype, max_abs_input(oo, dtype))
+    if return_lse:
+        assert_lse_close(L, L_ref)
 
 
 @pytest.mark.parametrize("N,base2", [(4, False), (8, True), (2, False)])
