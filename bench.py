@@ -180,7 +180,7 @@ def traffic_record(bench_log: str, fetch_dir: str, write_dir: str, commit: str) 
             f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d "
             f"<outdir>/{c}_{workload} -o pmc -- python3 <repo>/bench.py --workload "
             f"{line['config']['workload']}{' --out-f32' if workload.endswith('_f32out') else ''} "
-            "--steps 3 --warmup 1 --no-cpu-baseline --copy-calibration"
+            "--steps 3 --warmup 1 --no-cpu-baseline --no-floor --copy-calibration"
             for c in ("FETCH_SIZE", "WRITE_SIZE")],
     }
 
