@@ -368,29 +368,36 @@ def test_dcp_a2a_lse_reduce_on_kept_buffers(lsec):
         ptrs = (send.data_ptr(), recv.data_ptr())
 
 
-def test_unpack_combine_receive_buffer_off_16_byte_alignment(lsec):
+@pytest.mark.parametrize("N,B,H,dtype", [(8, 64, 16, "bf16"), (16, 37, 64, "f16"), (2, 1030, 4, "bf16")])
+def test_unpack_combine_receive_buffer_off_16_byte_alignment(lsec, N, B, H, dtype):
     """The same receive buffer 4 bytes past a 16-byte boundary (packed rows are
-    only 4-byte aligned anyway) gives the same results as an aligned one."""
-    N, B, H, D = 8, 64, 16, 128
-    _announce("unpack_combine, receive buffer 4 bytes off 16-byte alignment")
+    only 4-byte aligned anyway) gives the same results as an aligned one. The
+    aligned buffer takes the span kernel, the shifted one the tiled kernel;
+    both sum the planes in the same order, so the results agree bit for bit."""
+    D = 128
+    _announce(f"unpack_combine N={N} B={B} H={H} {dtype}, receive buffer 4 bytes off 16-byte alignment")
+    assert lsec.lsec_combine_path(N, B, H // N, D, packed=True, dtype=TDT[dtype]) == \
+        "combine_span_kernel"
     outs, lses = [], []
     for r in range(N):
-        a, b = synth.custom_inputs(1, B, H, D, seed=760 + r, special=SPECIALS)
+        a, b = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=760 + r, special=SPECIALS)
         outs.append(a[0])
         lses.append(b[0])
-    recv_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N) for r in range(N)])[1]
-    flat = torch.empty(recv_h.size + 8, dtype=torch.bfloat16, device=DEV)
+    recv_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N, dtype) for r in range(N)])[1]
+    flat = torch.empty(recv_h.size + 8, dtype=TDT[dtype], device=DEV)
     shifted = flat[2:2 + recv_h.size].view(recv_h.shape)
-    shifted.copy_(to_dev(recv_h, "bf16", DEV))
+    shifted.copy_(to_dev(recv_h, dtype, DEV))
     assert shifted.data_ptr() % 16 == 4
     y1, L1 = lsec.lsec_unpack_combine(shifted, return_lse=True)
-    y2, L2 = lsec.lsec_unpack_combine(to_dev(recv_h, "bf16", DEV), return_lse=True)
+    y2, L2 = lsec.lsec_unpack_combine(to_dev(recv_h, dtype, DEV), return_lse=True)
     torch.cuda.synchronize()
-    y_ref, L_ref = oracle.unpack_combine(recv_h, D, "bf16")
-    oo, _ = oracle.unpack(recv_h, D)
+    y_ref, L_ref = oracle.unpack_combine(recv_h, D, dtype)
+    oo, _ = oracle.unpack(recv_h, D, dtype)
     for y, L in ((y1, L1), (y2, L2)):
-        assert_output_close(y, y_ref, "bf16", max_abs_input(oo, "bf16"))
+        assert_output_close(y, y_ref, dtype, max_abs_input(oo, dtype))
         assert_lse_close(L, L_ref)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(L1.view(torch.int32), L2.view(torch.int32))
 
 
 @pytest.mark.parametrize("N,B,H,D,dtype", [
