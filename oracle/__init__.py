@@ -26,12 +26,14 @@ for 16-bit elements, 1 for fp32).
 Parity status: every function here is pinned by the CPU tests (closed forms,
 brute-force sharded attention, library log-sum-exp / softmax, the second
 formulation of the merge on the Ascend SFA context-parallel page, the simulated
-all-to-all). Two readings are not pinned against any source: the order of the
-LSE's bytes inside the two tail elements of a 16-bit packed row (memory order
-is taken; the round trip through pack and unpack is pinned), and
-``valid_tokens``, the valid-token masking of the direct all-to-all's reduce
-(parity unpinned; ``lse_combine_valid`` applies it in front of the pinned
-``lse_combine``).
+all-to-all; for ``valid_tokens`` / ``lse_combine_valid`` hand-derived counts in
+tests/golden/valid_tokens.json and a padded step of requests whose real tokens
+must combine to unsharded attention whatever the padding holds). One reading
+is not pinned against any source: the order of the LSE's bytes inside the two
+tail elements of a 16-bit packed row (memory order is taken; the round trip
+through pack and unpack is pinned). ``valid_tokens`` restates a reading of the
+direct all-to-all's masking (the page does not show that op's body); its pins
+fix what the reading says, not that the page's op says the same.
 """
 from __future__ import annotations
 
@@ -90,6 +92,10 @@ def _load():
         lib.oracle_unpack.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P]
         lib.oracle_unpack_combine.argtypes = [_P, ctypes.c_int, _I, _I, _I, _I, ctypes.c_int,
                                               _P, _P]
+        lib.oracle_valid_tokens.restype = _I
+        lib.oracle_valid_tokens.argtypes = [_P, _I, _I]
+        lib.oracle_lse_combine_valid.argtypes = [_P, ctypes.c_int, _P, _P, _I, _I, _I, _I, _I,
+                                                 ctypes.c_int, _P, _P, _P]
         _lib = lib
     return _lib
 
@@ -155,26 +161,47 @@ def lse_combine(outputs: np.ndarray, lses: np.ndarray, dtype: str, base2: bool =
     return y, L
 
 
-def valid_tokens(query_start_loc, capacity: int) -> int:
-    """The count of valid tokens of a padded step: the last of the requests'
-    cumulative token offsets, clamped to [0, capacity]. A reading of the
-    ``seq_lens`` / ``query_start_loc`` masking of
-    ``DirectDCPA2AWorkspace.lse_reduce`` (page "vllm.v1.attention.ops.dcp"),
-    whose body the page does not give: tokens past the last request are padding
-    with no result. Parity unpinned (no source fixes the reading)."""
-    t = int(np.asarray(query_start_loc).reshape(-1)[-1])
-    return min(max(t, 0), int(capacity))
+def valid_tokens(query_start_loc, capacity: int, num_reqs: int | None = None) -> int:
+    """The count of valid tokens of a padded step (``oracle_valid_tokens``):
+    entry ``num_reqs`` of the requests' cumulative token offsets (by default
+    the last entry), clamped to [0, capacity]. A reading of the ``seq_lens`` /
+    ``query_start_loc`` arguments of ``DirectDCPA2AWorkspace.lse_reduce``
+    (page "vllm.v1.attention.ops.dcp"), whose body the page does not give:
+    tokens past the last request are padding with no result."""
+    q = np.ascontiguousarray(np.asarray(query_start_loc).reshape(-1), dtype=np.int32)
+    nr = q.size - 1 if num_reqs is None else int(num_reqs)
+    if q.size == 0 or nr < 0 or nr >= q.size:
+        raise ValueError("query_start_loc needs num_reqs + 1 entries")
+    t = int(_load().oracle_valid_tokens(q.ctypes.data, nr, int(capacity)))
+    if t < 0:
+        raise ValueError("oracle valid_tokens: bad arguments")
+    return t
 
 
 def lse_combine_valid(outputs: np.ndarray, lses: np.ndarray, query_start_loc, dtype: str,
-                      base2: bool = False):
+                      base2: bool = False, num_reqs: int | None = None):
     """outputs [N,T,H,D], lses [N,T,H] of a step padded to T tokens ->
-    (y [Tv,H,D], L [Tv,H], Tv): ``lse_combine`` over the first Tv =
-    ``valid_tokens(query_start_loc, T)`` tokens; tokens [Tv, T) have no result."""
-    tv = valid_tokens(query_start_loc, outputs.shape[1])
-    y, L = lse_combine(np.ascontiguousarray(outputs[:, :tv]), np.ascontiguousarray(lses[:, :tv]),
-                       dtype, base2)
-    return y, L, tv
+    (y [Tv,H,D] f64, L [Tv,H] f64, Tv) (``oracle_lse_combine_valid``): the
+    combine of ``lse_combine`` over the first Tv = ``valid_tokens(
+    query_start_loc, T, num_reqs)`` tokens of every plane; tokens [Tv, T) have
+    no result."""
+    o = _bits(outputs, dtype)
+    l = _c(lses, np.float32)
+    N, T, H, D = o.shape
+    if l.shape != (N, T, H):
+        raise ValueError("lses shape must be outputs.shape[:3]")
+    q = np.ascontiguousarray(np.asarray(query_start_loc).reshape(-1), dtype=np.int32)
+    nr = q.size - 1 if num_reqs is None else int(num_reqs)
+    tv_expect = valid_tokens(q, T, nr)
+    y = np.empty((tv_expect, H, D), dtype=np.float64)
+    L = np.empty((tv_expect, H), dtype=np.float64)
+    tv = ctypes.c_int64(-1)
+    _check(_load().oracle_lse_combine_valid(o.ctypes.data, _DT[dtype], l.ctypes.data, q.ctypes.data,
+                                            nr, N, T, H, D, int(base2), y.ctypes.data,
+                                            L.ctypes.data, ctypes.byref(tv)), "lse_combine_valid")
+    if tv.value != tv_expect:
+        raise ValueError("oracle lse_combine_valid: inconsistent valid count")
+    return y, L, tv.value
 
 
 def merge(outputs: np.ndarray, lses: np.ndarray, dtype: str, token_dim: int,

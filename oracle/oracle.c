@@ -310,3 +310,54 @@ int oracle_unpack_combine(const void* recv, int dtype, int64_t N, int64_t B, int
     free(ob);
     return 0;
 }
+
+/* ---- the valid tokens of a padded step ----
+ *
+ * `DirectDCPA2AWorkspace.lse_reduce` on the page "vllm.v1.attention.ops.dcp"
+ * takes the step's `seq_lens` and `query_start_loc`, but the page does not
+ * show what the op does with them. Reading: `query_start_loc` holds the
+ * num_reqs + 1 cumulative token offsets of the step's requests (entry i is
+ * where request i's tokens start), so entry num_reqs is the number of real
+ * tokens; the tokens from there up to the padded capacity T are padding and
+ * get no result. The count is clamped to [0, T]. `seq_lens` changes nothing:
+ * a shard that holds no key of a request reports a NaN or infinite LSE for
+ * it, and the combine already drops such a shard.
+ * Returns the count, or -1 on a bad argument.
+ */
+int64_t oracle_valid_tokens(const int32_t* query_start_loc, int64_t num_reqs, int64_t capacity) {
+    if (!query_start_loc || num_reqs < 0 || capacity < 0) return -1;
+    int64_t t = query_start_loc[num_reqs];
+    if (t < 0) t = 0;
+    if (t > capacity) t = capacity;
+    return t;
+}
+
+/* The combine over the valid tokens of padded planes:
+ * outputs [N][T][H][D] bf16, fp16 or fp32 bits, lses [N][T][H] fp32 (T = the
+ * capacity); tokens [0, Tv) with Tv = oracle_valid_tokens(...) are combined
+ * exactly as oracle_lse_combine does: y [Tv][H][D] fp64, L [Tv][H] or NULL.
+ * *tv receives Tv. Returns 0, or -1 on a bad argument.
+ */
+int oracle_lse_combine_valid(const void* outputs, int dtype, const float* lses,
+                             const int32_t* query_start_loc, int64_t num_reqs, int64_t N,
+                             int64_t T, int64_t H, int64_t D, int base2, double* y, double* L,
+                             int64_t* tv) {
+    if (N < 1 || T < 0 || H < 1 || D < 1 || !elem_bytes(dtype) || !tv) return -1;
+    const int64_t Tv = oracle_valid_tokens(query_start_loc, num_reqs, T);
+    if (Tv < 0) return -1;
+    *tv = Tv;
+    const int64_t plane = T * H; /* rows per plane, padding included */
+    double* ob = (double*)malloc(sizeof(double) * (size_t)(N * D + N));
+    if (!ob) return -2;
+    double* lb = ob + N * D;
+    for (int64_t r = 0; r < Tv * H; ++r) {
+        for (int64_t n = 0; n < N; ++n) {
+            lb[n] = (double)lses[n * plane + r];
+            for (int64_t d = 0; d < D; ++d)
+                ob[n * D + d] = load_elem(outputs, (n * plane + r) * D + d, dtype);
+        }
+        oracle_combine_f64(ob, lb, N, 1, D, base2, &y[r * D], L ? &L[r] : 0);
+    }
+    free(ob);
+    return 0;
+}

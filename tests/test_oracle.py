@@ -437,3 +437,107 @@ def test_corrected_partial_closed_form(oracle_mod):
         assert abs(L[0, 0] - math.log(1.0 + math.exp(w3))) < 1e-15
     with pytest.raises(ValueError):
         oracle_mod.correct_partial(l, 2, o[0].reshape(1, 1, 2), "bf16")
+
+
+# ---------------------------------------------------------------- valid tokens of a padded step
+#
+# Reading of DirectDCPA2AWorkspace.lse_reduce (page "vllm.v1.attention.ops.dcp"),
+# whose seq_lens / query_start_loc arguments the page passes without showing
+# the op's body: entry num_reqs of query_start_loc counts the real tokens, the
+# rest of the capacity is padding with no result.
+
+VALID_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "valid_tokens.json")
+
+
+def _valid_cases():
+    with open(VALID_GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _valid_cases(), ids=lambda c: c["name"])
+def test_valid_tokens_hand_derived(oracle_mod, case):
+    q = np.array(case["query_start_loc"], dtype=np.int32)
+    assert oracle_mod.valid_tokens(q, case["capacity"], case["num_reqs"]) == case["valid"]
+    if case["num_reqs"] == len(q) - 1:  # the default is the last entry
+        assert oracle_mod.valid_tokens(q, case["capacity"]) == case["valid"]
+
+
+def _padded_step(rng, req_lens, T, N, H, dk, D, keys_per_req):
+    """A step of requests padded to T tokens, as the direct exchange delivers
+    it: every real token attends to its request's keys, which are split over N
+    shards (contiguous runs; a shard may hold none of a request's keys, and
+    then reports output 0 and LSE -inf). Partials and LSEs are stored in fp32.
+    Padding tokens hold NaN outputs and arbitrary LSEs. Returns the planes,
+    query_start_loc and the unsharded attention (output, LSE) of the real
+    tokens."""
+    qsl = np.concatenate([[0], np.cumsum(req_lens)]).astype(np.int32)
+    Tv = int(qsl[-1])
+    o = np.full((N, T, H, D), np.nan, dtype=np.float32)
+    lse = rng.uniform(-50, 50, size=(N, T, H)).astype(np.float32)
+    lse[:, Tv:][rng.random((N, T - Tv, H)) < 0.3] = np.inf
+    full = np.zeros((Tv, H, D))
+    full_l = np.zeros((Tv, H))
+    for r, n_tok in enumerate(req_lens):
+        L = keys_per_req[r]
+        k = rng.normal(size=(L, H, dk)) * 2.0
+        v = rng.normal(size=(L, H, D)) * 3.0
+        cuts = np.sort(rng.integers(0, L + 1, size=N - 1))  # may leave shards empty
+        sets = np.split(np.arange(L), cuts)
+        for t in range(qsl[r], qsl[r] + n_tok):
+            q = rng.normal(size=(H, dk))
+            for h in range(H):
+                full[t, h], full_l[t, h] = _attention(q[h], k[:, h], v[:, h])
+                for n, s in enumerate(sets):
+                    on, ln = _attention(q[h], k[s, h], v[s, h])
+                    o[n, t, h], lse[n, t, h] = on, ln
+    return o, lse, qsl, full, full_l
+
+
+@pytest.mark.parametrize("req_lens,T,N", [([3, 0, 4], 10, 3), ([1, 1, 1, 1], 6, 4),
+                                          ([5, 2], 7, 2), ([], 5, 2)])
+def test_valid_combine_is_attention_of_the_real_tokens(oracle_mod, req_lens, T, N):
+    """The real tokens of a padded step combine to the unsharded attention of
+    each token over its request's keys, whatever the padding holds; Tv is the
+    number of real tokens and no padding row is returned."""
+    rng = np.random.default_rng(sum(req_lens) * 31 + T + N)
+    H, dk, D = 2, 8, 6
+    o, lse, qsl, full, full_l = _padded_step(rng, req_lens, T, N, H, dk, D,
+                                                keys_per_req=[7 + 3 * i for i in range(len(req_lens))])
+    y, Lg, tv = oracle_mod.lse_combine_valid(o, lse, qsl, "f32")
+    assert tv == sum(req_lens) and y.shape == (tv, H, D) and Lg.shape == (tv, H)
+    if tv:
+        # fp32 storage of partials and LSEs: |y - y*| <= (1 + 4 max|l|) 2^-24 M
+        # (as in test_brute_force_fp32_storage), M = max |partial| of the real tokens
+        real_l = lse[:, :tv][np.isfinite(lse[:, :tv])]
+        M = np.nanmax(np.abs(o[:, :tv]))
+        bound = (1 + 4 * np.abs(real_l).max()) * 2.0 ** -24 * M
+        assert np.abs(y - full).max() <= bound
+        np.testing.assert_allclose(Lg, full_l, rtol=0, atol=4 * 2.0 ** -24 * np.abs(real_l).max() + 1e-12)
+        # the same as the plain combine of the first tv tokens
+        y2, L2 = oracle_mod.lse_combine(np.ascontiguousarray(o[:, :tv]),
+                                        np.ascontiguousarray(lse[:, :tv]), "f32")
+        assert np.array_equal(y, y2) and np.array_equal(Lg, L2)
+    # padding contents do not matter
+    o2, lse2 = o.copy(), lse.copy()
+    o2[:, tv:] = 1e30
+    lse2[:, tv:] = -np.inf
+    y3, L3, tv3 = oracle_mod.lse_combine_valid(o2, lse2, qsl, "f32")
+    assert tv3 == tv and np.array_equal(y3, y) and np.array_equal(L3, Lg)
+
+
+def test_valid_combine_counts_entry_num_reqs(oracle_mod, synth_mod):
+    """A query_start_loc longer than num_reqs + 1 (a buffer sized for more
+    requests): the count comes from entry num_reqs, and the capacity clamps it."""
+    o, l = synth_mod.custom_inputs(3, 9, 2, 8, dtype="bf16", seed=5)
+    q = np.array([0, 2, 5, 9, 9], dtype=np.int32)
+    for nr, want in ((0, 0), (1, 2), (2, 5), (3, 9), (4, 9)):
+        y, L, tv = oracle_mod.lse_combine_valid(o, l, q, "bf16", num_reqs=nr)
+        assert tv == want and y.shape[0] == want
+        if want:
+            y2, L2 = oracle_mod.lse_combine(np.ascontiguousarray(o[:, :want]),
+                                            np.ascontiguousarray(l[:, :want]), "bf16")
+            assert np.array_equal(y, y2) and np.array_equal(L, L2)
+    _, _, tv = oracle_mod.lse_combine_valid(o, l, np.array([0, 40], dtype=np.int32), "bf16")
+    assert tv == 9
+    with pytest.raises(ValueError):
+        oracle_mod.valid_tokens(q, 9, num_reqs=5)

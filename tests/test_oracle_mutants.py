@@ -53,6 +53,17 @@ MUTANTS = [
     ("correct_wrong_rank", "if (n == rank) wr = w;", "if (n == 0) wr = w;", None),
     ("correct_lse_without_max", "if (L) L[r] = (base2 ? log2(s) : log(s)) + m;",
      "if (L) L[r] = (base2 ? log2(s) : log(s));", 1),
+    ("valid_reads_previous_entry", "int64_t t = query_start_loc[num_reqs];",
+     "int64_t t = query_start_loc[num_reqs > 0 ? num_reqs - 1 : 0];", None),
+    ("valid_reads_next_entry", "int64_t t = query_start_loc[num_reqs];",
+     "int64_t t = query_start_loc[num_reqs + 1];", None),
+    ("valid_reads_first_entry", "int64_t t = query_start_loc[num_reqs];",
+     "int64_t t = query_start_loc[0];", None),
+    ("valid_no_capacity_clamp", "    if (t > capacity) t = capacity;\n", "", None),
+    ("valid_no_negative_clamp", "    if (t < 0) t = 0;\n", "", None),
+    ("valid_takes_the_last_tokens", "n * plane + r", "n * plane + (T - Tv) * H + r", None),
+    ("valid_plane_stride_of_valid_tokens", "const int64_t plane = T * H;",
+     "const int64_t plane = Tv * H;", None),
 ]
 
 RUNNER = textwrap.dedent("""
@@ -87,9 +98,14 @@ RUNNER = textwrap.dedent("""
         ("merge layout", lambda: t.test_merge_matches_page2_layout(m, synth, 2, "bf16")),
         ("corrected partials", lambda: t.test_corrected_partials_sum_to_the_combine(m, synth, True, "bf16")),
         ("corrected partial closed form", lambda: t.test_corrected_partial_closed_form(m)),
+        ("valid tokens: padded step of requests",
+         lambda: t.test_valid_combine_is_attention_of_the_real_tokens(m, [3, 0, 4], 10, 3)),
+        ("valid tokens: entry num_reqs", lambda: t.test_valid_combine_counts_entry_num_reqs(m, synth)),
     ]
     pins += [("closed form " + c["name"], (lambda c=c: t.test_closed_forms(m, c)))
              for c in t._golden_cases()]
+    pins += [("valid tokens " + c["name"], (lambda c=c: t.test_valid_tokens_hand_derived(m, c)))
+             for c in t._valid_cases()]
     failed = []
     for name, fn in pins:
         try:
