@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows_kernel(
 
     float acc[E];
 #pragma unroll
-    for (int k = 0; k < E; ++k) acc[k] = 0.0f;
+    for (int k = 0; k < E; ++k) acc[k] = kAccInit;
     float m, s;
     if constexpr (NT > 0) {
         float l[NT];
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void combine_elems_kernel(
         float s = 0.0f;
         for (int n = 0; n < N; ++n) s += weight(sanitize(load_lse(n)) - m, scale);
         const float inv = 1.0f / fmaxf(s, 1e-10f);
-        float acc = 0.0f;
+        float acc = kAccInit;
         for (int n = 0; n < N; ++n) {
             float w = weight(sanitize(load_lse(n)) - m, scale) * inv;
             acc = fmaf(Elem<DT>::dec1(rp[n * plane + d]), w, acc);
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kBlock) void correct_tiled_kernel(
         if (row[s] < rows) {
             float acc[E];
 #pragma unroll
-            for (int k = 0; k < E; ++k) acc[k] = 0.0f;
+            for (int k = 0; k < E; ++k) acc[k] = kAccInit;
             fma_chunk<DT>(v[s], wr, acc);
             if constexpr (SPLIT) {
                 float* p = static_cast<float*>(out) + uint64_t(row[s]) * D + lane * 4;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kBlock) void correct_elems_kernel(
             if (n == rank) wr = w;
         }
         wr *= 1.0f / fmaxf(s, 1e-10f);
-        store_elem<DT>(out, i, fmaf(Elem<DT>::dec1(part[i]), wr, 0.0f), out_f32);
+        store_elem<DT>(out, i, fmaf(Elem<DT>::dec1(part[i]), wr, kAccInit), out_f32);
         if (out_lse != nullptr && d == 0) out_lse[row] = global_lse(s, m, inv_scale);
     }
 }

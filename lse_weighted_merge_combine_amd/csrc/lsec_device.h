@@ -176,6 +176,11 @@ __device__ __forceinline__ float global_lse(float s, float m, float inv_scale) {
     return log2f(s) * inv_scale + m;
 }
 
+// Accumulators start at -0: fma(a, w, -0) is exactly a * w for every
+// product, a signed zero included (starting at +0 would turn a -0 product into
+// +0), so a single shard of weight 1 comes back bit for bit, -0 included.
+constexpr float kAccInit = -0.0f;
+
 // Accumulate one 16-byte chunk (kEpc elements) scaled by w into acc.
 template <int DT>
 __device__ __forceinline__ void fma_chunk(u32x4 v, float w, float (&acc)[Elem<DT>::kEpc]) {

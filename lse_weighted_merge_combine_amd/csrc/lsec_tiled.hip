@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kBlock) void combine_tiled_kernel(
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int k = 0; k < E; ++k) acc[s][k] = 0.0f;
+        for (int k = 0; k < E; ++k) acc[s][k] = kAccInit;
 #pragma unroll 1
     for (int n0 = 0; n0 < N; n0 += PG) {
         if (n0 > 0) load_group(n0);
@@ -233,9 +233,9 @@ __global__ __launch_bounds__(kBlock) void combine_span_kernel(
     const bool prev1 = lane == 48u;
     float acc[8], acce[6];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int q = 0; q < 8; ++q) acc[q] = kAccInit;
 #pragma unroll
-    for (int q = 0; q < 6; ++q) acce[q] = 0.0f;
+    for (int q = 0; q < 6; ++q) acce[q] = kAccInit;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const float w_own = __shfl(wn, n, 16);

@@ -90,3 +90,41 @@ def assert_lse_close(L_gpu: torch.Tensor, L_ref: np.ndarray, what: str = "") -> 
     err = float(np.max(np.abs(L[fin] - L_ref[fin])))
     assert err <= 1e-5, f"{what}: max |LSE gpu - oracle| = {err:.3g} > 1e-5"
     return err
+
+
+def host_threads() -> int:
+    """Threads for host-side oracle work: the CPUs this process may use, at
+    most 16 (a GPU machine's share for one GPU)."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def assert_combine_close_in_chunks(y_gpu: torch.Tensor, L_gpu, o: np.ndarray, l: np.ndarray,
+                                   dtype: str, base2: bool, M: float, chunk_tokens: int = 1024,
+                                   what: str = "") -> None:
+    """Every row of a combine [B, H, D] (and its global LSE [B, H], if given)
+    against the oracle, element by element. The oracle runs over token ranges
+    of o [N, B, H, D] / l [N, B, H] on host threads (rows are independent, so a
+    token range of the inputs gives exactly those rows' results), which bounds
+    host memory at full size."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    B = o.shape[1]
+    ranges = [(s, min(s + chunk_tokens, B)) for s in range(0, B, chunk_tokens)]
+
+    def ref(r):
+        s, e = r
+        return oracle.lse_combine(np.ascontiguousarray(o[:, s:e]), np.ascontiguousarray(l[:, s:e]),
+                                  dtype, base2=base2)
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        for (s, e), (y_ref, L_ref) in zip(ranges, ex.map(ref, ranges)):
+            assert_output_close(y_gpu[s:e], y_ref, dtype, M, f"{what} tokens {s}:{e}")
+            if L_gpu is not None:
+                assert_lse_close(L_gpu[s:e], L_ref, f"{what} tokens {s}:{e}")
