@@ -191,7 +191,14 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
     """Inputs on the device, preallocated outputs and the step's kernels.
     valid_tokens (direct_planes only): the count of valid tokens is read by the
     kernels from a query_start_loc array in device memory; the other tokens of
-    the padded step are neither read nor written."""
+    the padded step are neither read nor written.
+
+    Returns a namespace: w (the workload), kind, info (the JSON config),
+    kernels [(name, algorithmic bytes, launch fn)], rows, outputs (the step's
+    output buffers by name), host (the host inputs the CPU leg needs),
+    result_dtype and cpu_bytes (the algorithmic bytes of the oracle's pass)."""
+    from types import SimpleNamespace
+
     import numpy as np
     import torch
 
@@ -224,7 +231,6 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
         o, l = synth.combine_inputs(w)
         part = dev_bits(o[rank])
         lg = torch.from_numpy(l).to(dev)
-        del o
         out = torch.empty((w.B, w.H, w.D), dtype=odt, device=dev)
         rows = w.B * w.H
         nbytes = w.N * rows * 4 + rows * w.D * s + rows * w.D * os_
@@ -235,7 +241,8 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
             lsec.lsec_correct_partial(lg, rank, part, base_e=not w.base2, out=out, out_dtype=odt)
 
         kernels = [(kname, nbytes, step)]
-        host = None
+        host = (o, l, rank)
+        outputs = {"out": out}
         info["rank"] = rank
     elif w.kind == "planes":
         T_max = 2 * w.B
@@ -264,6 +271,7 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
 
         kernels = [(kname, nbytes, step)]
         host = (np.ascontiguousarray(o[:, :K]), np.ascontiguousarray(l[:, :K]))
+        outputs = {"out": out[:K], "out_lse": out_lse[:K]}
         rows = K * w.H
         info["T_max"] = T_max
     elif w.kind == "merge":
@@ -279,6 +287,7 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
 
         kernels = [(kname, nbytes, step)]
         host = (o, l)
+        outputs = {"out": out}
         rows = w.B * w.H
         info["token_dim"] = 2
     elif w.kind == "combine":
@@ -299,6 +308,9 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
 
         kernels = [(kname, nbytes, step)]
         host = (o, l)
+        outputs = {"out": out}
+        if out_lse is not None:
+            outputs["out_lse"] = out_lse
         rows = w.B * w.H
     else:
         Hl = w.H // w.N
@@ -328,9 +340,14 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
                    (f"{lsec.lsec_combine_path(w.N, w.B, Hl, w.D, packed=True, dtype=tdt)} "
                     f"({w.dtype}, N={w.N}, D={w.D}, packed rows)",
                     unpack_combine_bytes(w.N, w.B, Hl, w.D, s, True), unpack_combine)]
-        host = None
+        host = ([a for a, _ in outs], [b for _, b in outs])
+        outputs = {"send": send, "out": out, "out_lse": out_lse}
         rows = w.B * Hl
-    return w, info, kernels, host, rows
+    rdt = "f32" if (out_f32 or w.dtype == "f32") else w.dtype
+    cpu_bytes = combine_bytes(w.N, host[0].shape[1] if w.kind in ("combine", "planes") else w.B,
+                              w.H, w.D, s, w.return_lse, os_)
+    return SimpleNamespace(w=w, kind=w.kind, info=info, kernels=kernels, rows=rows,
+                           outputs=outputs, host=host, result_dtype=rdt, cpu_bytes=cpu_bytes)
 
 
 # ---------------------------------------------------------------- timing
@@ -341,7 +358,9 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
     the timed events, so the step's inputs come from HBM. `kernels` is one
     step's list of (name, bytes, fn), or a list of such lists (input sets that
     hold the same work in different memory): step i then runs set i mod the
-    number of sets."""
+    number of sets. Returns the wall time of the timed loop and, per kernel,
+    the list of its launch times in ms (HIP events on the current stream,
+    the one the kernels are launched on)."""
     import torch
 
     sets = kernels if kernels and isinstance(kernels[0], list) else [kernels]
@@ -374,23 +393,32 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
             ev[i][k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_kernel_ms = [0.0] * nk
-    for i in range(steps):
-        for k in range(nk):
-            per_kernel_ms[k] += ev[i][k].elapsed_time(ev[i][k + 1])
-    return wall, per_kernel_ms
+    times = [[ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(steps)] for k in range(nk)]
+    return wall, times
 
 
-def time_floor(kernels, per_kernel_ms, steps, warmup, flush_bytes, dev, flush_read=False,
-               rotate=0):
+def stats_us(ms):
+    """Mean, median, p10 / p90, min / max of launch times given in ms, in µs."""
+    import numpy as np
+
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"mean_us": round(float(a.mean()), 3), "median_us": round(float(np.median(a)), 3),
+            "p10_us": round(float(np.percentile(a, 10)), 3),
+            "p90_us": round(float(np.percentile(a, 90)), 3),
+            "min_us": round(float(a.min()), 3), "max_us": round(float(a.max()), 3)}
+
+
+def time_floor(kernels, times, steps, warmup, flush_bytes, dev, flush_read=False, rotate=0):
     """Time the measurement aids under the protocol of the workload's steps:
     an empty launch (one wave), and for each of the step's kernels a plain
     streaming read of as many bytes as that kernel moves (rounded down to 16)
     and a plain copy of half of them (as many bytes read as written), from
     buffers of their own. Each kernel's time per launch is reported as a
-    multiple of both: the read bounds the combining kernels, the copy the pack
-    and the corrected partial. With `rotate` the reads and copies cycle
-    through that many buffers, as the steps cycle through their input sets."""
+    multiple of both (means; medians too): the read bounds the combining
+    kernels, the copy the pack and the corrected partial. With `rotate` the
+    reads and copies cycle through that many buffers, as the steps cycle
+    through their input sets."""
+    import numpy as np
     import torch
 
     import lse_weighted_merge_combine_amd as lsec
@@ -413,60 +441,243 @@ def time_floor(kernels, per_kernel_ms, steps, warmup, flush_bytes, dev, flush_re
         _, c_ms = time_steps([[("copy", 2 * half, lambda a=a, c=c: lsec.lsec_floor_copy(a, c))]
                               for a, c in pairs], steps, warmup, flush_bytes, dev, flush_read)
         del pairs
-        read_ms, copy_ms = r_ms[0] / steps, c_ms[0] / steps
-        kernel_ms_k = per_kernel_ms[k] / steps
+        read_ms, copy_ms = float(np.mean(r_ms[0])), float(np.mean(c_ms[0]))
+        read_med, copy_med = float(np.median(r_ms[0])), float(np.median(c_ms[0]))
+        kernel_ms_k, kernel_med = float(np.mean(times[k])), float(np.median(times[k]))
         reads.append({"kernel": name, "bytes": nbytes, "read_us": round(read_ms * 1e3, 3),
+                      "read_median_us": round(read_med * 1e3, 3),
                       "read_GBps": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
                       "kernel_over_read": round(kernel_ms_k / read_ms, 3),
+                      "kernel_over_read_median": round(kernel_med / read_med, 3),
                       "copy_us": round(copy_ms * 1e3, 3),
+                      "copy_median_us": round(copy_med * 1e3, 3),
                       "copy_GBps": round(2 * half / (copy_ms * 1e-3) / 1e9, 1),
-                      "kernel_over_copy": round(kernel_ms_k / copy_ms, 3)})
-    return {"empty_launch_us": round(e_ms[0] / steps * 1e3, 3), "reads": reads,
+                      "kernel_over_copy": round(kernel_ms_k / copy_ms, 3),
+                      "kernel_over_copy_median": round(kernel_med / copy_med, 3)})
+    return {"empty_launch_us": round(float(np.mean(e_ms[0])) * 1e3, 3), "reads": reads,
             "kernels": ["floor_empty_kernel", "floor_read_kernel", "floor_copy_kernel"],
             "timing": "HIP events, same flush protocol as the steps"}
 
 
-# ---------------------------------------------------------------- CPU baseline
+# ---------------------------------------------------------------- CPU leg: oracle timing and parity
+#
+# The oracle (oracle/, plain fp64 C) is called from here only: the leg times
+# it on the host's cores over the workload, and compares the output buffers
+# the GPU produced from the same inputs (saved before the timed steps) with
+# its results.
 
-def cpu_baseline(w, host, threads: int):
-    """Time the fp64 oracle over the workload's rows on `threads` host threads
-    (token ranges split statically; input slicing is not timed)."""
+TOL = {"bf16": 8e-3, "f16": 1e-3, "f32": 2e-5}  # |y - y_oracle| <= TOL * M + 1e-6
+LSE_TOL = 1e-5                                    # absolute
+
+
+def host_threads() -> int:
+    """The host threads used for oracle work: the CPUs this process may use,
+    at most 16 (a GPU machine's share of its host for one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def max_abs_bits(bits, dtype: str) -> float:
+    """Largest finite |value| of an array of element patterns (uint16 bf16 /
+    fp16, float32 or uint32 fp32)."""
+    import numpy as np
+
+    b = np.ascontiguousarray(bits)
+    if dtype == "f32":
+        x = b.view(np.float32)
+    elif dtype == "bf16":
+        x = (b.astype(np.uint32) << 16).view(np.float32)
+    else:
+        x = b.view(np.float16)
+    with np.errstate(invalid="ignore"):
+        x = np.abs(x.astype(np.float64))
+    x = x[np.isfinite(x)]
+    return float(x.max()) if x.size else 0.0
+
+
+def _f64(t):
+    """A host tensor's values as float64 numpy."""
+    return t.float().numpy().astype("float64")
+
+
+class Check:
+    """Running maximum of |gpu - oracle| for one output buffer."""
+
+    def __init__(self, name, kind, dtype=None, M=None):
+        self.name, self.kind, self.dtype, self.M = name, kind, dtype, M
+        self.err, self.ok, self.n = 0.0, True, 0
+
+    def values(self, got, ref):
+        import numpy as np
+
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        self.n += ref.size
+        same_nan = np.array_equal(np.isnan(got), np.isnan(ref))
+        inf = np.isinf(ref)
+        fin = np.isfinite(ref)
+        same_inf = np.array_equal(got[inf], ref[inf]) and bool(np.all(np.isfinite(got[fin])))
+        if not (same_nan and same_inf):
+            self.ok = False
+        if fin.any():
+            self.err = max(self.err, float(np.max(np.abs(got[fin] - ref[fin]))))
+        if self.err > self.tol():
+            self.ok = False
+
+    def bits(self, got, ref):
+        import numpy as np
+
+        self.n += np.asarray(ref).size
+        if not np.array_equal(np.asarray(got), np.asarray(ref)):
+            self.ok = False
+
+    def tol(self):
+        if self.kind == "lse":
+            return LSE_TOL
+        if self.kind == "bits":
+            return 0.0
+        return TOL[self.dtype] * self.M + 1e-6
+
+    def record(self):
+        r = {"buffer": self.name, "elements": self.n, "ok": bool(self.ok)}
+        if self.kind == "bits":
+            r["rule"] = "bit-exact"
+        else:
+            r.update({"max_abs_err": self.err, "tol": self.tol(),
+                      "rule": "|gpu - oracle| <= 1e-5" if self.kind == "lse" else
+                      f"|gpu - oracle| <= {TOL[self.dtype]} * M + 1e-6, M = {self.M:.6g}"})
+        return r
+
+
+def _token_parts(B, parts):
+    import numpy as np
+
+    parts = max(1, min(parts, B))
+    b = np.linspace(0, B, parts + 1).astype(int)
+    return list(zip(b[:-1].tolist(), b[1:].tolist()))
+
+
+def _run_parts(fn, parts, threads):
+    """Run fn(part) for every part on `threads` host threads (ctypes drops the
+    GIL inside the oracle); returns (wall seconds, results in part order)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    t0 = time.perf_counter()
+    if threads == 1:
+        res = [fn(p) for p in parts]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            res = list(ex.map(fn, parts))
+    return time.perf_counter() - t0, res
+
+
+def cpu_leg(work, saved, threads: int, time_it: bool):
+    """The oracle over the workload: parity of the GPU's saved output buffers
+    and, with time_it (combine workloads), the CPU baseline: the oracle as it
+    stands over the whole workload on one thread and on `threads` threads
+    (token ranges split statically), median of 3 runs each."""
     import numpy as np
 
     import oracle
 
-    o, l = host
-    B = o.shape[1]  # the tokens timed on the GPU (fewer than w.B with --valid-tokens)
-    if B == 0:
-        return None
-    threads = max(1, min(threads, B))
-    bounds = np.linspace(0, B, threads + 1).astype(int)
-    parts = [(np.ascontiguousarray(o[:, a:b]), np.ascontiguousarray(l[:, a:b]))
-             for a, b in zip(bounds[:-1], bounds[1:])]
     oracle._load()
-    errs = []
+    w = work.w
+    checks = []
+    cpu = None
+    if work.kind in ("combine", "planes"):
+        o, l = work.host
+        B = o.shape[1]
+        rdt = work.result_dtype
+        M = max_abs_bits(o, w.dtype)
+        y_chk = Check("out", "values", rdt, M)
+        l_chk = Check("out_lse", "lse") if "out_lse" in saved else None
 
-    def run(p):
-        try:
-            oracle.lse_combine(p[0], p[1], w.dtype, base2=w.base2)
-        except Exception as e:  # noqa: BLE001 - reported below
-            errs.append(e)
+        def part(r):
+            a, b = r
+            return oracle.lse_combine(np.ascontiguousarray(o[:, a:b]), np.ascontiguousarray(l[:, a:b]),
+                                      w.dtype, base2=w.base2)
 
-    ts = [threading.Thread(target=run, args=(p,)) for p in parts]
-    t0 = time.perf_counter()
-    for t in ts:
-        t.start()
-    for t in ts:
-        t.join()
-    dt = time.perf_counter() - t0
-    if errs:
-        raise errs[0]
-    nbytes = combine_bytes(w.N, B, w.H, w.D, 4 if w.dtype == "f32" else 2, w.return_lse)
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "rows_per_s": round(B * w.H / dt, 1),
-            "sample": f"the whole workload ({B * w.H} rows, N={w.N}, D={w.D}) through the fp64 "
-                      f"C oracle, token ranges split over {threads} threads"}
+        def compare(parts, res):
+            for (a, b), (y, L) in zip(parts, res):
+                y_chk.values(_f64(saved["out"][a:b]), y)
+                if l_chk is not None:
+                    l_chk.values(_f64(saved["out_lse"][a:b]), L)
+
+        many = _token_parts(B, threads)
+        runs = []
+        for _ in range(3 if time_it else 1):
+            dt, res = _run_parts(part, many, threads)
+            runs.append(dt)
+        compare(many, res)
+        del res
+        checks = [y_chk] + ([l_chk] if l_chk is not None else [])
+        if time_it and B:
+            single = []
+            for _ in range(3):
+                dt, res = _run_parts(part, [(0, B)], 1)
+                single.append(dt)
+                del res
+            nbytes = work.cpu_bytes
+            rows = B * w.H
+
+            def leg(ts, nthreads):
+                med = float(np.median(ts))
+                return {"value": round(nbytes / med / 1e9, 3), "unit": "GB/s",
+                        "seconds": round(med, 4), "seconds_runs": [round(t, 4) for t in ts],
+                        "rows_per_s": round(rows / med, 1), "threads": nthreads}
+            multi = leg(runs, len(many))
+            cpu = {"value": multi["value"], "unit": "GB/s", "cores": len(many), "kind": "oracle",
+                   "sample": f"the whole workload ({rows} rows, N={w.N}, D={w.D}) through the "
+                             f"fp64 C oracle, median of 3 runs: token ranges split statically over "
+                             f"{len(many)} threads, and once more on 1 thread",
+                   "seconds": multi["seconds"], "seconds_runs": multi["seconds_runs"],
+                   "rows_per_s": multi["rows_per_s"], "single_thread": leg(single, 1),
+                   "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+                   "cpu_model": cpu_info()}
+        else:
+            cpu = {"oracle_s": round(runs[0], 4), "threads": len(many)}
+    elif work.kind == "packed":
+        outs, lses = work.host
+        N, Hl = w.N, w.H // w.N
+        t0 = time.perf_counter()
+        send_ref = oracle.pack_send(outs[0], lses[0], N, w.dtype)
+        c = Check("send", "bits")
+        c.bits(saved["send"].view(_int_view(w.dtype)).numpy().view(send_ref.dtype), send_ref)
+        so = np.stack([np.ascontiguousarray(a[:, :Hl]) for a in outs])
+        sl = np.stack([np.ascontiguousarray(b[:, :Hl]) for b in lses])
+        y, L = oracle.lse_combine(so, sl, w.dtype, base2=w.base2)
+        yc = Check("out", "values", w.dtype, max_abs_bits(so, w.dtype))
+        yc.values(_f64(saved["out"]), y)
+        lc = Check("out_lse", "lse")
+        lc.values(_f64(saved["out_lse"]), L)
+        checks = [c, yc, lc]
+        cpu = {"oracle_s": round(time.perf_counter() - t0, 4), "threads": 1}
+    elif work.kind == "merge":
+        o, l = work.host
+        t0 = time.perf_counter()
+        y, _ = oracle.merge(o, l, w.dtype, 2, base2=w.base2)
+        yc = Check("out", "values", w.dtype, max_abs_bits(o, w.dtype))
+        yc.values(_f64(saved["out"]), y)
+        checks = [yc]
+        cpu = {"oracle_s": round(time.perf_counter() - t0, 4), "threads": 1}
+    elif work.kind == "correct":
+        o, l, rank = work.host
+        t0 = time.perf_counter()
+        y, _ = oracle.correct_partial(l, rank, o[rank], w.dtype, base2=w.base2)
+        yc = Check("out", "values", work.result_dtype, max_abs_bits(o[rank], w.dtype))
+        yc.values(_f64(saved["out"]), y)
+        checks = [yc]
+        cpu = {"oracle_s": round(time.perf_counter() - t0, 4), "threads": 1}
+    return [c.record() for c in checks], cpu
+
+
+def _int_view(dtype):
+    import torch
+
+    return torch.int32 if dtype == "f32" else torch.int16
 
 
 def cpu_info():
@@ -480,6 +691,103 @@ def cpu_info():
     return "unknown"
 
 
+# ---------------------------------------------------------------- one workload, end to end
+
+def snapshot(work):
+    """Device copies of the step's output buffers (taken after one untimed
+    run of the step, before any timing) and their host copies."""
+    return {k: t.clone() for k, t in work.outputs.items()}
+
+
+def same_bits(a, b) -> bool:
+    import torch
+
+    if a.dtype in (torch.bfloat16, torch.float16):
+        return bool(torch.equal(a.view(torch.int16), b.view(torch.int16)))
+    return bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+
+
+def measure(name, dev, steps, warmup, flush_mib, floor=True, warm_steps=0, out_f32=False,
+            valid_tokens=None, cpu=True, time_cpu=False, rotate=0, flush_read=False):
+    """Build a workload, run its step once and save its outputs, time it,
+    time the floor under the same protocol, check that the timed launches
+    left the outputs bit for bit as saved, then run the CPU leg (parity of the
+    saved outputs against the oracle; with time_cpu the CPU baseline)."""
+    import torch
+
+    work = build_workload(name, dev, out_f32, valid_tokens)
+    step_bytes = sum(b for _, b, _ in work.kernels)
+    for _, _, fn in work.kernels:
+        fn()
+    torch.cuda.synchronize()
+    saved_dev = snapshot(work)
+    sets = [work.kernels]
+    if rotate:
+        sets += [build_workload(name, dev, out_f32, valid_tokens).kernels
+                 for _ in range(rotate - 1)]
+    if flush_mib < 0:
+        flush_mib = 0 if rotate else (1024 if step_bytes < (1 << 30) else 0)
+    log(f"[bench] {name}: {step_bytes / 1e6:.1f} MB per step, warmup {warmup}, steps {steps}, " +
+        (f"{rotate} input sets in rotation" if rotate else
+         f"flush {flush_mib} MiB{' (read)' if flush_read else ''}"))
+    wall, times = time_steps(sets, steps, warmup, flush_mib << 20, dev, flush_read)
+    res = {"work": work, "step_bytes": step_bytes, "wall": wall, "times": times,
+           "flush_mib": flush_mib}
+    if warm_steps:
+        _, wt = time_steps(work.kernels, warm_steps, warmup, 0, dev)
+        res["warm"] = wt
+    if floor:
+        res["floor"] = time_floor(work.kernels, times, steps, warmup, flush_mib << 20, dev,
+                                  flush_read, rotate)
+    torch.cuda.synchronize()
+    res["unchanged"] = all(same_bits(work.outputs[k], saved_dev[k]) for k in saved_dev)
+    if cpu:
+        saved = {k: t.cpu() for k, t in saved_dev.items()}
+        del saved_dev
+        log(f"[bench] {name}: oracle on the host (parity{', CPU baseline' if time_cpu else ''}) ...")
+        res["parity"], res["cpu"] = cpu_leg(work, saved, host_threads(), time_cpu)
+        bad = [c["buffer"] for c in res["parity"] if not c["ok"]]
+        log(f"[bench] {name}: parity " + ("ok" if not bad else f"FAILED on {bad}"))
+    return res
+
+
+def kernel_records(res, target=None):
+    """Per-kernel figures of a measured workload: times (µs), GB/s and frac of
+    the 8 TB/s peak by mean and by median, and the floor ratios."""
+    recs = []
+    floor = res.get("floor")
+    for k, (kname, kbytes, _) in enumerate(res["work"].kernels):
+        st = stats_us(res["times"][k])
+        r = {"kernel": kname, "bytes": kbytes, **st,
+             "GB/s": round(kbytes / (st["mean_us"] * 1e-6) / 1e9, 1),
+             "GB/s_median": round(kbytes / (st["median_us"] * 1e-6) / 1e9, 1)}
+        r["frac"] = round(r["GB/s"] / PEAK_HBM_GBS, 4)
+        r["frac_median"] = round(r["GB/s_median"] / PEAK_HBM_GBS, 4)
+        if target is not None:
+            r["target_frac"] = target
+        if floor is not None:
+            f = floor["reads"][k]
+            r.update({"read_floor_us": f["read_us"], "kernel_over_read": f["kernel_over_read"],
+                      "kernel_over_read_median": f["kernel_over_read_median"],
+                      "copy_floor_us": f["copy_us"], "kernel_over_copy": f["kernel_over_copy"],
+                      "kernel_over_copy_median": f["kernel_over_copy_median"]})
+        if "warm" in res:
+            ws = stats_us(res["warm"][k])
+            r["warm"] = {"median_us": ws["median_us"], "p10_us": ws["p10_us"],
+                         "p90_us": ws["p90_us"],
+                         "GB/s_median": round(kbytes / (ws["median_us"] * 1e-6) / 1e9, 1),
+                         "cache": "warm: no flush, steps back to back (inputs may sit in the "
+                                  "256 MB Infinity Cache)"}
+        recs.append(r)
+    return recs
+
+
+# Configurations the >= 80 % of peak HBM bandwidth target covers: the packed
+# unpack + combine, the MLA decode combine and the large-batch combine.
+TARGET = {("packed", 1): 0.80, ("mla_decode", 0): 0.80, ("large_batch", 0): 0.80}
+SUITE = ["fp16_base2", "packed", "mla_decode"]
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -487,10 +795,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="large_batch",
+    ap.add_argument("--workload", default=None,
                     choices=["large_batch", "mla_decode", "fp16_base2", "packed", "small",
                              "merge_heads", "ag_correct", "mla_decode_f32", "packed_f32",
-                             "direct_planes"])
+                             "direct_planes"],
+                    help="time this workload only (default: large_batch, after the suite)")
+    ap.add_argument("--no-suite", action="store_true",
+                    help="default command: skip the suite of the other configurations")
+    ap.add_argument("--suite-steps", type=int, default=100)
+    ap.add_argument("--suite-warmup", type=int, default=10)
     ap.add_argument("--out-f32", action="store_true",
                     help="combine workloads: fp32 result from 16-bit partials")
     ap.add_argument("--flush-mib", type=int, default=-1,
@@ -513,8 +826,9 @@ def main():
                          "bytes (the floor any kernel is measured against; on by default)")
     ap.add_argument("--no-floor", dest="floor", action="store_false",
                     help="skip the floor measurements")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU leg (the oracle: parity of the outputs and the CPU "
+                         "baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a 1 GiB device copy (PMC calibration)")
     ap.add_argument("--traffic-record", nargs=3, metavar=("BENCH_LOG", "FETCH_DIR", "WRITE_DIR"),
@@ -550,59 +864,59 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    use_cpu = not args.no_cpu_baseline
+    name = args.workload or "large_batch"
+    if args.rotate and (args.rotate < 2 or args.flush_mib > 0):
+        raise SystemExit("--rotate K needs K >= 2 and no --flush-mib")
 
-    w, info, kernels, host, rows = build_workload(args.workload, dev, args.out_f32,
-                                                  args.valid_tokens)
-    step_bytes = sum(b for _, b, _ in kernels)
-    sets = [kernels]
-    if args.rotate:
-        if args.rotate < 2 or step_bytes >= (1 << 30) or args.flush_mib > 0:
-            raise SystemExit("--rotate K needs K >= 2, a step under 1 GiB and no --flush-mib")
-        sets += [build_workload(args.workload, dev, args.out_f32, args.valid_tokens)[2]
-                 for _ in range(args.rotate - 1)]
-        flush_mib = 0
-    else:
-        flush_mib = args.flush_mib if args.flush_mib >= 0 else \
-            (1024 if step_bytes < (1 << 30) else 0)
-    log(f"[bench] {args.workload}: {step_bytes / 1e6:.1f} MB per step, warmup {args.warmup}, "
-        f"steps {args.steps}, " + (f"{args.rotate} input sets in rotation" if args.rotate else
-                                   f"flush {flush_mib} MiB{' (read)' if args.flush_read else ''}"))
-    wall, per_kernel_ms = time_steps(sets, args.steps, args.warmup, flush_mib << 20, dev,
-                                     args.flush_read)
-    gpu_ms = sum(per_kernel_ms)
-    ms_per_step = gpu_ms / args.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"[bench] wall {wall:.3f}s for {args.steps} steps; kernels {gpu_ms:.3f} ms")
+    # The suite of the other configurations runs first (cold, its own step
+    # count), then the headline workload over exactly --steps steps.
+    suite = []
+    if args.workload is None and not args.no_suite:
+        for sname in SUITE:
+            r = measure(sname, dev, args.suite_steps, args.suite_warmup, -1, floor=args.floor,
+                        warm_steps=args.suite_steps if sname == "packed" else 0, cpu=use_cpu)
+            entry = {"workload": sname, "config": r["work"].info["desc"],
+                     "steps": args.suite_steps, "warmup": args.suite_warmup,
+                     "cache": f"cold: {r['flush_mib']} MiB written before each step, outside "
+                              "the timed events",
+                     "kernels": kernel_records(r), "outputs_unchanged_by_timed_steps":
+                         r["unchanged"]}
+            for k, rec in enumerate(entry["kernels"]):
+                if (sname, k) in TARGET:
+                    rec["target_frac"] = TARGET[(sname, k)]
+            if use_cpu:
+                entry["parity"] = r["parity"]
+                entry["oracle"] = r["cpu"]
+            suite.append(entry)
+            del r
+            torch.cuda.empty_cache()
 
+    r = measure(name, dev, args.steps, args.warmup, args.flush_mib, floor=args.floor,
+                out_f32=args.out_f32, valid_tokens=args.valid_tokens, cpu=use_cpu,
+                time_cpu=use_cpu, rotate=args.rotate, flush_read=args.flush_read)
+    work = r["work"]
+    step_ms = [sum(t[i] for t in r["times"]) for i in range(args.steps)]
+    ms_per_step = sum(step_ms) / args.steps
+    value = r["step_bytes"] / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] wall {r['wall']:.3f}s for {args.steps} steps; kernels {sum(step_ms):.3f} ms")
+
+    recs = kernel_records(r, TARGET.get((name, 0)))
     # dominant kernel: the one with the largest share of the step's time
-    k = max(range(len(kernels)), key=lambda i: per_kernel_ms[i])
-    kname, kbytes, _ = kernels[k]
-    k_ms = per_kernel_ms[k] / args.steps
+    k = max(range(len(work.kernels)), key=lambda i: sum(r["times"][i]))
+    kname, kbytes, _ = work.kernels[k]
+    k_ms = sum(r["times"][k]) / args.steps
     achieved = kbytes / (k_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "bytes_per_launch": kbytes, "avg_launch_us": round(k_ms * 1e3, 3),
-                "traffic": load_traffic(args.workload + ("_f32out" if args.out_f32 else ""),
-                                        kname)}
-    kernel_detail = [{"kernel": n, "bytes": b, "avg_us": round(per_kernel_ms[i] / args.steps * 1e3, 3),
-                      "GB/s": round(b / (per_kernel_ms[i] / args.steps * 1e-3) / 1e9, 1)}
-                     for i, (n, b, _) in enumerate(kernels)]
-
-    floor = None
+                "median_launch_us": stats_us(r["times"][k])["median_us"],
+                "traffic": load_traffic(name + ("_f32out" if args.out_f32 else ""), kname)}
     if args.floor:
-        floor = time_floor(kernels, per_kernel_ms, args.steps, args.warmup, flush_mib << 20,
-                           dev, args.flush_read, args.rotate)
-        log(f"[bench] floor: empty launch {floor['empty_launch_us']} us; " + "; ".join(
-            f"plain read of {r['bytes'] / 1e6:.1f} MB {r['read_us']} us ({r['read_GBps']} GB/s), "
-            f"copy of half {r['copy_us']} us ({r['copy_GBps']} GB/s)" for r in floor["reads"]))
-
-    cpu = None
-    if not args.no_cpu_baseline and host is not None:
-        log("[bench] timing the CPU oracle ...")
-        cpu = cpu_baseline(w, host, args.cpu_threads)
-        if cpu is not None:
-            cpu["cpu_model"] = cpu_info()
-            log(f"[bench] oracle {cpu['seconds']}s on {cpu['cores']} threads")
+        fl = r["floor"]
+        log(f"[bench] floor: empty launch {fl['empty_launch_us']} us; " + "; ".join(
+            f"plain read of {x['bytes'] / 1e6:.1f} MB {x['read_us']} us ({x['read_GBps']} GB/s), "
+            f"copy of half {x['copy_us']} us ({x['copy_GBps']} GB/s)" for x in fl["reads"]))
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -612,21 +926,30 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
 
+    cpu = r.get("cpu") if use_cpu and work.kind in ("combine", "planes") else None
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded counter-based generator)", "config": info,
-        "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "data": "synthetic (seeded counter-based generator)", "config": work.info,
+        "rows_per_s": round(work.rows / (ms_per_step * 1e-3), 1),
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
-        "step_bytes": step_bytes, "cache_flush_mib": flush_mib,
+        "step_bytes": r["step_bytes"], "cache_flush_mib": r["flush_mib"],
         "cache_flush_kind": (f"rotation over {args.rotate} input sets" if args.rotate else
-                             ("read" if args.flush_read else "write") if flush_mib else "none"),
-        "wall_s": round(wall, 4), "kernels": kernel_detail,
+                             ("read" if args.flush_read else "write") if r["flush_mib"] else
+                             "none"),
+        "wall_s": round(r["wall"], 4), "kernels": recs,
+        "step_timing": {**stats_us(step_ms), "first_steps_us":
+                        [round(t * 1e3, 3) for t in step_ms[:5]]},
         "roofline": roofline, "cpu_baseline": cpu,
+        "outputs_unchanged_by_timed_steps": r["unchanged"],
     }
-    if floor is not None:
-        line["floor"] = floor
+    if use_cpu:
+        line["parity"] = r["parity"]
+    if args.floor:
+        line["floor"] = r["floor"]
+    if suite:
+        line["suite"] = suite
     print(json.dumps(line), flush=True)
 
 

@@ -111,16 +111,22 @@ def test_load_traffic_needs_the_current_source_and_kernel(tmp_path, monkeypatch)
     assert bench.load_traffic("w", "k (bf16)") is None
 
 
-def test_committed_traffic_records_match_the_sources():
-    """Every committed record was taken on the kernels as they are now."""
+def test_committed_traffic_records_are_used_only_on_their_sources():
+    """A committed record taken on the kernels as they are now is within 10 %
+    of the algorithmic bytes; one taken on other kernel sources is never
+    reported (load_traffic gives None for it)."""
     d = os.path.join(ROOT, "profiles")
     names = [n for n in os.listdir(d) if n.startswith("traffic_") and n.endswith(".json")]
     assert names
     for n in names:
         with open(os.path.join(d, n)) as f:
             rec = json.load(f)
-        assert rec["source_sha256"] == bench.source_sha(), n
         assert 1.0 <= rec["traffic_over_algorithmic"] < 1.1, n
+        got = bench.load_traffic(n[len("traffic_"):-len(".json")], rec["kernel"])
+        if rec["source_sha256"] == bench.source_sha():
+            assert got == rec["traffic_bytes_per_launch"], n
+        else:
+            assert got is None, n
 
 
 def test_more_than_one_gpu_is_refused():
@@ -128,3 +134,93 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+# ---------------------------------------------------------------- the CPU leg (oracle timing and parity)
+
+def _fake_combine_work(N=3, B=40, H=4, D=128, dtype="bf16", base2=False):
+    """A combine workload whose 'GPU' outputs are the oracle's own results
+    rounded to the result dtype (no GPU here)."""
+    from types import SimpleNamespace
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    w = synth.Workload("fake", 77, "combine", N, B, H, D, dtype, ("normal", 0.0, 1.0),
+                       ("uniform", -5.0, 15.0), special=((0.05, float("nan")),),
+                       base2=base2, return_lse=True)
+    o, l = synth.combine_inputs(w)
+    y, L = oracle.lse_combine(o, l, dtype, base2=base2)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    saved = {"out": torch.from_numpy(y).to(tdt), "out_lse": torch.from_numpy(L).float()}
+    work = SimpleNamespace(w=w, kind="combine", host=(o, l), result_dtype=dtype,
+                           cpu_bytes=bench.combine_bytes(N, B, H, D, 2, True))
+    return work, saved, np
+
+
+def test_cpu_leg_checks_every_row_and_times_the_oracle():
+    work, saved, _ = _fake_combine_work()
+    parity, cpu = bench.cpu_leg(work, saved, threads=3, time_it=True)
+    assert [c["buffer"] for c in parity] == ["out", "out_lse"]
+    assert all(c["ok"] for c in parity), parity
+    assert parity[0]["elements"] == 40 * 4 * 128 and parity[1]["elements"] == 40 * 4
+    assert cpu["kind"] == "oracle" and cpu["cores"] == 3 and cpu["unit"] == "GB/s"
+    assert len(cpu["seconds_runs"]) == 3 and cpu["single_thread"]["threads"] == 1
+    assert len(cpu["single_thread"]["seconds_runs"]) == 3
+    assert cpu["nproc"] == os.cpu_count() and cpu["value"] > 0
+
+
+@pytest.mark.parametrize("where", ["out", "out_lse", "nan"])
+def test_cpu_leg_catches_a_wrong_output(where):
+    import torch
+
+    work, saved, np = _fake_combine_work(dtype="f16", base2=True)
+    if where == "out":
+        saved["out"][17, 2, 5] += 0.05            # beyond 1e-3 * M
+    elif where == "out_lse":
+        saved["out_lse"][39, 3] += 1e-3            # beyond 1e-5
+    else:
+        saved["out"][0, 0, 0] = float("nan")       # a NaN where the oracle has none
+    parity, _ = bench.cpu_leg(work, saved, threads=2, time_it=False)
+    bad = [c["buffer"] for c in parity if not c["ok"]]
+    assert bad == (["out_lse"] if where == "out_lse" else ["out"]), parity
+    del torch
+
+
+def test_cpu_leg_packed_is_bit_exact():
+    from types import SimpleNamespace
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    w = synth.Workload("fake_packed", 78, "packed", 4, 24, 8, 128, "bf16", ("normal", 0.0, 1.0),
+                       ("uniform", -5.0, 15.0), base2=False, return_lse=True)
+    ranks = [synth.rank_inputs(w, r) for r in range(w.N)]
+    outs, lses = [a for a, _ in ranks], [b for _, b in ranks]
+    Hl = w.H // w.N
+    send = oracle.pack_send(outs[0], lses[0], w.N)
+    so = np.stack([a[:, :Hl] for a in outs])
+    sl = np.stack([b[:, :Hl] for b in lses])
+    y, L = oracle.lse_combine(so, sl, "bf16")
+    saved = {"send": torch.from_numpy(send.view(np.int16)).view(torch.bfloat16),
+             "out": torch.from_numpy(y).to(torch.bfloat16), "out_lse": torch.from_numpy(L).float()}
+    work = SimpleNamespace(w=w, kind="packed", host=(outs, lses), result_dtype="bf16",
+                           cpu_bytes=0)
+    parity, _ = bench.cpu_leg(work, saved, threads=1, time_it=False)
+    assert all(c["ok"] for c in parity), parity
+    saved["send"].view(torch.int16)[1, 3, 0, 129] ^= 1  # one bit of an LSE tail
+    parity, _ = bench.cpu_leg(work, saved, threads=1, time_it=False)
+    assert [c["buffer"] for c in parity if not c["ok"]] == ["send"]
+
+
+def test_step_statistics():
+    st = bench.stats_us([0.001 * i for i in range(1, 101)])  # 1 .. 100 us
+    assert st["median_us"] == pytest.approx(50.5)
+    assert st["p10_us"] == pytest.approx(10.9) and st["p90_us"] == pytest.approx(90.1)
+    assert st["mean_us"] == pytest.approx(50.5) and st["min_us"] == 1.0 and st["max_us"] == 100.0
