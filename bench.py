@@ -352,16 +352,25 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
 
 # ---------------------------------------------------------------- timing
 
-def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
+def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False, dispatch=True):
     """Time `steps` steps after `warmup`. With flush_bytes, a buffer of that
     size is rewritten (or, with flush_read, summed) before each step, outside
     the timed events, so the step's inputs come from HBM. `kernels` is one
     step's list of (name, bytes, fn), or a list of such lists (input sets that
     hold the same work in different memory): step i then runs set i mod the
-    number of sets. Returns the wall time of the timed loop and, per kernel,
-    the list of its launch times in ms (HIP events on the current stream,
-    the one the kernels are launched on)."""
+    number of sets. Every fn makes one library call, which launches one kernel.
+
+    Returns the wall time of the timed loop and, per kernel, two lists of
+    launch times in ms: by HIP events recorded around each launch on the
+    current stream (the one the kernels are launched on), which include the
+    event markers' own time; and, with `dispatch`, by the kernel's own
+    dispatch (lsec_time_next_launch: events that the launch itself records),
+    the kernel's duration as a kernel trace reports it (else None). Timing
+    the dispatch adds work to the stream around each launch, so the marker
+    times of a dispatch-timed loop are not those of plain launches."""
     import torch
+
+    import lse_weighted_merge_combine_amd as lsec
 
     sets = kernels if kernels and isinstance(kernels[0], list) else [kernels]
     flush = torch.ones(max(flush_bytes // 4, 1), dtype=torch.float32, device=dev) \
@@ -372,6 +381,7 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
     torch.cuda.synchronize()
     nk = len(sets[0])
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    timer = lsec.LaunchTimer(steps * nk) if dispatch else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if flush is None and sum(b for _, b, _ in sets[0]) < (1 << 30):
@@ -389,12 +399,18 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False):
                 flush.fill_(float(i))
         ev[i][0].record()
         for k, (_, _, fn) in enumerate(sets[i % len(sets)]):
+            if timer is not None:
+                timer.arm(i * nk + k)
             fn()
             ev[i][k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     times = [[ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(steps)] for k in range(nk)]
-    return wall, times
+    ktimes = None
+    if timer is not None:
+        ktimes = [[timer.elapsed_ms(i * nk + k) for i in range(steps)] for k in range(nk)]
+        timer.close()
+    return wall, times, ktimes
 
 
 def stats_us(ms):
@@ -408,23 +424,23 @@ def stats_us(ms):
             "min_us": round(float(a.min()), 3), "max_us": round(float(a.max()), 3)}
 
 
-def time_floor(kernels, times, steps, warmup, flush_bytes, dev, flush_read=False, rotate=0):
+def time_floor(kernels, ktimes, steps, warmup, flush_bytes, dev, flush_read=False, rotate=0):
     """Time the measurement aids under the protocol of the workload's steps:
     an empty launch (one wave), and for each of the step's kernels a plain
     streaming read of as many bytes as that kernel moves (rounded down to 16)
     and a plain copy of half of them (as many bytes read as written), from
     buffers of their own. Each kernel's time per launch is reported as a
-    multiple of both (means; medians too): the read bounds the combining
-    kernels, the copy the pack and the corrected partial. With `rotate` the
-    reads and copies cycle through that many buffers, as the steps cycle
-    through their input sets."""
+    multiple of both (means and medians of the kernels' own dispatch times,
+    on both sides): the read bounds the combining kernels, the copy the pack
+    and the corrected partial. With `rotate` the reads and copies cycle
+    through that many buffers, as the steps cycle through their input sets."""
     import numpy as np
     import torch
 
     import lse_weighted_merge_combine_amd as lsec
 
-    _, e_ms = time_steps([("empty", 0, lambda: lsec.lsec_floor_empty(dev))], steps, warmup,
-                         flush_bytes, dev, flush_read)
+    _, _, e_ms = time_steps([("empty", 0, lambda: lsec.lsec_floor_empty(dev))], steps, warmup,
+                            flush_bytes, dev, flush_read)
     reads = []
     n_sets = max(rotate, 1)
     for k, (name, nbytes, _) in enumerate(kernels):
@@ -432,18 +448,18 @@ def time_floor(kernels, times, steps, warmup, flush_bytes, dev, flush_read=False
         bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(n_sets)]
         sink = torch.empty(max(lsec.load_library().lsec_floor_read_blocks(nbytes), 1),
                            dtype=torch.int32, device=dev)
-        _, r_ms = time_steps([[("read", nbytes, lambda b=b: lsec.lsec_floor_read(b, sink))]
-                              for b in bufs], steps, warmup, flush_bytes, dev, flush_read)
+        _, _, r_ms = time_steps([[("read", nbytes, lambda b=b: lsec.lsec_floor_read(b, sink))]
+                                 for b in bufs], steps, warmup, flush_bytes, dev, flush_read)
         del bufs, sink
         half = (nbytes // 2) - (nbytes // 2) % 16
         pairs = [(torch.ones(half // 4, dtype=torch.int32, device=dev),
                   torch.empty(half // 4, dtype=torch.int32, device=dev)) for _ in range(n_sets)]
-        _, c_ms = time_steps([[("copy", 2 * half, lambda a=a, c=c: lsec.lsec_floor_copy(a, c))]
-                              for a, c in pairs], steps, warmup, flush_bytes, dev, flush_read)
+        _, _, c_ms = time_steps([[("copy", 2 * half, lambda a=a, c=c: lsec.lsec_floor_copy(a, c))]
+                                 for a, c in pairs], steps, warmup, flush_bytes, dev, flush_read)
         del pairs
         read_ms, copy_ms = float(np.mean(r_ms[0])), float(np.mean(c_ms[0]))
         read_med, copy_med = float(np.median(r_ms[0])), float(np.median(c_ms[0]))
-        kernel_ms_k, kernel_med = float(np.mean(times[k])), float(np.median(times[k]))
+        kernel_ms_k, kernel_med = float(np.mean(ktimes[k])), float(np.median(ktimes[k]))
         reads.append({"kernel": name, "bytes": nbytes, "read_us": round(read_ms * 1e3, 3),
                       "read_median_us": round(read_med * 1e3, 3),
                       "read_GBps": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
@@ -456,7 +472,8 @@ def time_floor(kernels, times, steps, warmup, flush_bytes, dev, flush_read=False
                       "kernel_over_copy_median": round(kernel_med / copy_med, 3)})
     return {"empty_launch_us": round(float(np.mean(e_ms[0])) * 1e3, 3), "reads": reads,
             "kernels": ["floor_empty_kernel", "floor_read_kernel", "floor_copy_kernel"],
-            "timing": "HIP events, same flush protocol as the steps"}
+            "timing": "the kernels' own dispatch times (lsec_time_next_launch), the same flush "
+                      "protocol as the steps"}
 
 
 # ---------------------------------------------------------------- CPU leg: oracle timing and parity
@@ -708,11 +725,18 @@ def same_bits(a, b) -> bool:
 
 
 def measure(name, dev, steps, warmup, flush_mib, floor=True, warm_steps=0, out_f32=False,
-            valid_tokens=None, cpu=True, time_cpu=False, rotate=0, flush_read=False):
+            valid_tokens=None, cpu=True, time_cpu=False, rotate=0, flush_read=False,
+            plain=False):
     """Build a workload, run its step once and save its outputs, time it,
     time the floor under the same protocol, check that the timed launches
     left the outputs bit for bit as saved, then run the CPU leg (parity of the
-    saved outputs against the oracle; with time_cpu the CPU baseline)."""
+    saved outputs against the oracle; with time_cpu the CPU baseline).
+
+    Kernel figures come from the kernels' own dispatch times. With `plain`,
+    the steps are first timed with plain launches and events around each
+    step (the timed region of the headline: `steps` steps after `warmup`),
+    then the kernels' dispatch times are taken over another `steps` launches
+    of the same steps."""
     import torch
 
     work = build_workload(name, dev, out_f32, valid_tokens)
@@ -730,14 +754,20 @@ def measure(name, dev, steps, warmup, flush_mib, floor=True, warm_steps=0, out_f
     log(f"[bench] {name}: {step_bytes / 1e6:.1f} MB per step, warmup {warmup}, steps {steps}, " +
         (f"{rotate} input sets in rotation" if rotate else
          f"flush {flush_mib} MiB{' (read)' if flush_read else ''}"))
-    wall, times = time_steps(sets, steps, warmup, flush_mib << 20, dev, flush_read)
-    res = {"work": work, "step_bytes": step_bytes, "wall": wall, "times": times,
-           "flush_mib": flush_mib}
+    res = {"work": work, "step_bytes": step_bytes, "flush_mib": flush_mib}
+    if plain:
+        res["wall"], res["times"], _ = time_steps(sets, steps, warmup, flush_mib << 20, dev,
+                                                  flush_read, dispatch=False)
+    wall, times, ktimes = time_steps(sets, steps, 0 if plain else warmup, flush_mib << 20, dev,
+                                     flush_read)
+    res["ktimes"] = ktimes
+    if not plain:
+        res["wall"], res["times"] = wall, times
     if warm_steps:
-        _, wt = time_steps(work.kernels, warm_steps, warmup, 0, dev)
+        _, _, wt = time_steps(work.kernels, warm_steps, warmup, 0, dev)
         res["warm"] = wt
     if floor:
-        res["floor"] = time_floor(work.kernels, times, steps, warmup, flush_mib << 20, dev,
+        res["floor"] = time_floor(work.kernels, ktimes, steps, warmup, flush_mib << 20, dev,
                                   flush_read, rotate)
     torch.cuda.synchronize()
     res["unchanged"] = all(same_bits(work.outputs[k], saved_dev[k]) for k in saved_dev)
@@ -752,12 +782,14 @@ def measure(name, dev, steps, warmup, flush_mib, floor=True, warm_steps=0, out_f
 
 
 def kernel_records(res, target=None):
-    """Per-kernel figures of a measured workload: times (µs), GB/s and frac of
-    the 8 TB/s peak by mean and by median, and the floor ratios."""
+    """Per-kernel figures of a measured workload: the kernel's own dispatch
+    times (µs: mean, median, p10, p90, min, max), GB/s and frac of the 8 TB/s
+    peak by mean and by median, the floor ratios, and the mean and median of
+    the same launches timed by event markers around them."""
     recs = []
     floor = res.get("floor")
     for k, (kname, kbytes, _) in enumerate(res["work"].kernels):
-        st = stats_us(res["times"][k])
+        st = stats_us(res["ktimes"][k])
         r = {"kernel": kname, "bytes": kbytes, **st,
              "GB/s": round(kbytes / (st["mean_us"] * 1e-6) / 1e9, 1),
              "GB/s_median": round(kbytes / (st["median_us"] * 1e-6) / 1e9, 1)}
@@ -765,6 +797,7 @@ def kernel_records(res, target=None):
         r["frac_median"] = round(r["GB/s_median"] / PEAK_HBM_GBS, 4)
         if target is not None:
             r["target_frac"] = target
+        r["timing"] = "the kernel's own dispatch (lsec_time_next_launch)"
         if floor is not None:
             f = floor["reads"][k]
             r.update({"read_floor_us": f["read_us"], "kernel_over_read": f["kernel_over_read"],
@@ -894,7 +927,7 @@ def main():
 
     r = measure(name, dev, args.steps, args.warmup, args.flush_mib, floor=args.floor,
                 out_f32=args.out_f32, valid_tokens=args.valid_tokens, cpu=use_cpu,
-                time_cpu=use_cpu, rotate=args.rotate, flush_read=args.flush_read)
+                time_cpu=use_cpu, rotate=args.rotate, flush_read=args.flush_read, plain=True)
     work = r["work"]
     step_ms = [sum(t[i] for t in r["times"]) for i in range(args.steps)]
     ms_per_step = sum(step_ms) / args.steps
@@ -902,15 +935,21 @@ def main():
     log(f"[bench] wall {r['wall']:.3f}s for {args.steps} steps; kernels {sum(step_ms):.3f} ms")
 
     recs = kernel_records(r, TARGET.get((name, 0)))
-    # dominant kernel: the one with the largest share of the step's time
-    k = max(range(len(work.kernels)), key=lambda i: sum(r["times"][i]))
+    # dominant kernel: the one with the largest share of the step's time; its
+    # launch duration is the kernel's own dispatch time (events the launch
+    # itself records, as a kernel trace reports it)
+    k = max(range(len(work.kernels)), key=lambda i: sum(r["ktimes"][i]))
     kname, kbytes, _ = work.kernels[k]
-    k_ms = sum(r["times"][k]) / args.steps
+    k_ms = sum(r["ktimes"][k]) / args.steps
     achieved = kbytes / (k_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "bytes_per_launch": kbytes, "avg_launch_us": round(k_ms * 1e3, 3),
-                "median_launch_us": stats_us(r["times"][k])["median_us"],
+                "median_launch_us": stats_us(r["ktimes"][k])["median_us"],
+                "launch_timing": "HIP events recorded by the kernel's own dispatch on the stream "
+                                 "it runs on (lsec_time_next_launch), over --steps launches after "
+                                 "the timed region; value and ms_per_step come from events around "
+                                 "each of the timed region's plain launches",
                 "traffic": load_traffic(name + ("_f32out" if args.out_f32 else ""), kname)}
     if args.floor:
         fl = r["floor"]
@@ -940,7 +979,9 @@ def main():
                              "none"),
         "wall_s": round(r["wall"], 4), "kernels": recs,
         "step_timing": {**stats_us(step_ms), "first_steps_us":
-                        [round(t * 1e3, 3) for t in step_ms[:5]]},
+                        [round(t * 1e3, 3) for t in step_ms[:5]],
+                        "timing": "HIP events around each step of the timed region (plain "
+                                  "launches)"},
         "roofline": roofline, "cpu_baseline": cpu,
         "outputs_unchanged_by_timed_steps": r["unchanged"],
     }

@@ -11,7 +11,11 @@
  *                       arithmetic, no layout and (almost) no writes;
  *  - lsec_floor_copy  : a plain copy with those loads and 16-byte
  *                       non-temporal stores, the same for calls that write as
- *                       much as they read (pack, unpack, corrected partial).
+ *                       much as they read (pack, unpack, corrected partial);
+ *  - lsec_time_next_launch : times the next kernel the library launches from
+ *                       the calling thread by its own dispatch, so that a
+ *                       caller can time single short launches without the
+ *                       cost of separate event markers around them.
  * A combining call that moves b bytes cannot finish faster than a plain read
  * of b bytes, a call that reads and writes b / 2 bytes each not faster than
  * a plain copy of b / 2 bytes, and no call faster than an empty launch; for
@@ -29,6 +33,24 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/*
+ * lsec_time_next_launch -- arm a pair of events for the next kernel that this
+ * library launches from the calling thread (any entry point of lsec.h or of
+ * this header; each launches exactly one kernel). That launch records its
+ * kernel's start in `start` and its end in `stop`, taken from the kernel's own
+ * dispatch (hipExtLaunchKernelGGL), so hipEventElapsedTime(start, stop) is
+ * the kernel's duration without the time of event markers recorded around
+ * it; the pair is then disarmed. Later launches are plain launches again.
+ *   start, stop : hipEvent_t handles the caller created (hipEventCreate) on
+ *                 the device of the next launch; both NULL disarms a pair
+ *                 that no launch has taken yet (a call that fails its
+ *                 argument checks launches nothing and leaves it armed)
+ * Not for calls under stream capture. Arming is per thread: a launch from
+ * another thread is never timed by it.
+ * Errors: NULL (exactly one of the two is NULL).
+ */
+int lsec_time_next_launch(void* start, void* stop);
 
 /*
  * lsec_floor_empty -- launch one wave of 64 lanes that returns at once.

@@ -128,6 +128,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_floor_read.argtypes = [P, I64, P, P]
     lib.lsec_floor_copy.restype = I
     lib.lsec_floor_copy.argtypes = [P, P, I64, P]
+    lib.lsec_time_next_launch.restype = I
+    lib.lsec_time_next_launch.argtypes = [P, P]
     _lib = lib
     return lib
 
@@ -585,6 +587,76 @@ def lsec_floor_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
               "lsec_floor_copy")
 
 
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime this process already runs on (torch's; liblsec.so binds
+    to the same copy by its soname), for the event calls of LaunchTimer."""
+    global _hip
+    if _hip is None:
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        hip = ctypes.CDLL(path or "libamdhip64.so.7")
+        hip.hipEventCreate.restype = ctypes.c_int
+        hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        hip.hipEventDestroy.restype = ctypes.c_int
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        hip.hipEventElapsedTime.restype = ctypes.c_int
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        _hip = hip
+    return _hip
+
+
+class LaunchTimer:
+    """Times single launches of the library by the kernels' own dispatch
+    (lsec_time_next_launch): ``arm(i)`` before a call times its kernel into
+    pair i; after a synchronisation ``elapsed_ms(i)`` is that kernel's
+    duration. Events are created on the current device."""
+
+    def __init__(self, pairs: int):
+        hip = _hip_runtime()
+        self._ev = []
+        for _ in range(2 * pairs):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                self.close()
+                raise LsecError("hipEventCreate failed")
+            self._ev.append(e)
+
+    def arm(self, i: int) -> None:
+        _raise_on(load_library().lsec_time_next_launch(self._ev[2 * i], self._ev[2 * i + 1]),
+                  "lsec_time_next_launch")
+
+    def disarm(self) -> None:
+        load_library().lsec_time_next_launch(None, None)
+
+    def elapsed_ms(self, i: int) -> float:
+        ms = ctypes.c_float()
+        rc = _hip_runtime().hipEventElapsedTime(ctypes.byref(ms), self._ev[2 * i],
+                                                self._ev[2 * i + 1])
+        if rc != 0:
+            raise LsecError(f"hipEventElapsedTime failed ({rc}): was pair {i} timed?")
+        return float(ms.value)
+
+    def close(self) -> None:
+        for e in self._ev:
+            _hip_runtime().hipEventDestroy(e)
+        self._ev = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+
 def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev or \
             not t.is_contiguous():
@@ -598,4 +670,5 @@ __all__ = [
     "lsec_combine_planes", "lse_combine", "pack_send", "unpack_combine", "dcp_a2a_lse_reduce",
     "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
     "lsec_floor_empty", "lsec_floor_read", "lsec_floor_copy", "dcp_a2a_send_recv_buffers",
+    "LaunchTimer",
 ]

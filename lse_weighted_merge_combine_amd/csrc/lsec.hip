@@ -535,15 +535,15 @@ void launch_combine_rows(const void* src, const float* lse, int N, uint32_t rows
     const auto* s = static_cast<const typename Elem<DT>::T*>(src);
     if constexpr (DT != LSEC_FP32) {
         if (out_f32) {
-            combine_rows_kernel<DT, NT, PACKED, true><<<blocks, kBlock, 0, st>>>(
-                s, lse, N, rows, make_fastdiv(g), rpb, stride, pl.plane, pl.lse_plane, D, scale,
-                inv_scale, out, out_f32, out_lse, om);
+            launch(combine_rows_kernel<DT, NT, PACKED, true>, dim3(blocks), dim3(kBlock), 0, st,
+                   s, lse, N, rows, make_fastdiv(g), rpb, stride, pl.plane, pl.lse_plane, D,
+                   scale, inv_scale, out, out_f32, out_lse, om);
             return;
         }
     }
-    combine_rows_kernel<DT, NT, PACKED, false><<<blocks, kBlock, 0, st>>>(
-        s, lse, N, rows, make_fastdiv(g), rpb, stride, pl.plane, pl.lse_plane, D, scale,
-        inv_scale, out, out_f32, out_lse, om);
+    launch(combine_rows_kernel<DT, NT, PACKED, false>, dim3(blocks), dim3(kBlock), 0, st, s, lse,
+           N, rows, make_fastdiv(g), rpb, stride, pl.plane, pl.lse_plane, D, scale, inv_scale,
+           out, out_f32, out_lse, om);
 }
 
 template <int DT, bool PACKED>
@@ -633,10 +633,10 @@ void run_combine_dt(const void* src, const float* lse, int64_t N, int64_t rows, 
                                out, out_f32, out_lse, om, st);
     } else {
         const int64_t stride = PACKED ? D + Elem<DT>::kPack : D;
-        combine_elems_kernel<DT, PACKED><<<general_grid(rows * D), kBlock, 0, st>>>(
-            static_cast<const typename Elem<DT>::T*>(src), lse, int(N), rows, stride, pl.plane,
-            pl.lse_plane, D, scale, inv_scale, out, out_f32, out_lse, map_a, map_c, om.valid,
-            int64_t(om.rows_per_token));
+        launch(combine_elems_kernel<DT, PACKED>, dim3(general_grid(rows * D)), dim3(kBlock), 0,
+               st, static_cast<const typename Elem<DT>::T*>(src), lse, int(N), rows, stride,
+               pl.plane, pl.lse_plane, D, scale, inv_scale, out, out_f32, out_lse, map_a, map_c,
+               om.valid, int64_t(om.rows_per_token));
     }
 }
 
@@ -673,9 +673,9 @@ void launch_correct_s(int S, const float* lse, int N, int rank, const void* part
     constexpr uint32_t RPS = kBlock / G;
     const unsigned blocks = (rows + RPS * S - 1) / (RPS * S);
     const auto* p = static_cast<const typename Elem<DT>::T*>(part);
-#define LSEC_CORRECT(SV)                                                             \
-    correct_tiled_kernel<DT, G, SV, SPLIT><<<blocks, kBlock, 0, st>>>(lse, N, rank, p, rows, \
-                                                                     scale, inv_scale, out, out_lse)
+#define LSEC_CORRECT(SV)                                                                     \
+    launch(correct_tiled_kernel<DT, G, SV, SPLIT>, dim3(blocks), dim3(kBlock), 0, st, lse, N, \
+           rank, p, rows, scale, inv_scale, out, out_lse)
     switch (S) {
         case 8: LSEC_CORRECT(8); break;
         case 4: LSEC_CORRECT(4); break;
@@ -690,9 +690,9 @@ void launch_correct(bool tiled, const float* lse, int64_t N, int64_t rank, const
                     int64_t rows, int64_t D, float scale, float inv_scale, void* out,
                     int out_f32, float* out_lse, hipStream_t st) {
     if (!tiled) {
-        correct_elems_kernel<DT><<<general_grid(rows * D), kBlock, 0, st>>>(
-            lse, int(N), int(rank), static_cast<const typename Elem<DT>::T*>(part), rows, D,
-            scale, inv_scale, out, out_f32, out_lse);
+        launch(correct_elems_kernel<DT>, dim3(general_grid(rows * D)), dim3(kBlock), 0, st, lse,
+               int(N), int(rank), static_cast<const typename Elem<DT>::T*>(part), rows, D, scale,
+               inv_scale, out, out_f32, out_lse);
         return;
     }
     constexpr int E = Elem<DT>::kEpc;
@@ -728,19 +728,16 @@ void launch_pack(bool fast, const void* attn_out, const float* lse, int64_t B, i
         const uint32_t rpb = kBlock / g;
         const unsigned blocks = unsigned((rows + rpb * kPackRows - 1) / (rpb * kPackRows));
         if (aligned(send, 16))
-            pack_lds_kernel<T><<<blocks, kBlock, 0, st>>>(in, lse, uint32_t(rows), make_fastdiv(g),
-                                                          rpb, make_fastdiv(uint32_t(Hl)),
-                                                          make_fastdiv(uint32_t(B)), uint32_t(H),
-                                                          int(D), dst);
+            launch(pack_lds_kernel<T>, dim3(blocks), dim3(kBlock), 0, st, in, lse, uint32_t(rows),
+                   make_fastdiv(g), rpb, make_fastdiv(uint32_t(Hl)), make_fastdiv(uint32_t(B)),
+                   uint32_t(H), int(D), dst);
         else
-            pack_rows_kernel<T><<<blocks, kBlock, 0, st>>>(in, lse, uint32_t(rows),
-                                                           make_fastdiv(g), rpb,
-                                                           make_fastdiv(uint32_t(Hl)),
-                                                           make_fastdiv(uint32_t(B)), uint32_t(H),
-                                                           int(D), dst);
+            launch(pack_rows_kernel<T>, dim3(blocks), dim3(kBlock), 0, st, in, lse, uint32_t(rows),
+                   make_fastdiv(g), rpb, make_fastdiv(uint32_t(Hl)), make_fastdiv(uint32_t(B)),
+                   uint32_t(H), int(D), dst);
     } else {
-        pack_elems_kernel<T><<<general_grid(total), kBlock, 0, st>>>(in, lse, B, H, Hl, D, total,
-                                                                      dst);
+        launch(pack_elems_kernel<T>, dim3(general_grid(total)), dim3(kBlock), 0, st, in, lse, B,
+               H, Hl, D, total, dst);
     }
 }
 
@@ -753,11 +750,11 @@ void launch_unpack(bool fast, const void* recv, int64_t total_rows, int64_t D, i
         const uint32_t g = uint32_t(D / (16 / sizeof(T)));
         const uint32_t rpb = kBlock / g;
         const unsigned blocks = unsigned((total_rows + rpb - 1) / rpb);
-        unpack_rows_kernel<T><<<blocks, kBlock, 0, st>>>(src, uint32_t(total_rows),
-                                                         make_fastdiv(g), rpb, int(D), outs, lses);
+        launch(unpack_rows_kernel<T>, dim3(blocks), dim3(kBlock), 0, st, src, uint32_t(total_rows),
+               make_fastdiv(g), rpb, int(D), outs, lses);
     } else {
-        unpack_elems_kernel<T><<<general_grid(total), kBlock, 0, st>>>(src, total_rows, D, outs,
-                                                                        lses);
+        launch(unpack_elems_kernel<T>, dim3(general_grid(total)), dim3(kBlock), 0, st, src,
+               total_rows, D, outs, lses);
     }
 }
 

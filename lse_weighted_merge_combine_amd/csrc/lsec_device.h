@@ -6,6 +6,7 @@
 
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -288,6 +289,33 @@ __device__ __forceinline__ uint32_t xcd_chunked_block(uint32_t bid, uint32_t nbl
     if (bid >= full) return bid;
     const uint32_t xcd = bid % 8, i = bid / 8;
     return ((i / kXcdChunk) * 8 + xcd) * kXcdChunk + i % kXcdChunk;
+}
+
+// ---------------------------------------------------------------- kernel launch
+//
+// Every kernel of the library is launched through launch(): a plain launch on
+// the caller's stream, unless the calling thread has armed a pair of events
+// with the measurement aid lsec_time_next_launch (lsec_floor.h). Then this
+// launch records its kernel's start and end in them (hipExtLaunchKernelGGL,
+// whose timestamps come from the kernel's own dispatch, without separate
+// event markers around it) and the pair is disarmed.
+struct LaunchEvents {
+    hipEvent_t start, stop;
+};
+
+// The armed pair of the calling thread (nulls if none); disarms it.
+// Defined with the measurement aids (lsec_floor.hip).
+LaunchEvents take_launch_events();
+
+template <typename... P, typename... A>
+inline void launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t st,
+                   A... args) {
+    const LaunchEvents ev = take_launch_events();
+    if (ev.start != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(shmem), st, ev.start, ev.stop, 0u,
+                              args...);
+    else
+        kernel<<<grid, block, shmem, st>>>(args...);
 }
 
 // ---------------------------------------------------------------- host interface of the tiled combine

@@ -1,6 +1,7 @@
 // lsec_floor.hip -- measurement aids of liblsec.so (include/lsec_floor.h): an
 // empty launch, a plain streaming read and a plain copy, the reference points
-// the library's kernels are timed against. Not part of the combine.
+// the library's kernels are timed against, and the per-thread events that
+// lsec_time_next_launch arms for the next launch. Not part of the combine.
 //
 // Build with -Xclang -target-feature -Xclang -packed-fp32-ops (as every unit
 // of the library).
@@ -65,16 +66,32 @@ __global__ __launch_bounds__(kBlock) void floor_copy_kernel(const u32x4* __restr
     }
 }
 
+// Events armed by lsec_time_next_launch, per calling thread.
+thread_local LaunchEvents g_armed{nullptr, nullptr};
+
 }  // namespace
+
+LaunchEvents take_launch_events() {
+    const LaunchEvents ev = g_armed;
+    g_armed = LaunchEvents{nullptr, nullptr};
+    return ev;
+}
+
 }  // namespace lsec_detail
 
 using namespace lsec_detail;
 
 extern "C" {
 
+int lsec_time_next_launch(void* start, void* stop) {
+    if ((start == nullptr) != (stop == nullptr)) return LSEC_ERR_NULL;
+    g_armed = LaunchEvents{static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)};
+    return LSEC_OK;
+}
+
 int lsec_floor_empty(void* stream) {
     (void)hipGetLastError();
-    floor_empty_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>();
+    launch(floor_empty_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? LSEC_OK : LSEC_ERR_LAUNCH;
 }
 
@@ -92,8 +109,9 @@ int lsec_floor_read(const void* src, int64_t bytes, uint32_t* sink, void* stream
     if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
         return LSEC_ERR_ALIGNMENT;
     (void)hipGetLastError();
-    floor_read_kernel<<<unsigned(blocks), kBlock, 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const u32x4*>(src), uint64_t(bytes) / 16, sink);
+    launch(floor_read_kernel, dim3(unsigned(blocks)), dim3(kBlock), 0,
+           static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), uint64_t(bytes) / 16,
+           sink);
     return hipGetLastError() == hipSuccess ? LSEC_OK : LSEC_ERR_LAUNCH;
 }
 
@@ -105,8 +123,9 @@ int lsec_floor_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0)
         return LSEC_ERR_ALIGNMENT;
     (void)hipGetLastError();
-    floor_copy_kernel<<<unsigned(blocks), kBlock, 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), uint64_t(bytes) / 16);
+    launch(floor_copy_kernel, dim3(unsigned(blocks)), dim3(kBlock), 0,
+           static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+           static_cast<u32x4*>(dst), uint64_t(bytes) / 16);
     return hipGetLastError() == hipSuccess ? LSEC_OK : LSEC_ERR_LAUNCH;
 }
 

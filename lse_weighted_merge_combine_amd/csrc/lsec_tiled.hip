@@ -309,9 +309,9 @@ void launch_tiled_s(int S, const TiledArgs& a) {
     constexpr uint32_t RPS = kBlock / G;
     const unsigned blocks = (a.rows + RPS * S - 1) / (RPS * S);
 #define LSEC_TILED(SV)                                                                         \
-    combine_tiled_kernel<DT, NT, G, SV, PACKED, SPLIT><<<blocks, kBlock, tiled_lds_cap(SV), a.st>>>( \
-        a.src, a.lse, a.n, a.rows, a.stride, a.plane_bytes, a.lse_plane, a.scale, a.inv_scale,   \
-        a.out, a.out_lse, a.om)
+    launch(combine_tiled_kernel<DT, NT, G, SV, PACKED, SPLIT>, dim3(blocks), dim3(kBlock),      \
+           tiled_lds_cap(SV), a.st, a.src, a.lse, a.n, a.rows, a.stride, a.plane_bytes,          \
+           a.lse_plane, a.scale, a.inv_scale, a.out, a.out_lse, a.om)
     switch (S) {
         case 16: LSEC_TILED(16); break;
         case 8: LSEC_TILED(8); break;
@@ -365,9 +365,9 @@ void launch_span(int N, const TiledArgs& a) {
     if constexpr (DT != LSEC_FP32) {
         const uint32_t spans = a.rows / 4;
         const unsigned blocks = (spans + kBlock / 64 - 1) / (kBlock / 64);
-#define LSEC_SPAN(NV)                                                                       \
-    combine_span_kernel<DT, NV><<<blocks, kBlock, 0, a.st>>>(a.src, spans, a.plane_bytes,   \
-                                                             a.scale, a.inv_scale, a.out, a.out_lse)
+#define LSEC_SPAN(NV)                                                                        \
+    launch(combine_span_kernel<DT, NV>, dim3(blocks), dim3(kBlock), 0, a.st, a.src, spans,     \
+           a.plane_bytes, a.scale, a.inv_scale, a.out, a.out_lse)
         switch (N) {
             case 2: LSEC_SPAN(2); break;
             case 4: LSEC_SPAN(4); break;

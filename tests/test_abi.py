@@ -41,7 +41,8 @@ def test_header_declares_expected_entry_points():
               "lsec_combine_planes", "lsec_combine_planes_valid", "lsec_correct_partial",
               "lsec_combine_path"):
         assert n in _declared([HEADER])
-    for n in ("lsec_floor_empty", "lsec_floor_read", "lsec_floor_read_blocks", "lsec_floor_copy"):
+    for n in ("lsec_floor_empty", "lsec_floor_read", "lsec_floor_read_blocks", "lsec_floor_copy",
+              "lsec_time_next_launch"):
         assert n in names
 
 
@@ -311,6 +312,17 @@ def test_floor_read_validation(lib):
     assert lib.lsec_floor_copy(None, other, 32, None) == 1      # NULL
     assert lib.lsec_floor_copy(fake, None, 32, None) == 1       # NULL
     assert lib.lsec_floor_copy(fake, ctypes.c_void_p((1 << 21) + 8), 32, None) == 5  # ALIGNMENT
+
+
+def test_time_next_launch_arms_and_disarms(lib):
+    """Arming and disarming touch no GPU state; exactly one NULL is an error."""
+    lib.lsec_time_next_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.lsec_time_next_launch(fake, None) == 1           # NULL
+    assert lib.lsec_time_next_launch(None, fake) == 1           # NULL
+    assert lib.lsec_time_next_launch(None, None) == 0           # disarm (nothing armed)
+    assert lib.lsec_time_next_launch(fake, fake) == 0           # armed ...
+    assert lib.lsec_time_next_launch(None, None) == 0           # ... and disarmed unused
 
 
 def test_floor_header_compiles_as_c99(tmp_path):

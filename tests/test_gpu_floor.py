@@ -87,3 +87,46 @@ def test_floor_copy_rejects_bad_sizes(lsec):
         lsec.lsec_floor_copy(a, torch.zeros(4, dtype=torch.int32, device=DEV))
     with pytest.raises(ValueError):
         lsec.lsec_floor_copy(a[:3], torch.zeros(3, dtype=torch.int32, device=DEV))
+
+
+def test_time_next_launch_times_one_kernel(lsec):
+    """lsec_time_next_launch: the armed launch records its own start and end;
+    a 256 MiB read takes about 40 us at 6.5-7 TB/s, and the dispatch-timed
+    duration is positive and not above the time between event markers around
+    the same launch. Only the armed launch is timed (the next one leaves the
+    pair as it was), and the results of a timed call are those of a plain one."""
+    print("[case] lsec_time_next_launch", flush=True)
+    src = torch.ones((256 << 20) // 4, dtype=torch.int32, device=DEV)
+    sink = torch.empty(lsec.load_library().lsec_floor_read_blocks(256 << 20), dtype=torch.int32,
+                       device=DEV)
+    lsec.lsec_floor_read(src, sink)  # warm up
+    timer = lsec.LaunchTimer(2)
+    try:
+        for i in range(2):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            timer.arm(i)
+            lsec.lsec_floor_read(src, sink)
+            b.record()
+            torch.cuda.synchronize()
+            k_ms, m_ms = timer.elapsed_ms(i), a.elapsed_time(b)
+            print(f"dispatch {k_ms * 1e3:.1f} us, markers {m_ms * 1e3:.1f} us", flush=True)
+            assert 0.0 < k_ms <= m_ms + 1e-3
+            assert k_ms < 1.0  # 256 MiB in well under a millisecond
+        # an unarmed launch does not touch the pairs
+        before = timer.elapsed_ms(1)
+        lsec.lsec_floor_read(src, sink)
+        torch.cuda.synchronize()
+        assert timer.elapsed_ms(1) == before
+        # armed and disarmed: the next launch is plain
+        timer.arm(0)
+        timer.disarm()
+        lsec.lsec_floor_empty()
+        torch.cuda.synchronize()
+    finally:
+        timer.close()
+    # the words the read produced are the same with and without timing
+    plain = lsec.lsec_floor_read(src)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, sink)
