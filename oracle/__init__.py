@@ -69,9 +69,13 @@ _I = ctypes.c_int64
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        # LSEC_ORACLE_LIB: another build of the same source (the sanitizer test's)
+        path = os.environ.get("LSEC_ORACLE_LIB")
+        if path is None:
+            path = _LIB
+            if not os.path.exists(path):
+                build()
+        lib = ctypes.CDLL(path)
         lib.oracle_bf16_to_f64.restype = ctypes.c_double
         lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
