@@ -360,14 +360,17 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False, dispa
     hold the same work in different memory): step i then runs set i mod the
     number of sets. Every fn makes one library call, which launches one kernel.
 
-    Returns the wall time of the timed loop and, per kernel, two lists of
-    launch times in ms: by HIP events recorded around each launch on the
-    current stream (the one the kernels are launched on), which include the
-    event markers' own time; and, with `dispatch`, by the kernel's own
-    dispatch (lsec_time_next_launch: events that the launch itself records),
-    the kernel's duration as a kernel trace reports it (else None). Timing
-    the dispatch adds work to the stream around each launch, so the marker
-    times of a dispatch-timed loop are not those of plain launches."""
+    Returns a dict: "wall" (s, the timed loop on the host clock); "step_ms"
+    (per step, by HIP events on the current stream, the one the kernels are
+    launched on): without a flush the steps run back to back and one pair of
+    events spans all of them, so every entry is the region's time divided by
+    the steps; with a flush, events around each step, which include the
+    event markers' own time; and, with `dispatch`, "kernel_ms": per kernel,
+    the list of its launch times by the kernel's own dispatch
+    (lsec_time_next_launch: events that the launch itself records), the
+    kernel's duration as a kernel trace reports it (else None). Timing the
+    dispatch adds work to the stream around each launch, so the step times of
+    a dispatch-timed loop are not those of plain launches."""
     import torch
 
     import lse_weighted_merge_combine_amd as lsec
@@ -380,37 +383,49 @@ def time_steps(kernels, steps, warmup, flush_bytes, dev, flush_read=False, dispa
             fn()
     torch.cuda.synchronize()
     nk = len(sets[0])
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    region = flush is None
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+          for _ in range(1 if region else steps)]
     timer = lsec.LaunchTimer(steps * nk) if dispatch else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if flush is None and sum(b for _, b, _ in sets[0]) < (1 << 30):
-        # Small steps back to back: without a backlog the GPU would wait for
-        # the host to enqueue each launch, and the events around a launch
-        # would time that gap. A spin of ~20 ms + 0.1 ms per launch (about
-        # 2.4e6 cycles per ms on MI355X) lets the host enqueue every step
-        # before the first one runs; wall_s then includes the spin.
-        torch.cuda._sleep(int(2.4e6 * (20 + 0.1 * steps * nk)))
+    if flush is None:
+        # Steps back to back: without a backlog the GPU would wait for the
+        # host to enqueue each launch (small steps), or at least the first
+        # one, after the region's start event (every step). A spin of ~2 ms,
+        # or of ~20 ms + 0.1 ms per launch for steps under 1 GiB (about 2.4e6
+        # cycles per ms on MI355X), lets the host get ahead before the first
+        # step runs; wall_s then includes the spin, the events do not.
+        small = sum(b for _, b, _ in sets[0]) < (1 << 30)
+        torch.cuda._sleep(int(2.4e6 * ((20 + 0.1 * steps * nk) if small else 2)))
+    if region:
+        ev[0][0].record()
     for i in range(steps):
         if flush is not None:
             if flush_read:
                 flush.sum()
             else:
                 flush.fill_(float(i))
-        ev[i][0].record()
+            ev[i][0].record()
         for k, (_, _, fn) in enumerate(sets[i % len(sets)]):
             if timer is not None:
                 timer.arm(i * nk + k)
             fn()
-            ev[i][k + 1].record()
+        if not region:
+            ev[i][1].record()
+    if region:
+        ev[0][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    times = [[ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(steps)] for k in range(nk)]
-    ktimes = None
+    if region:
+        step_ms = [ev[0][0].elapsed_time(ev[0][1]) / steps] * steps
+    else:
+        step_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    kernel_ms = None
     if timer is not None:
-        ktimes = [[timer.elapsed_ms(i * nk + k) for i in range(steps)] for k in range(nk)]
+        kernel_ms = [[timer.elapsed_ms(i * nk + k) for i in range(steps)] for k in range(nk)]
         timer.close()
-    return wall, times, ktimes
+    return {"wall": wall, "step_ms": step_ms, "kernel_ms": kernel_ms, "region": region}
 
 
 def stats_us(ms):
@@ -439,8 +454,8 @@ def time_floor(kernels, ktimes, steps, warmup, flush_bytes, dev, flush_read=Fals
 
     import lse_weighted_merge_combine_amd as lsec
 
-    _, _, e_ms = time_steps([("empty", 0, lambda: lsec.lsec_floor_empty(dev))], steps, warmup,
-                            flush_bytes, dev, flush_read)
+    e_ms = time_steps([("empty", 0, lambda: lsec.lsec_floor_empty(dev))], steps, warmup,
+                      flush_bytes, dev, flush_read)["kernel_ms"]
     reads = []
     n_sets = max(rotate, 1)
     for k, (name, nbytes, _) in enumerate(kernels):
@@ -448,14 +463,15 @@ def time_floor(kernels, ktimes, steps, warmup, flush_bytes, dev, flush_read=Fals
         bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(n_sets)]
         sink = torch.empty(max(lsec.load_library().lsec_floor_read_blocks(nbytes), 1),
                            dtype=torch.int32, device=dev)
-        _, _, r_ms = time_steps([[("read", nbytes, lambda b=b: lsec.lsec_floor_read(b, sink))]
-                                 for b in bufs], steps, warmup, flush_bytes, dev, flush_read)
+        r_ms = time_steps([[("read", nbytes, lambda b=b: lsec.lsec_floor_read(b, sink))]
+                           for b in bufs], steps, warmup, flush_bytes, dev, flush_read)["kernel_ms"]
         del bufs, sink
         half = (nbytes // 2) - (nbytes // 2) % 16
         pairs = [(torch.ones(half // 4, dtype=torch.int32, device=dev),
                   torch.empty(half // 4, dtype=torch.int32, device=dev)) for _ in range(n_sets)]
-        _, _, c_ms = time_steps([[("copy", 2 * half, lambda a=a, c=c: lsec.lsec_floor_copy(a, c))]
-                                 for a, c in pairs], steps, warmup, flush_bytes, dev, flush_read)
+        c_ms = time_steps([[("copy", 2 * half, lambda a=a, c=c: lsec.lsec_floor_copy(a, c))]
+                           for a, c in pairs], steps, warmup, flush_bytes, dev,
+                          flush_read)["kernel_ms"]
         del pairs
         read_ms, copy_ms = float(np.mean(r_ms[0])), float(np.mean(c_ms[0]))
         read_med, copy_med = float(np.median(r_ms[0])), float(np.median(c_ms[0]))
@@ -732,11 +748,13 @@ def measure(name, dev, steps, warmup, flush_mib, floor=True, warm_steps=0, out_f
     left the outputs bit for bit as saved, then run the CPU leg (parity of the
     saved outputs against the oracle; with time_cpu the CPU baseline).
 
-    Kernel figures come from the kernels' own dispatch times. With `plain`,
-    the steps are first timed with plain launches and events around each
-    step (the timed region of the headline: `steps` steps after `warmup`),
-    then the kernels' dispatch times are taken over another `steps` launches
-    of the same steps."""
+    Kernel figures come from the kernels' own dispatch times over `steps`
+    steps after `warmup`. With `plain`, the steps are then timed once more
+    with plain launches, after the floor: the timed region of the headline,
+    `steps` steps after `warmup` (see time_steps for its events). The GPU
+    runs its first few milliseconds of work after an idle spell measurably
+    slower (the first 20 launches of the large-batch combine 1-2 %), so the
+    measurement passes run first."""
     import torch
 
     work = build_workload(name, dev, out_f32, valid_tokens)
@@ -755,22 +773,23 @@ def measure(name, dev, steps, warmup, flush_mib, floor=True, warm_steps=0, out_f
         (f"{rotate} input sets in rotation" if rotate else
          f"flush {flush_mib} MiB{' (read)' if flush_read else ''}"))
     res = {"work": work, "step_bytes": step_bytes, "flush_mib": flush_mib}
-    if plain:
-        res["wall"], res["times"], _ = time_steps(sets, steps, warmup, flush_mib << 20, dev,
-                                                  flush_read, dispatch=False)
-    wall, times, ktimes = time_steps(sets, steps, 0 if plain else warmup, flush_mib << 20, dev,
-                                     flush_read)
-    res["ktimes"] = ktimes
+    t = time_steps(sets, steps, warmup, flush_mib << 20, dev, flush_read)
+    res["ktimes"] = t["kernel_ms"]
     if not plain:
-        res["wall"], res["times"] = wall, times
+        res["wall"], res["step_ms"], res["region"] = t["wall"], t["step_ms"], t["region"]
     if warm_steps:
-        _, _, wt = time_steps(work.kernels, warm_steps, warmup, 0, dev)
-        res["warm"] = wt
+        res["warm"] = time_steps(work.kernels, warm_steps, warmup, 0, dev)["kernel_ms"]
     if floor:
-        res["floor"] = time_floor(work.kernels, ktimes, steps, warmup, flush_mib << 20, dev,
-                                  flush_read, rotate)
+        res["floor"] = time_floor(work.kernels, res["ktimes"], steps, warmup, flush_mib << 20,
+                                  dev, flush_read, rotate)
+    if plain:
+        # the timed region last: `warmup` untimed steps, then exactly `steps`
+        # steps of plain launches
+        t = time_steps(sets, steps, warmup, flush_mib << 20, dev, flush_read, dispatch=False)
+        res["wall"], res["step_ms"], res["region"] = t["wall"], t["step_ms"], t["region"]
     torch.cuda.synchronize()
     res["unchanged"] = all(same_bits(work.outputs[k], saved_dev[k]) for k in saved_dev)
+    res["ktimes_of_steps"] = [sum(kt[i] for kt in res["ktimes"]) for i in range(steps)]
     if cpu:
         saved = {k: t.cpu() for k, t in saved_dev.items()}
         del saved_dev
@@ -929,7 +948,7 @@ def main():
                 out_f32=args.out_f32, valid_tokens=args.valid_tokens, cpu=use_cpu,
                 time_cpu=use_cpu, rotate=args.rotate, flush_read=args.flush_read, plain=True)
     work = r["work"]
-    step_ms = [sum(t[i] for t in r["times"]) for i in range(args.steps)]
+    step_ms = r["step_ms"]
     ms_per_step = sum(step_ms) / args.steps
     value = r["step_bytes"] / (ms_per_step * 1e-3) / 1e9
     log(f"[bench] wall {r['wall']:.3f}s for {args.steps} steps; kernels {sum(step_ms):.3f} ms")
@@ -947,9 +966,9 @@ def main():
                 "bytes_per_launch": kbytes, "avg_launch_us": round(k_ms * 1e3, 3),
                 "median_launch_us": stats_us(r["ktimes"][k])["median_us"],
                 "launch_timing": "HIP events recorded by the kernel's own dispatch on the stream "
-                                 "it runs on (lsec_time_next_launch), over --steps launches after "
-                                 "the timed region; value and ms_per_step come from events around "
-                                 "each of the timed region's plain launches",
+                                 "it runs on (lsec_time_next_launch), over --steps launches before "
+                                 "the timed region; value and ms_per_step come from the timed "
+                                 "region's plain launches",
                 "traffic": load_traffic(name + ("_f32out" if args.out_f32 else ""), kname)}
     if args.floor:
         fl = r["floor"]
@@ -978,10 +997,15 @@ def main():
                              ("read" if args.flush_read else "write") if r["flush_mib"] else
                              "none"),
         "wall_s": round(r["wall"], 4), "kernels": recs,
-        "step_timing": {**stats_us(step_ms), "first_steps_us":
-                        [round(t * 1e3, 3) for t in step_ms[:5]],
-                        "timing": "HIP events around each step of the timed region (plain "
-                                  "launches)"},
+        "step_timing": ({"timing": "one pair of HIP events around the timed region's plain "
+                                   "launches, back to back: ms_per_step is its time / steps",
+                         "region_us": round(sum(step_ms) * 1e3, 3)} if r["region"] else
+                        {**stats_us(step_ms), "timing": "HIP events around each step of the "
+                                                        "timed region (plain launches)"}),
+        "dispatch_step_timing": {**stats_us(r["ktimes_of_steps"]), "first_steps_us":
+                                 [round(t * 1e3, 3) for t in r["ktimes_of_steps"][:5]],
+                                 "timing": "the step's kernels by their own dispatch, over --steps "
+                                           "launches before the timed region"},
         "roofline": roofline, "cpu_baseline": cpu,
         "outputs_unchanged_by_timed_steps": r["unchanged"],
     }
