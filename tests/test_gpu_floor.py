@@ -130,3 +130,35 @@ def test_time_next_launch_times_one_kernel(lsec):
     plain = lsec.lsec_floor_read(src)
     torch.cuda.synchronize()
     assert torch.equal(plain, sink)
+
+
+def test_timed_launches_of_the_hot_path_match_plain_ones(lsec):
+    """A combine, a pack and an unpack + combine launched with events armed
+    (hipExtLaunchKernelGGL) produce the same bits as plain launches, and each
+    armed pair times exactly its own call's kernel."""
+    import synth
+    print("[case] timed hot-path launches", flush=True)
+    N, B, H, D = 8, 512, 16, 128
+    o, l = synth.custom_inputs(N, B, H, D, dtype="bf16", seed=71)
+    og = torch.from_numpy(o.view(np.int16)).view(torch.bfloat16).to(DEV)
+    lg = torch.from_numpy(l).to(DEV)
+    ref_y, ref_L = lsec.lsec_combine(og, lg, return_lse=True)
+    send_ref = lsec.lsec_pack_send(og[0], lg[0], N)
+    uc_ref = lsec.lsec_unpack_combine(send_ref, return_lse=True)
+    torch.cuda.synchronize()
+    timer = lsec.LaunchTimer(3)
+    try:
+        timer.arm(0)
+        y, L = lsec.lsec_combine(og, lg, return_lse=True)
+        timer.arm(1)
+        send = lsec.lsec_pack_send(og[0], lg[0], N)
+        timer.arm(2)
+        uy, uL = lsec.lsec_unpack_combine(send, return_lse=True)
+        torch.cuda.synchronize()
+        assert all(timer.elapsed_ms(i) > 0.0 for i in range(3))
+    finally:
+        timer.close()
+    for a, b in ((y, ref_y), (uy, uc_ref[0]), (send, send_ref)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for a, b in ((L, ref_L), (uL, uc_ref[1])):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
