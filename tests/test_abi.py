@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -333,3 +334,39 @@ def test_floor_header_compiles_as_c99(tmp_path):
                           "-I", os.path.join(ROOT, "include"), str(src)],
                          capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With liblsec.so absent, every hot-path entry point of the binding
+    raises instead of computing anything: there is no CPU fallback, and the
+    oracle is never imported."""
+    import shutil
+    pkg = os.path.join(ROOT, "lse_weighted_merge_combine_amd")
+    shutil.copytree(pkg, tmp_path / "lse_weighted_merge_combine_amd",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    code = f"""
+import sys, torch
+sys.path.insert(0, {str(tmp_path)!r})
+import lse_weighted_merge_combine_amd as m
+assert m.__file__.startswith({str(tmp_path)!r}), m.__file__
+o = torch.zeros(2, 3, 4, 128, dtype=torch.bfloat16)
+l = torch.zeros(2, 3, 4)
+calls = [(m.lse_combine, (o, l)), (m.lsec_combine, (o, l)), (m.pack_send, (o[0], l[0], 2)),
+         (m.unpack_combine, (torch.zeros(2, 3, 2, 130, dtype=torch.bfloat16), 128)),
+         (m.lse_weighted_combine, (o, l)), (m.load_library, ())]
+for fn, args in calls:
+    try:
+        fn(*args)
+    except (ImportError, ValueError) as e:
+        pass
+    else:
+        raise SystemExit(f"{{fn.__name__}} returned without the library")
+try:
+    m.load_library()
+except ImportError as e:
+    assert "missing" in str(e), e
+assert "oracle" not in sys.modules
+print("ok")
+"""
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0 and res.stdout.strip().endswith("ok"), res.stdout + res.stderr

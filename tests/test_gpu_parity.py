@@ -93,7 +93,7 @@ def _packed_ranks(w, b_lo=0, b_hi=None):
 
 def test_packed_workload_full(lsec):
     """8 ranks x [2048,64,128] bf16: GPU pack on every rank (bit-exact with the
-    oracle), all-to-all stand-in, GPU unpack+combine on two receiving ranks."""
+    oracle), all-to-all stand-in, GPU unpack+combine on every receiving rank."""
     w = synth.WORKLOADS["packed"]
     _announce("packed full: 8 ranks pack, exchange, unpack_combine")
     outs, lses = _packed_ranks(w)
@@ -106,7 +106,7 @@ def test_packed_workload_full(lsec):
         sends.append(s)
     so, sl = np.stack(outs), np.stack(lses)
     M = max_abs_input(so, w.dtype)
-    for p in (0, 5):
+    for p in range(w.N):
         recv = torch.stack([sends[r][p] for r in range(w.N)]).contiguous()
         y, L = lsec.lsec_unpack_combine(recv, base_e=True, return_lse=True)
         uo, ul = lsec.lsec_unpack(recv)
