@@ -97,7 +97,8 @@ int lsec_pack_dim(int dtype);
  * Per (b, h) row: l'_n = -inf if l_n is NaN or +-inf; m = max_n l'_n (0 if
  * that is -inf); w_n = exp(l'_n - m) or 2^(l'_n - m); S = sum_n w_n;
  * out = sum_n outputs_n * w_n / max(S, 1e-10); out_lse = ln S + m or
- * log2 S + m. N = 1 with a finite LSE returns its input unchanged.
+ * log2 S + m. N = 1 with a finite LSE returns its input unchanged, bit for
+ * bit (-0 and subnormals included), and its LSE as the global LSE.
  * Errors: NULL, SHAPE, DTYPE, BASE, ALIGNMENT, LAUNCH.
  */
 int lsec_combine(const void* outputs, const float* lses, int64_t N, int64_t B, int64_t H,
