@@ -238,9 +238,9 @@ int lsec_unpack(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D, i
  * rank, Hl) launches for these sizes and `dtype` (as passed to those calls),
  * given whether the buffers meet the fast alignment (aligned_buffers != 0: 16
  * bytes for outputs, recv and out). Returns a static string such as
- * "combine_tiled_kernel S=16", "combine_span_kernel", "combine_rows_kernel" or
- * "combine_elems_kernel"; "none" when the arguments launch nothing or are
- * invalid. Touches no GPU state.
+ * "combine_tiled_kernel S=16", "combine_span_kernel", "combine_span32_kernel",
+ * "combine_rows_kernel" or "combine_elems_kernel"; "none" when the arguments
+ * launch nothing or are invalid. Touches no GPU state.
  */
 const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int dtype, int packed,
                               int aligned_buffers);

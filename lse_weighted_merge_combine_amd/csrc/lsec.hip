@@ -583,10 +583,11 @@ struct CombinePlan {
 };
 
 // `pl` gives the plane geometry of the separate layout (packed planes are
-// always dense). `span_ok`: packed 16-bit rows, a result in the input dtype,
-// planes 16-byte aligned, identity output order and no valid count -- then
-// the calls that would run the tiled kernel with S = 1 on rows of 128 values
-// with N = 2, 4, 8 or 16 run the span kernel when the rows are a multiple of 4.
+// always dense). `span_ok`: packed rows, a result in the input dtype, planes
+// 16-byte aligned, identity output order and no valid count -- then the calls
+// that would run the tiled kernel with S = 1 on rows of 128 values with N = 2,
+// 4, 8 or 16 run a span kernel when the rows are a multiple of 4
+// (combine_span_kernel for 16-bit elements, combine_span32_kernel for fp32).
 CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, int64_t esize, bool packed,
                          bool fast, Planes pl, bool span_ok = false) {
     if (!fast) return {kPathElems, 0};
@@ -602,7 +603,8 @@ CombinePlan plan_combine(int64_t N, int64_t rows, int64_t D, int64_t esize, bool
             const uint64_t min_blocks = N >= 16 ? kTiledMinBlocksN16 : kTiledMinBlocks;
             int S = 16;
             while (S > 1 && (uint64_t(rows) + rps * S - 1) / (rps * S) < min_blocks) S /= 2;
-            if (S == 1 && span_ok && packed && esize == 2 && D == 128 && rows % 4 == 0 &&
+            if (S == 1 && span_ok && packed && (esize == 2 || esize == 4) && D == 128 &&
+                rows % 4 == 0 &&
                 (N == 2 || N == 4 || N == 8 || N == 16))
                 return {kPathSpan, 1};
             return {kPathTiled, S};
@@ -621,7 +623,7 @@ void run_combine_dt(const void* src, const float* lse, int64_t N, int64_t rows, 
         const TiledArgs a{src, lse, int(N), uint32_t(rows), uint32_t(stride),
                           uint64_t(pl.plane) * sizeof(typename Elem<DT>::T), uint32_t(pl.lse_plane),
                           scale, inv_scale, out, out_f32, out_lse, om, st};
-        if constexpr (PACKED && DT != LSEC_FP32) {
+        if constexpr (PACKED) {
             if (plan.kind == kPathSpan) {
                 launch_span<DT>(int(N), a);
                 return;
@@ -651,8 +653,8 @@ int run_combine(const void* src, const float* lse, int64_t N, int64_t rows, int6
                     uint32_t(rows_per_token)};
     const float scale = base == LSEC_BASE_2 ? 1.0f : kLog2E;
     const float inv_scale = base == LSEC_BASE_2 ? 1.0f : kLn2;
-    const bool span_ok = PACKED && dt.esize == 2 && !dt.out_f32 && aligned(src, 16) &&
-                         map_a == 0 && valid == nullptr;
+    const bool span_ok = PACKED && dt.out_esize == dt.esize && aligned(src, 16) && map_a == 0 &&
+                         valid == nullptr;
     const CombinePlan plan = plan_combine(N, rows, D, dt.esize, PACKED, fast, pl, span_ok);
     (void)hipGetLastError();
 #define LSEC_RUN(DTV)                                                                        \
@@ -838,11 +840,11 @@ const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int dt
     const bool fast = aligned_buffers && fast_d(D, dt.esize) && rows < (int64_t(1) << 31);
     int64_t rd;
     if (!mul_ok(rows, D, &rd)) return "none";
-    const bool span_ok = packed && aligned_buffers && dt.esize == 2 && !dt.out_f32;
+    const bool span_ok = packed && aligned_buffers && dt.out_esize == dt.esize;
     const CombinePlan plan =
         plan_combine(N, rows, D, dt.esize, packed != 0, fast, Planes{rd, rows}, span_ok);
     if (plan.kind == kPathElems) return "combine_elems_kernel";
-    if (plan.kind == kPathSpan) return "combine_span_kernel";
+    if (plan.kind == kPathSpan) return dt.esize == 2 ? "combine_span_kernel" : "combine_span32_kernel";
     if (plan.kind == kPathRows) return "combine_rows_kernel";
     switch (plan.S) {
         case 16: return "combine_tiled_kernel S=16";

@@ -341,9 +341,9 @@ struct TiledArgs {
 template <int DT, bool PACKED>
 void launch_tiled(int N, int S, int D, const TiledArgs& a);
 
-// Launches the span combine of packed rows (lsec_tiled.hip, 16-bit DT only):
-// D = 128, N in {2, 4, 8, 16}, a.rows a multiple of 4, a.src 16-byte aligned,
-// identity output order, no valid count, a result in the input dtype.
+// Launches the span combine of packed rows (lsec_tiled.hip): D = 128, N in
+// {2, 4, 8, 16}, a.rows a multiple of 4, a.src 16-byte aligned, identity
+// output order, no valid count, a result in the input dtype (16-bit or fp32).
 template <int DT>
 void launch_span(int N, const TiledArgs& a);
 

@@ -288,6 +288,125 @@ __global__ __launch_bounds__(kBlock) void combine_span_kernel(
     st16(static_cast<char*>(out) + uint64_t(span) * kSpanOut + 16u * lane, res);
 }
 
+
+// ---------------------------------------------------------------- combine (packed fp32 spans)
+//
+// Packed rows of 128 fp32 values (516 bytes with the LSE in element 128) in
+// whole spans of four rows, N = 2, 4, 8 or 16, 16-byte aligned planes: a
+// 2064-byte span, 129 aligned 16-byte chunks. Lane i loads chunks i and
+// 64 + i of each plane and every lane chunk 128 (one address per wave).
+// Dword d of a span is element d - 129 r of row r = d / 129; the four LSEs
+// are dwords 128 (chunk 32, dword 0), 257 (chunk 64, dword 1), 386 (chunk 96,
+// dword 2) and 515 (chunk 128, dword 3), read by readlane, and lane 16 r + j
+// keeps shard j's of row r. The weights then follow the slotted kernel exactly
+// (16-lane DPP max and sum, the same normalisation); the weight of row r for
+// plane n is read back from lane 16 r + n, and every element is accumulated
+// in plane order, so the results are those of the slotted kernel bit for
+// bit. Result chunk o of row k = o / 32 is span dwords 4 o + k .. + 3: the
+// lane's own accumulators of chunk o from dword k on, then the first k dwords
+// of chunk o + 1 (the next lane's; for lane 63 chunk 64's, held by lane 0,
+// or chunk 128's), so every store is a whole aligned 16-byte chunk.
+template <int NT>
+__global__ __launch_bounds__(kBlock) void combine_span32_kernel(
+    const void* src, uint32_t spans, uint64_t plane_bytes, float scale, float inv_scale,
+    float* __restrict__ out, float* __restrict__ out_lse) {
+    static_assert(NT >= 2 && NT <= 16, "N compiled in");
+    constexpr uint32_t kSpanIn = 2064, kSpanOut = 512;  // bytes in, fp32 values out
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t k = lane >> 4;  // the row this lane's shard weight belongs to
+    const uint32_t j = lane & 15u;
+    const uint32_t span = xcd_chunked_block(blockIdx.x, gridDim.x) * (kBlock / 64) + threadIdx.x / 64;
+    if (span >= spans) return;  // uniform per wave; no block-wide synchronisation follows
+    const char* base = reinterpret_cast<const char*>(src) + uint64_t(span) * kSpanIn;
+    u32x4 ca[NT], cb[NT], e[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const char* pb = base + uint64_t(n) * plane_bytes;
+        ca[n] = ld16(pb + 16u * lane);
+        cb[n] = ld16(pb + 1024u + 16u * lane);
+        e[n] = ld16(pb + 2048u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto rl = [](uint32_t v, int src_lane) {
+        return uint32_t(__builtin_amdgcn_readlane(int(v), src_lane));
+    };
+    float l = -__builtin_inff();
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const uint32_t t0 = rl(ca[n].x, 32), t1 = rl(cb[n].y, 0), t2 = rl(cb[n].z, 32);
+        const uint32_t mine = k == 0u ? t0 : (k == 1u ? t1 : (k == 2u ? t2 : e[n].w));
+        if (j == uint32_t(n)) l = __uint_as_float(mine);
+    }
+    l = j < uint32_t(NT) ? sanitize(l) : -__builtin_inff();
+    float m = row16_max(l);
+    if (m == -__builtin_inff()) m = 0.0f;
+    const float w = j < uint32_t(NT) ? weight(l - m, scale) : 0.0f;
+    const float sum = row16_sum(w);
+    const float wn = w * (1.0f / fmaxf(sum, 1e-10f));
+    if (out_lse != nullptr && j == 0u) out_lse[uint64_t(span) * 4u + k] = global_lse(sum, m, inv_scale);
+    // Rows of this lane's dwords. Chunk `lane` (dwords 4 lane .. + 3): row 0
+    // below lane 32, row 1 above; lane 32's dword 0 is row 0's LSE, its other
+    // dwords row 1's. Chunk 64 + lane: lane 0's dwords 0 and 1 are row 1's
+    // (element 127 and the LSE), 2 and 3 row 2's; row 2 up to lane 31; lane
+    // 32's dwords 0 to 2 are row 2's (the LSE last), dword 3 row 3's; row 3
+    // above. Chunk 128: row 3 (elements 125-127, then the LSE). LSE dwords are
+    // accumulated like the others and never stored.
+    const bool lo = lane < 32u;
+    float acca[4], accb[4], acce[3];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acca[q] = accb[q] = kAccInit;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) acce[q] = kAccInit;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const float w0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wn), n));
+        const float w1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wn), 16 + n));
+        const float w2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wn), 32 + n));
+        const float w3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wn), 48 + n));
+        const float wa0 = lane <= 32u ? w0 : w1;
+        const float wa = lo ? w0 : w1;
+        const float wb01 = lane == 0u ? w1 : (lane <= 32u ? w2 : w3);
+        const float wb2 = lane <= 32u ? w2 : w3;
+        const float wb3 = lo ? w2 : w3;
+        acca[0] = fmaf(__uint_as_float(ca[n].x), wa0, acca[0]);
+        acca[1] = fmaf(__uint_as_float(ca[n].y), wa, acca[1]);
+        acca[2] = fmaf(__uint_as_float(ca[n].z), wa, acca[2]);
+        acca[3] = fmaf(__uint_as_float(ca[n].w), wa, acca[3]);
+        accb[0] = fmaf(__uint_as_float(cb[n].x), wb01, accb[0]);
+        accb[1] = fmaf(__uint_as_float(cb[n].y), wb01, accb[1]);
+        accb[2] = fmaf(__uint_as_float(cb[n].z), wb2, accb[2]);
+        accb[3] = fmaf(__uint_as_float(cb[n].w), wb3, accb[3]);
+        acce[0] = fmaf(__uint_as_float(e[n].x), w3, acce[0]);
+        acce[1] = fmaf(__uint_as_float(e[n].y), w3, acce[1]);
+        acce[2] = fmaf(__uint_as_float(e[n].z), w3, acce[2]);
+    }
+    // The first dwords of the next chunk: the next lane's, or for lane 63
+    // chunk 64 (lane 0's second chunk) and chunk 128. Every shuffle runs on all
+    // lanes before the selection: a lane shuffle reads 0 from a lane that is
+    // switched off, so it must not sit in a branch that leaves lane 63 out.
+    const bool last = lane == 63u;
+    const float down0 = __shfl_down(acca[0], 1);
+    const float first_b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, accb[0]), 0));
+    const float na0 = last ? first_b : down0;
+    float nb[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const float down = __shfl_down(accb[q], 1);
+        nb[q] = last ? acce[q] : down;
+    }
+    // Chunk `lane` of the result: row 0 below lane 32 (dwords 0-3), row 1 above
+    // (dwords 1-3 and the next chunk's 0). Chunk 64 + lane: row 2 below lane
+    // 32 (dwords 2, 3 and the next chunk's 0, 1), row 3 above (dword 3 and the
+    // next chunk's 0-2).
+    const u32x4 r0 = lo ? f32_chunk(acca[0], acca[1], acca[2], acca[3])
+                        : f32_chunk(acca[1], acca[2], acca[3], na0);
+    const u32x4 r1 = lo ? f32_chunk(accb[2], accb[3], nb[0], nb[1])
+                        : f32_chunk(accb[3], nb[0], nb[1], nb[2]);
+    float* po = out + uint64_t(span) * kSpanOut;
+    st16(po + 4u * lane, r0);
+    st16(po + 256u + 4u * lane, r1);
+}
+
 }  // namespace
 
 // Occupancy cap for the tiled combine, as dynamic LDS that the kernel never
@@ -358,13 +477,13 @@ void launch_tiled(int N, int S, int D, const TiledArgs& a) {
 template void launch_tiled<LSEC_TILED_DT, false>(int, int, int, const TiledArgs&);
 template void launch_tiled<LSEC_TILED_DT, true>(int, int, int, const TiledArgs&);
 
-// 16-bit elements only; the fp32 unit instantiates an empty launcher that the
-// host never calls (it routes only 16-bit packed rows here).
+// Packed rows of 128 values in whole spans of four: combine_span_kernel for
+// 16-bit elements, combine_span32_kernel for fp32.
 template <int DT>
 void launch_span(int N, const TiledArgs& a) {
+    const uint32_t spans = a.rows / 4;
+    const unsigned blocks = (spans + kBlock / 64 - 1) / (kBlock / 64);
     if constexpr (DT != LSEC_FP32) {
-        const uint32_t spans = a.rows / 4;
-        const unsigned blocks = (spans + kBlock / 64 - 1) / (kBlock / 64);
 #define LSEC_SPAN(NV)                                                                        \
     launch(combine_span_kernel<DT, NV>, dim3(blocks), dim3(kBlock), 0, a.st, a.src, spans,     \
            a.plane_bytes, a.scale, a.inv_scale, a.out, a.out_lse)
@@ -375,6 +494,18 @@ void launch_span(int N, const TiledArgs& a) {
             default: LSEC_SPAN(16); break;
         }
 #undef LSEC_SPAN
+    } else {
+        float* out = static_cast<float*>(a.out);
+#define LSEC_SPAN32(NV)                                                                      \
+    launch(combine_span32_kernel<NV>, dim3(blocks), dim3(kBlock), 0, a.st, a.src, spans,       \
+           a.plane_bytes, a.scale, a.inv_scale, out, a.out_lse)
+        switch (N) {
+            case 2: LSEC_SPAN32(2); break;
+            case 4: LSEC_SPAN32(4); break;
+            case 8: LSEC_SPAN32(8); break;
+            default: LSEC_SPAN32(16); break;
+        }
+#undef LSEC_SPAN32
     }
 }
 

@@ -158,7 +158,9 @@ def test_python_binding_rejects_bad_tensors():
     ((8, 2048, 8, 256, 0, 1, 1), "combine_tiled_kernel S=1"),    # packed, D != 128
     ((8, 2048, 8, 128, 0, 1, 0), "combine_elems_kernel"),        # packed, unaligned buffers
     ((8, 2048, 8, 128, 256, 1, 1), "combine_tiled_kernel S=1"),  # packed, fp32 result
-    ((8, 2048, 8, 128, 2, 1, 1), "combine_tiled_kernel S=1"),    # fp32 packed rows
+    ((8, 2048, 8, 128, 2, 1, 1), "combine_span32_kernel"),      # fp32 packed rows, whole spans
+    ((8, 2047, 2, 128, 2, 1, 1), "combine_tiled_kernel S=1"),    # fp32 packed rows, not whole spans
+    ((8, 2048, 8, 256, 2, 1, 1), "combine_tiled_kernel S=2"),    # fp32 packed rows, D != 128
     ((17, 2048, 8, 128, 0, 1, 1), "combine_rows_kernel"),        # packed, N > 16
     ((16, 16384, 32, 128, 0, 0, 0), "combine_elems_kernel"),   # buffers not 16-byte aligned
     ((1, 50, 3, 512, 0, 0, 1), "combine_rows_kernel"),          # N = 1

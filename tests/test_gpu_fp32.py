@@ -251,6 +251,70 @@ def test_tiled_unpack_combine_f32(lsec, N, B, H, D, slots):
     assert_lse_close(L, L_ref)
 
 
+@pytest.mark.parametrize("N,B,Hl,base2,return_lse", [
+    (2, 6, 2, False, True),       # 12 rows: three spans, one partial block
+    (4, 1027, 4, True, True),     # 4108 rows: 1027 spans, the last block partial
+    (8, 2048, 8, False, True),    # the packed_f32 workload's receive side
+    (8, 4101, 4, False, False),   # 16404 rows, no global LSE
+    (16, 257, 4, True, True),     # N = 16
+])
+def test_span32_unpack_combine(lsec, N, B, Hl, base2, return_lse):
+    """Packed rows of 128 fp32 values in whole spans of four: the fp32 span
+    kernel (aligned chunk loads, the LSEs taken from them, realigned stores)."""
+    D, H = 128, N * Hl
+    _announce(f"span32 unpack_combine N={N} B={B} Hl={Hl} base2={base2}")
+    assert lsec.lsec_combine_path(N, B, Hl, D, packed=True, dtype=F32) == "combine_span32_kernel"
+    outs, lses = [], []
+    for r in range(N):
+        a, b = synth.custom_inputs(1, B, H, D, dtype="f32", seed=1900 + 31 * N + r,
+                                   special=SPECIALS)
+        outs.append(a[0])
+        lses.append(b[0])
+    recv_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N, dtype="f32")
+                              for r in range(N)])[N - 1]
+    res = lsec.lsec_unpack_combine(to_dev(recv_h, "f32", DEV), base_e=not base2,
+                                   return_lse=return_lse)
+    torch.cuda.synchronize()
+    y, L = res if return_lse else (res, None)
+    y_ref, L_ref = oracle.unpack_combine(recv_h, D, "f32", base2)
+    oo, _ = oracle.unpack(recv_h, D, dtype="f32")
+    assert_output_close(y, y_ref, "f32", max_abs_input(oo, "f32"))
+    if return_lse:
+        assert_lse_close(L, L_ref)
+
+
+@pytest.mark.parametrize("N,B,H", [(8, 64, 16), (16, 37, 64), (2, 1030, 4)])
+def test_span32_matches_the_tiled_kernel_bit_for_bit(lsec, N, B, H):
+    """The same fp32 receive buffer 4 bytes past a 16-byte boundary takes the
+    tiled kernel, the aligned one the span kernel; both weight and sum the
+    planes in the same order, so the results agree bit for bit."""
+    D = 128
+    _announce(f"span32 vs tiled N={N} B={B} H={H}")
+    assert lsec.lsec_combine_path(N, B, H // N, D, packed=True, dtype=F32) == \
+        "combine_span32_kernel"
+    outs, lses = [], []
+    for r in range(N):
+        a, b = synth.custom_inputs(1, B, H, D, dtype="f32", seed=1760 + r, special=SPECIALS)
+        outs.append(a[0])
+        lses.append(b[0])
+    recv_h = oracle.exchange([oracle.pack_send(outs[r], lses[r], N, dtype="f32")
+                              for r in range(N)])[1]
+    flat = torch.empty(recv_h.size + 4, dtype=F32, device=DEV)
+    shifted = flat[1:1 + recv_h.size].view(recv_h.shape)
+    shifted.copy_(to_dev(recv_h, "f32", DEV))
+    assert shifted.data_ptr() % 16 == 4
+    y1, L1 = lsec.lsec_unpack_combine(shifted, return_lse=True)
+    y2, L2 = lsec.lsec_unpack_combine(to_dev(recv_h, "f32", DEV), return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.unpack_combine(recv_h, D, "f32")
+    oo, _ = oracle.unpack(recv_h, D, dtype="f32")
+    for y, L in ((y1, L1), (y2, L2)):
+        assert_output_close(y, y_ref, "f32", max_abs_input(oo, "f32"))
+        assert_lse_close(L, L_ref)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    assert torch.equal(L1.view(torch.int32), L2.view(torch.int32))
+
+
 def test_f32_exchange_on_the_gpu(lsec):
     """4 ranks pack fp32 outputs on the GPU, the all-to-all is a host-side
     placement, and each receiver's unpack_combine matches the oracle's
