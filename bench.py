@@ -335,7 +335,9 @@ def build_workload(name: str, dev, out_f32: bool = False, valid_tokens=None):
             lsec.lsec_unpack_combine(recv, base_e=not w.base2, return_lse=True, out=out,
                                      out_lse=out_lse)
 
-        pack_kernel = "pack_lds_kernel" if send.data_ptr() % 16 == 0 else "pack_rows_kernel"
+        send_align = next(a for a in (16, 8, 4, 2, 1) if send.data_ptr() % a == 0)
+        pack_kernel = lsec.lsec_pack_path(w.N, w.B, w.H, w.D, tdt, a0.data_ptr() % 16 == 0,
+                                          send_align)
         kernels = [(f"{pack_kernel} ({w.dtype})", pack_bytes(w.N, w.B, w.H, w.D, s), pack),
                    (f"{lsec.lsec_combine_path(w.N, w.B, Hl, w.D, packed=True, dtype=tdt)} "
                     f"({w.dtype}, N={w.N}, D={w.D}, packed rows)",

@@ -120,6 +120,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lsec_correct_partial.argtypes = [P, I64, I64, P, I64, I64, I64, I, I, P, P, P]
     lib.lsec_combine_path.restype = ctypes.c_char_p
     lib.lsec_combine_path.argtypes = [I64, I64, I64, I64, I, I, I]
+    lib.lsec_pack_path.restype = ctypes.c_char_p
+    lib.lsec_pack_path.argtypes = [I64, I64, I64, I64, I, I, I]
     lib.lsec_floor_empty.restype = I
     lib.lsec_floor_empty.argtypes = [P]
     lib.lsec_floor_read_blocks.restype = I64
@@ -453,6 +455,15 @@ def lsec_combine_path(N: int, B: int, H: int, D: int, packed: bool = False,
     return load_library().lsec_combine_path(N, B, H, D, code, int(packed), int(aligned)).decode()
 
 
+def lsec_pack_path(N: int, B: int, H: int, D: int, dtype: torch.dtype = torch.bfloat16,
+                   in_aligned: bool = True, send_align: int = 16) -> str:
+    """Name of the kernel lsec_pack_send launches for these sizes (diagnostics)."""
+    code = _DTYPES.get(dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return load_library().lsec_pack_path(N, B, H, D, code, int(in_aligned), int(send_align)).decode()
+
+
 def lse_weighted_combine(outputs: torch.Tensor, lses: torch.Tensor, return_lse: bool = False,
                          is_lse_base_on_e: bool = True):
     """The page's ``_lse_weighted_combine(outputs, lses, return_lse, is_lse_base_on_e)``,
@@ -666,7 +677,7 @@ def _check_out(t: torch.Tensor, shape, dtype, dev) -> None:
 
 __all__ = [
     "lsec_pack_dim", "lsec_combine", "lsec_pack_send", "lsec_unpack_combine", "lsec_unpack",
-    "lsec_combine_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
+    "lsec_combine_path", "lsec_pack_path", "lsec_merge", "merge_dcp_outputs", "lsec_correct_partial",
     "lsec_combine_planes", "lse_combine", "pack_send", "unpack_combine", "dcp_a2a_lse_reduce",
     "lse_weighted_combine", "load_library", "status_string", "LsecError", "LIB_PATH",
     "lsec_floor_empty", "lsec_floor_read", "lsec_floor_copy", "dcp_a2a_send_recv_buffers",

@@ -720,27 +720,44 @@ void launch_correct(bool tiled, const float* lse, int64_t N, int64_t rank, const
 #undef LSEC_CORRECT_G
 }
 
+// Which pack kernel serves a call. `in_aligned`: attn_out is 16-byte aligned;
+// `send_align`: the send buffer's alignment in bytes (16, 4 or the element
+// size). Whole 16-byte chunks per lane need fast_d(D), rows < 2^31, an aligned
+// input and a 4-byte aligned send buffer; with a 16-byte aligned one the rows
+// go out through LDS in whole cache lines.
+enum { kPackPathElems = 0, kPackPathRows = 1, kPackPathLds = 2 };
+
+int plan_pack(int64_t D, int64_t esize, int64_t rows, bool in_aligned, int send_align) {
+    if (!(fast_d(D, esize) && rows < (int64_t(1) << 31) && in_aligned && send_align >= 4))
+        return kPackPathElems;
+    return send_align < 16 ? kPackPathRows : kPackPathLds;
+}
+
+int send_alignment(const void* p, int64_t esize) {
+    return aligned(p, 16) ? 16 : (aligned(p, 4) ? 4 : int(esize));
+}
+
 template <typename T>
-void launch_pack(bool fast, const void* attn_out, const float* lse, int64_t B, int64_t H,
+void launch_pack(int kind, const void* attn_out, const float* lse, int64_t B, int64_t H,
                  int64_t Hl, int64_t D, int64_t rows, int64_t total, void* send, hipStream_t st) {
     const T* in = static_cast<const T*>(attn_out);
     T* dst = static_cast<T*>(send);
-    if (fast) {
-        const uint32_t g = uint32_t(D / (16 / sizeof(T)));
-        const uint32_t rpb = kBlock / g;
-        const unsigned blocks = unsigned((rows + rpb * kPackRows - 1) / (rpb * kPackRows));
-        if (aligned(send, 16))
-            launch(pack_lds_kernel<T>, dim3(blocks), dim3(kBlock), 0, st, in, lse, uint32_t(rows),
-                   make_fastdiv(g), rpb, make_fastdiv(uint32_t(Hl)), make_fastdiv(uint32_t(B)),
-                   uint32_t(H), int(D), dst);
-        else
-            launch(pack_rows_kernel<T>, dim3(blocks), dim3(kBlock), 0, st, in, lse, uint32_t(rows),
-                   make_fastdiv(g), rpb, make_fastdiv(uint32_t(Hl)), make_fastdiv(uint32_t(B)),
-                   uint32_t(H), int(D), dst);
-    } else {
+    if (kind == kPackPathElems) {
         launch(pack_elems_kernel<T>, dim3(general_grid(total)), dim3(kBlock), 0, st, in, lse, B,
                H, Hl, D, total, dst);
+        return;
     }
+    const uint32_t g = uint32_t(D / (16 / sizeof(T)));
+    const uint32_t rpb = kBlock / g;
+    const unsigned blocks = unsigned((rows + rpb * kPackRows - 1) / (rpb * kPackRows));
+    if (kind == kPackPathRows)
+        launch(pack_rows_kernel<T>, dim3(blocks), dim3(kBlock), 0, st, in, lse, uint32_t(rows),
+               make_fastdiv(g), rpb, make_fastdiv(uint32_t(Hl)), make_fastdiv(uint32_t(B)),
+               uint32_t(H), int(D), dst);
+    else
+        launch(pack_lds_kernel<T>, dim3(blocks), dim3(kBlock), 0, st, in, lse, uint32_t(rows),
+               make_fastdiv(g), rpb, make_fastdiv(uint32_t(Hl)), make_fastdiv(uint32_t(B)),
+               uint32_t(H), int(D), dst);
 }
 
 template <typename T>
@@ -828,6 +845,21 @@ const char* lsec_status_string(int status) {
         case LSEC_ERR_TOKEN_DIM: return "token_dim must be 1 or 2";
         case LSEC_ERR_RANK: return "rank must be in [0, N)";
         default: return "unknown status";
+    }
+}
+
+const char* lsec_pack_path(int64_t N, int64_t B, int64_t H, int64_t D, int dtype, int in_aligned,
+                           int send_align) {
+    Dtype dt;
+    if (N < 1 || B < 1 || H < 1 || D < 1 || H % N != 0 || !parse_dtype(dtype, false, &dt))
+        return "none";
+    int64_t rows;
+    if (!mul_ok(B, H, &rows)) return "none";
+    const int sa = send_align >= 16 ? 16 : (send_align >= 4 ? 4 : int(dt.esize));
+    switch (plan_pack(D, dt.esize, rows, in_aligned != 0, sa)) {
+        case kPackPathLds: return "pack_lds_kernel";
+        case kPackPathRows: return "pack_rows_kernel";
+        default: return "pack_elems_kernel";
     }
 }
 
@@ -965,12 +997,12 @@ int lsec_pack_send(const void* attn_out, const float* attn_lse, int64_t N, int64
     const int64_t Hl = H / N;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const bool fast = fast_d(D, dt.esize) && rows < (int64_t(1) << 31) && aligned(attn_out, 16) &&
-                      aligned(send, 4);
+    const int kind =
+        plan_pack(D, dt.esize, rows, aligned(attn_out, 16), send_alignment(send, dt.esize));
     if (dt.esize == 4)
-        launch_pack<uint32_t>(fast, attn_out, attn_lse, B, H, Hl, D, rows, total, send, st);
+        launch_pack<uint32_t>(kind, attn_out, attn_lse, B, H, Hl, D, rows, total, send, st);
     else
-        launch_pack<uint16_t>(fast, attn_out, attn_lse, B, H, Hl, D, rows, total, send, st);
+        launch_pack<uint16_t>(kind, attn_out, attn_lse, B, H, Hl, D, rows, total, send, st);
     return launch_status();
 }
 

@@ -40,7 +40,7 @@ def test_header_declares_expected_entry_points():
     for n in ("lsec_combine", "lsec_merge", "lsec_pack_send", "lsec_unpack_combine",
               "lsec_unpack", "lsec_pack_dim", "lsec_status_string", "lsec_version",
               "lsec_combine_planes", "lsec_combine_planes_valid", "lsec_correct_partial",
-              "lsec_combine_path"):
+              "lsec_combine_path", "lsec_pack_path"):
         assert n in _declared([HEADER])
     for n in ("lsec_floor_empty", "lsec_floor_read", "lsec_floor_read_blocks", "lsec_floor_copy",
               "lsec_time_next_launch"):
@@ -181,6 +181,30 @@ def test_python_binding_rejects_bad_tensors():
 ])
 def test_combine_path(lib, args, want):
     assert lib.lsec_combine_path(*args).decode() == want
+
+
+@pytest.mark.parametrize("args,want", [
+    # N, B, H, D, dtype, in_aligned, send_align
+    ((8, 2048, 64, 128, 0, 1, 16), "pack_lds_kernel"),      # the packed workload
+    ((8, 2048, 64, 128, 1, 1, 16), "pack_lds_kernel"),      # fp16
+    ((1, 3, 4, 128, 0, 1, 64), "pack_lds_kernel"),          # N = 1, odd B
+    ((8, 2048, 64, 128, 2, 1, 16), "pack_lds_kernel"),      # fp32 rows
+    ((8, 2048, 48, 128, 0, 1, 16), "pack_lds_kernel"),      # Hl = 6
+    ((8, 2048, 64, 256, 0, 1, 16), "pack_lds_kernel"),      # D = 256
+    ((2, 4, 4, 1024, 2, 1, 16), "pack_lds_kernel"),         # fp32: 256 lanes per row
+    ((2, 4, 4, 2048, 2, 1, 16), "pack_elems_kernel"),       # fp32: D > 1024
+    ((8, 2048, 64, 128, 0, 1, 4), "pack_rows_kernel"),      # send buffer 4-byte aligned
+    ((8, 2048, 64, 128, 0, 1, 8), "pack_rows_kernel"),
+    ((8, 2048, 64, 128, 0, 0, 16), "pack_elems_kernel"),    # attn_out not 16-byte aligned
+    ((8, 2048, 64, 128, 0, 1, 2), "pack_elems_kernel"),     # send buffer 2-byte aligned
+    ((8, 16, 64, 12, 0, 1, 16), "pack_elems_kernel"),       # D % 8 != 0
+    ((8, 16, 60, 128, 0, 1, 16), "none"),                   # H % N != 0
+    ((8, 0, 64, 128, 0, 1, 16), "none"),                    # B = 0
+    ((8, 16, 64, 128, 256, 1, 16), "none"),                 # no fp32-result flag on a pack
+    ((8, 16, 64, 128, 7, 1, 16), "none"),                   # unknown dtype
+])
+def test_pack_path(lib, args, want):
+    assert lib.lsec_pack_path(*args).decode() == want
 
 
 def test_merge_validation(lib):

@@ -414,6 +414,44 @@ def test_pack_unpack_shapes(lsec, N, B, H, D, dtype):
     assert_lse_close(L, L_ref)
 
 
+@pytest.mark.parametrize("N,B,H,dtype,offset", [
+    (1, 3, 4, "bf16", 0),      # N = 1
+    (2, 7, 8, "f16", 0),       # Hl = 4, ragged B
+    (4, 5, 48, "bf16", 0),     # Hl = 12
+    (16, 33, 256, "f16", 0),   # Hl = 16
+    (3, 129, 12, "bf16", 0),   # N = 3
+    (4, 1001, 16, "bf16", 0),  # 16016 rows: 251 blocks, the last one partly filled
+    (4, 37, 16, "f16", 16),    # buffers 16 bytes into their allocations
+])
+def test_pack_lds_shapes(lsec, N, B, H, dtype, offset):
+    """The LDS pack over several heads per rank, ragged token counts, grids
+    long enough for the XCD-ordered walk and buffers 16 bytes into their
+    allocations: the send buffer must equal the oracle's bit for bit, the LSE
+    tails included (NaN payloads, infinities, -0 and subnormals)."""
+    D = 128
+    _announce(f"pack_lds N={N} B={B} H={H} {dtype} offset={offset}")
+    assert lsec.lsec_pack_path(N, B, H, D, TDT[dtype]) == "pack_lds_kernel"
+    o, l = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=91 + N + B, special=SPECIALS)
+    o, l = o[0], l[0]
+    lb = l.view(np.uint32)
+    lb[0, 0] = 0x7FC0BEEF            # NaN payload
+    lb[-1, -1] = 0x80000000          # -0
+    lb[B // 2, H // 2] = 0x00000003  # subnormal
+    lb[B - 1, 0] = 0xFF800000        # -inf
+    e = offset // 2                  # elements of the offset
+    oflat = torch.empty(o.size + e, dtype=TDT[dtype], device=DEV)
+    og = oflat[e:].view(B, H, D)
+    og.copy_(to_dev(o, dtype, DEV))
+    lflat = torch.empty(l.size + offset // 4, dtype=torch.float32, device=DEV)
+    lg = lflat[offset // 4:].view(B, H)
+    lg.copy_(f32_to_dev(l, DEV))
+    sflat = torch.empty(B * H * (D + 2) + e, dtype=TDT[dtype], device=DEV)
+    send = sflat[e:].view(N, B, H // N, D + 2)
+    lsec.lsec_pack_send(og, lg, N, send=send)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(send), oracle.pack_send(o, l, N))
+
+
 def test_misaligned_buffers_take_general_path(lsec):
     """Views that start 2 bytes into an allocation (only element-aligned)."""
     N, B, H, D = 4, 6, 5, 128
