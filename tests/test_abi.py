@@ -47,6 +47,45 @@ def test_header_declares_expected_entry_points():
         assert n in names
 
 
+def _prototypes(headers=None):
+    """{name: (return type, [parameter types])} of every function include/*.h
+    declares (parameter names dropped)."""
+    protos = {}
+    for h in headers or HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^([A-Za-z_][\w \t\*]*?)\b(lsec_\w+)\s*\(([^)]*)\)\s*;", src,
+                             flags=re.M):
+            params = " ".join(m.group(3).split())
+            decls = [] if params in ("", "void") else [d.strip() for d in params.split(",")]
+            types = [re.sub(r"\s*\b\w+$", "", d) if re.search(r"[\w*]\s+\**\w+$", d) else d
+                     for d in decls]
+            protos[m.group(2)] = (" ".join(m.group(1).split()), types)
+    return protos
+
+
+def _ctype(c_type, is_return=False):
+    t = c_type.replace(" ", "")
+    if is_return and t == "constchar*":
+        return ctypes.c_char_p
+    if "*" in t:
+        return ctypes.c_void_p
+    return {"int": ctypes.c_int, "int64_t": ctypes.c_int64}[t]
+
+
+def test_binding_signatures_match_the_headers(lib):
+    """Every declared function has ctypes argtypes / restype in the binding,
+    and they match the header's parameter list one for one (a pointer is
+    c_void_p, int64_t c_int64, int c_int; const char* returns c_char_p)."""
+    protos = _prototypes()
+    assert len(protos) == len(_declared())
+    for name, (ret, params) in protos.items():
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None, f"{name}: the binding sets no argtypes"
+        assert list(fn.argtypes) == [_ctype(p) for p in params], \
+            f"{name}: argtypes {fn.argtypes} against the header's ({', '.join(params)})"
+        assert fn.restype == _ctype(ret, is_return=True), f"{name}: restype {fn.restype} against {ret}"
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
