@@ -250,10 +250,11 @@ const char* lsec_combine_path(int64_t N, int64_t B, int64_t H, int64_t D, int dt
  * launches for these sizes and `dtype` (as passed to it; no LSEC_OUT_FP32),
  * given whether attn_out is 16-byte aligned (in_aligned != 0) and the
  * alignment of the send buffer in bytes (send_align: 16 or more, 4 to 15, or
- * less). Returns a static string: "pack_lds_kernel" (whole 16-byte chunks of
- * D, 16-byte aligned buffers), "pack_rows_kernel" (a send buffer aligned to 4
- * bytes only), "pack_elems_kernel" (any other), or "none" when the arguments
- * are invalid. Touches no GPU state.
+ * less). Returns a static string: "pack_pipe_kernel" (whole 16-byte chunks
+ * of D, 16-byte aligned buffers: rows assembled in LDS, a persistent grid),
+ * "pack_rows_kernel" (a send buffer aligned to 4 bytes only),
+ * "pack_elems_kernel" (any other), or "none" when the arguments are invalid.
+ * Touches no GPU state.
  */
 const char* lsec_pack_path(int64_t N, int64_t B, int64_t H, int64_t D, int dtype, int in_aligned,
                            int send_align);

@@ -224,13 +224,13 @@ def test_combine_path(lib, args, want):
 
 @pytest.mark.parametrize("args,want", [
     # N, B, H, D, dtype, in_aligned, send_align
-    ((8, 2048, 64, 128, 0, 1, 16), "pack_lds_kernel"),      # the packed workload
-    ((8, 2048, 64, 128, 1, 1, 16), "pack_lds_kernel"),      # fp16
-    ((1, 3, 4, 128, 0, 1, 64), "pack_lds_kernel"),          # N = 1, odd B
-    ((8, 2048, 64, 128, 2, 1, 16), "pack_lds_kernel"),      # fp32 rows
-    ((8, 2048, 48, 128, 0, 1, 16), "pack_lds_kernel"),      # Hl = 6
-    ((8, 2048, 64, 256, 0, 1, 16), "pack_lds_kernel"),      # D = 256
-    ((2, 4, 4, 1024, 2, 1, 16), "pack_lds_kernel"),         # fp32: 256 lanes per row
+    ((8, 2048, 64, 128, 0, 1, 16), "pack_pipe_kernel"),      # the packed workload
+    ((8, 2048, 64, 128, 1, 1, 16), "pack_pipe_kernel"),      # fp16
+    ((1, 3, 4, 128, 0, 1, 64), "pack_pipe_kernel"),          # N = 1, odd B
+    ((8, 2048, 64, 128, 2, 1, 16), "pack_pipe_kernel"),      # fp32 rows
+    ((8, 2048, 48, 128, 0, 1, 16), "pack_pipe_kernel"),      # Hl = 6
+    ((8, 2048, 64, 256, 0, 1, 16), "pack_pipe_kernel"),      # D = 256
+    ((2, 4, 4, 1024, 2, 1, 16), "pack_pipe_kernel"),         # fp32: 256 lanes per row
     ((2, 4, 4, 2048, 2, 1, 16), "pack_elems_kernel"),       # fp32: D > 1024
     ((8, 2048, 64, 128, 0, 1, 4), "pack_rows_kernel"),      # send buffer 4-byte aligned
     ((8, 2048, 64, 128, 0, 1, 8), "pack_rows_kernel"),

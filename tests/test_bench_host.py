@@ -52,14 +52,14 @@ def _write_counters(path, counter, rows):
 def test_traffic_record_scales_by_the_copy_calibration(tmp_path):
     alg = 1000 * 1024
     line = {"config": {"workload": "packed"},
-            "roofline": {"kernel": "pack_lds_kernel (bf16)", "bytes_per_launch": alg},
-            "kernels": [{"kernel": "pack_lds_kernel (bf16)", "bytes": alg},
+            "roofline": {"kernel": "pack_pipe_kernel (bf16)", "bytes_per_launch": alg},
+            "kernels": [{"kernel": "pack_pipe_kernel (bf16)", "bytes": alg},
                         {"kernel": "combine_tiled_kernel S=1 (bf16, N=8, D=128, packed rows)",
                          "bytes": 2 * alg}]}
     log = tmp_path / "bench.log"
     log.write_text("[bench] something\n" + json.dumps(line) + "\n")
     gib_kib = float(1 << 20)
-    pack = "void lsec_detail::(anonymous namespace)::pack_lds_kernel<unsigned short>(...)"
+    pack = "void lsec_detail::(anonymous namespace)::pack_pipe_kernel<unsigned short>(...)"
     comb = "void lsec_detail::(anonymous namespace)::combine_tiled_kernel<0, 8, 16, 1, true, false>(...)"
     copy = "__amd_rocclr_copyBuffer"
     # FETCH counts 0.5 per KiB read, WRITE 1.0 per KiB written (as measured on the device)
@@ -71,7 +71,7 @@ def test_traffic_record_scales_by_the_copy_calibration(tmp_path):
                      (copy, gib_kib), (copy, gib_kib), (copy, gib_kib)])
     rec = bench.traffic_record(str(log), str(tmp_path / "f"), str(tmp_path / "w"), "abc123")
     assert rec["workload"] == "packed"
-    assert rec["kernel"] == "pack_lds_kernel (bf16)"
+    assert rec["kernel"] == "pack_pipe_kernel (bf16)"
     assert rec["counters_taken_at_commit"] == "abc123"
     assert rec["copy_calibration"]["fetch_factor"] == pytest.approx(0.5)
     assert rec["copy_calibration"]["write_factor"] == pytest.approx(1.0)

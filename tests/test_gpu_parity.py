@@ -420,17 +420,20 @@ def test_pack_unpack_shapes(lsec, N, B, H, D, dtype):
     (4, 5, 48, "bf16", 0),     # Hl = 12
     (16, 33, 256, "f16", 0),   # Hl = 16
     (3, 129, 12, "bf16", 0),   # N = 3
-    (4, 1001, 16, "bf16", 0),  # 16016 rows: 251 blocks, the last one partly filled
+    (4, 1001, 16, "bf16", 0),  # 16016 rows: 251 tiles, the last one partly filled
+    (4, 4099, 16, "bf16", 0),  # 65584 rows: 1025 tiles of 64 rows on 1024 blocks
+    (8, 5000, 64, "f16", 0),   # 320000 rows: 5000 tiles, four or five per block
     (4, 37, 16, "f16", 16),    # buffers 16 bytes into their allocations
 ])
-def test_pack_lds_shapes(lsec, N, B, H, dtype, offset):
-    """The LDS pack over several heads per rank, ragged token counts, grids
-    long enough for the XCD-ordered walk and buffers 16 bytes into their
-    allocations: the send buffer must equal the oracle's bit for bit, the LSE
-    tails included (NaN payloads, infinities, -0 and subnormals)."""
+def test_pack_pipe_shapes(lsec, N, B, H, dtype, offset):
+    """The pipelined LDS pack over several heads per rank, ragged token
+    counts, more tiles than its grid has blocks (blocks that walk two tiles,
+    the last one partly filled) and buffers 16 bytes into their allocations:
+    the send buffer must equal the oracle's bit for bit, the LSE tails
+    included (NaN payloads, infinities, -0 and subnormals)."""
     D = 128
-    _announce(f"pack_lds N={N} B={B} H={H} {dtype} offset={offset}")
-    assert lsec.lsec_pack_path(N, B, H, D, TDT[dtype]) == "pack_lds_kernel"
+    _announce(f"pack_pipe N={N} B={B} H={H} {dtype} offset={offset}")
+    assert lsec.lsec_pack_path(N, B, H, D, TDT[dtype]) == "pack_pipe_kernel"
     o, l = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=91 + N + B, special=SPECIALS)
     o, l = o[0], l[0]
     lb = l.view(np.uint32)
@@ -450,6 +453,26 @@ def test_pack_lds_shapes(lsec, N, B, H, dtype, offset):
     lsec.lsec_pack_send(og, lg, N, send=send)
     torch.cuda.synchronize()
     assert np.array_equal(bits_of(send), oracle.pack_send(o, l, N))
+
+
+@pytest.mark.parametrize("N,B,H,D,dtype", [
+    (2, 2049, 16, 256, "bf16"),   # 32 rows per tile: 1025 tiles, the last 16 rows
+    (4, 1025, 16, 512, "bf16"),   # 16 rows per tile: 1025 tiles, the last 16 rows
+    (2, 21761, 16, 24, "f16"),    # 3 lanes per row, 340 rows per tile: 1025 tiles
+    (2, 2049, 16, 128, "f32"),    # fp32 rows, 32 per tile: 1025 tiles
+    (2, 257, 16, 1024, "f32"),    # 256 lanes per row, 4 rows per tile: 1028 tiles
+])
+def test_pack_pipe_tile_walk(lsec, N, B, H, D, dtype):
+    """Row widths whose tiles outnumber the pipelined pack's blocks, so blocks
+    walk several tiles through both LDS stages and the last tile is ragged:
+    bit for bit the oracle's send buffer."""
+    _announce(f"pack_pipe walk N={N} B={B} H={H} D={D} {dtype}")
+    assert lsec.lsec_pack_path(N, B, H, D, TDT[dtype]) == "pack_pipe_kernel"
+    o, l = synth.custom_inputs(1, B, H, D, dtype=dtype, seed=7 * D + B, special=SPECIALS)
+    o, l = o[0], l[0]
+    send = lsec.lsec_pack_send(to_dev(o, dtype, DEV), f32_to_dev(l, DEV), N)
+    torch.cuda.synchronize()
+    assert np.array_equal(elem_bits_of(send, dtype), oracle.pack_send(o, l, N, dtype=dtype))
 
 
 def test_misaligned_buffers_take_general_path(lsec):
