@@ -130,3 +130,47 @@ def test_valid_count_changes_between_replays_of_one_graph(lsec):
             assert_lse_close(out_lse[:tv], L_ref, f"offsets {offsets}")
         assert bool(torch.all(out[tv:] == -7.0)) and bool(torch.all(out_lse[tv:] == -7.0)), \
             f"offsets {offsets}: a padding row was written"
+
+
+FIRST_PACK_IN_CAPTURE = r"""
+import sys
+import torch
+sys.path.insert(0, sys.argv[1])
+import lse_weighted_merge_combine_amd as lsec
+lsec.load_library()
+dev = torch.device("cuda:0")
+N, B, H, D = 8, 3000, 64, 128  # 192,000 send rows: 3,000 tiles, several per block
+assert lsec.lsec_pack_path(N, B, H, D) == "pack_pipe_kernel"
+gen = torch.Generator().manual_seed(5)
+a = torch.randn(B, H, D, generator=gen).to(torch.bfloat16).to(dev)
+l = (torch.rand(B, H, generator=gen) * 20 - 5).to(dev)
+send = torch.empty((N, B, H // N, D + 2), dtype=torch.bfloat16, device=dev)
+torch.cuda.synchronize()
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):
+    lsec.lsec_pack_send(a, l, N, send=send)  # the first pack of this process
+for i in range(3):
+    send.zero_()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ref = lsec.lsec_pack_send(a, l, N)
+    torch.cuda.synchronize()
+    assert torch.equal(send.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+print("first pack captured: replays match the eager pack")
+"""
+
+
+def test_first_pack_of_a_process_inside_capture(lsec):
+    """The pack sizes its persistent grid from the device's compute units,
+    queried on the first pack call of a process; a process whose first pack is
+    captured in a graph (run here in a fresh child process) must replay the
+    same bytes as an eager pack."""
+    import subprocess
+    import sys
+    print("[case] first pack of a fresh process inside graph capture", flush=True)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", FIRST_PACK_IN_CAPTURE, root],
+                         capture_output=True, text=True, timeout=240)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-4000:]
+    assert "replays match" in res.stdout
