@@ -507,7 +507,7 @@ LSE_TOL = 1e-5                                    # absolute
 
 def host_threads() -> int:
     """The host threads used for oracle work: the CPUs this process may use,
-    at most 16 (a GPU machine's share of its host for one GPU)."""
+    at most 16 (one GPU's share of a host's CPUs)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

@@ -94,7 +94,7 @@ def assert_lse_close(L_gpu: torch.Tensor, L_ref: np.ndarray, what: str = "") -> 
 
 def host_threads() -> int:
     """Threads for host-side oracle work: the CPUs this process may use, at
-    most 16 (a GPU machine's share for one GPU)."""
+    most 16 (one GPU's share of a host's CPUs)."""
     import os
     try:
         n = len(os.sched_getaffinity(0))
