@@ -946,6 +946,8 @@ def main():
             if use_cpu:
                 entry["parity"] = r["parity"]
                 entry["oracle"] = r["cpu"]
+            # the outputs the parity check above saw, for the rotation's check below
+            flush_outputs = {k: t.cpu() for k, t in r["work"].outputs.items()}
             del r
             torch.cuda.empty_cache()
             if sname in SUITE_ROTATION:
@@ -956,9 +958,14 @@ def main():
                     "cache": f"cold: {sets} input sets in rotation "
                              f"({sets * rr['step_bytes'] / 1e9:.1f} GB), no flush kernel",
                     "kernels": kernel_records(rr),
-                    "outputs_unchanged_by_timed_steps": rr["unchanged"]}
+                    "outputs_unchanged_by_timed_steps": rr["unchanged"],
+                    # the first set holds the same seeded inputs as the flush run
+                    "outputs_identical_to_the_flush_run": all(
+                        same_bits(rr["work"].outputs[k].cpu(), t)
+                        for k, t in flush_outputs.items())}
                 del rr
                 torch.cuda.empty_cache()
+            del flush_outputs
             suite.append(entry)
 
     r = measure(name, dev, args.steps, args.warmup, args.flush_mib, floor=args.floor,
