@@ -2,9 +2,10 @@
 
 Each output (and global LSE) buffer is a view inside a larger allocation whose
 bands before and after it hold a sentinel byte. After the call the bands must
-be unchanged, and the view must hold the same bits as the same call on plain
-tensors (whose parity with the oracle the other GPU tests check). One case per
-kernel family, with ragged tails, multi-tile walks and odd widths.
+be unchanged, the view must hold the same bits as the same call on plain
+tensors (whose parity with the oracle the other GPU tests check), and the
+inputs must be bit for bit what they were. One case per kernel family, with
+ragged tails, multi-tile walks and odd widths.
 """
 import math
 import os
@@ -66,12 +67,19 @@ def _packed(lsec, N, B, Hl, D, dtype, seed):
     return lsec.lsec_pack_send(to_dev(o[0], dtype, DEV), f32_to_dev(l[0], DEV), N)
 
 
-def _check(results_guarded, results_plain, guards, what):
+def _check(results_guarded, results_plain, guards, what, inputs=()):
+    """`inputs`: (tensor, its copy from before the calls) pairs."""
     torch.cuda.synchronize()
     for g in guards:
         assert g.bands_intact(), f"{what}: a write outside the output buffer"
     for a, b in zip(results_guarded, results_plain):
         assert _same_bits(a, b), f"{what}: guarded and plain results differ"
+    for now, before in inputs:
+        assert _same_bits(now, before), f"{what}: an input was written"
+
+
+def _kept(*tensors):
+    return [(t, t.clone()) for t in tensors]
 
 
 @pytest.mark.parametrize("N,B,H,D,dtype,out_f32", [
@@ -88,12 +96,13 @@ def _check(results_guarded, results_plain, guards, what):
 def test_combine_writes_only_its_outputs(lsec, N, B, H, D, dtype, out_f32):
     print(f"[case] combine bounds N={N} B={B} H={H} D={D} {dtype} out_f32={out_f32}", flush=True)
     og, lg = _inputs(N, B, H, D, dtype, seed=N * 7 + B)
+    kept = _kept(og, lg)
     rdt = torch.float32 if (out_f32 or dtype == "f32") else TDT[dtype]
     out, out_lse = Guarded((B, H, D), rdt), Guarded((B, H), torch.float32)
     kw = {"out_dtype": torch.float32} if out_f32 else {}
     lsec.lsec_combine(og, lg, return_lse=True, out=out.t, out_lse=out_lse.t, **kw)
     y, L = lsec.lsec_combine(og, lg, return_lse=True, **kw)
-    _check((out.t, out_lse.t), (y, L), (out, out_lse), "combine")
+    _check((out.t, out_lse.t), (y, L), (out, out_lse), "combine", kept)
 
 
 @pytest.mark.parametrize("N,B,Hl,D,dtype", [
@@ -106,14 +115,15 @@ def test_combine_writes_only_its_outputs(lsec, N, B, H, D, dtype, out_f32):
 def test_unpack_combine_and_unpack_write_only_their_outputs(lsec, N, B, Hl, D, dtype):
     print(f"[case] receive-side bounds N={N} B={B} Hl={Hl} D={D} {dtype}", flush=True)
     recv = _packed(lsec, N, B, Hl, D, dtype, seed=B + D)
+    kept = _kept(recv)
     out, out_lse = Guarded((B, Hl, D), TDT[dtype]), Guarded((B, Hl), torch.float32)
     lsec.lsec_unpack_combine(recv, return_lse=True, out=out.t, out_lse=out_lse.t)
     y, L = lsec.lsec_unpack_combine(recv, return_lse=True)
-    _check((out.t, out_lse.t), (y, L), (out, out_lse), "unpack_combine")
+    _check((out.t, out_lse.t), (y, L), (out, out_lse), "unpack_combine", kept)
     outs, lses = Guarded((N, B, Hl, D), TDT[dtype]), Guarded((N, B, Hl), torch.float32)
     lsec.lsec_unpack(recv, outputs=outs.t, lses=lses.t)
     uo, ul = lsec.lsec_unpack(recv)
-    _check((outs.t, lses.t), (uo, ul), (outs, lses), "unpack")
+    _check((outs.t, lses.t), (uo, ul), (outs, lses), "unpack", kept)
 
 
 @pytest.mark.parametrize("N,B,H,D,dtype,offset", [
@@ -126,11 +136,12 @@ def test_unpack_combine_and_unpack_write_only_their_outputs(lsec, N, B, Hl, D, d
 def test_pack_writes_only_the_send_buffer(lsec, N, B, H, D, dtype, offset):
     print(f"[case] pack bounds N={N} B={B} H={H} D={D} {dtype} offset={offset}", flush=True)
     og, lg = _inputs(1, B, H, D, dtype, seed=H + D)
+    kept = _kept(og, lg)
     P = lsec.lsec_pack_dim(TDT[dtype])
     send = Guarded((N, B, H // N, D + P), TDT[dtype], offset=offset)
     lsec.lsec_pack_send(og[0], lg[0], N, send=send.t)
     ref = lsec.lsec_pack_send(og[0], lg[0], N)
-    _check((send.t,), (ref,), (send,), "pack_send")
+    _check((send.t,), (ref,), (send,), "pack_send", kept)
 
 
 @pytest.mark.parametrize("token_dim", [1, 2])
@@ -138,20 +149,22 @@ def test_merge_writes_only_its_outputs(lsec, token_dim):
     print(f"[case] merge bounds token_dim={token_dim}", flush=True)
     N, A, C, D = 8, 37, 5, 128
     og, lg = _inputs(N, A, C, D, "bf16", seed=token_dim)
+    kept = _kept(og, lg)
     y, L = lsec.lsec_merge(og, lg, token_dim, return_lse=True)
     out, out_lse = Guarded(tuple(y.shape), torch.bfloat16), Guarded(tuple(L.shape), torch.float32)
     lsec.lsec_merge(og, lg, token_dim, return_lse=True, out=out.t, out_lse=out_lse.t)
-    _check((out.t, out_lse.t), (y, L), (out, out_lse), "merge")
+    _check((out.t, out_lse.t), (y, L), (out, out_lse), "merge", kept)
 
 
 def test_correct_partial_writes_only_its_outputs(lsec):
     print("[case] corrected partial bounds", flush=True)
     N, B, H, D = 8, 50, 16, 512
     og, lg = _inputs(N, B, H, D, "bf16", seed=5)
+    kept = _kept(og, lg)
     out, out_lse = Guarded((B, H, D), torch.bfloat16), Guarded((B, H), torch.float32)
     lsec.lsec_correct_partial(lg, 3, og[3], return_lse=True, out=out.t, out_lse=out_lse.t)
     y, L = lsec.lsec_correct_partial(lg, 3, og[3], return_lse=True)
-    _check((out.t, out_lse.t), (y, L), (out, out_lse), "correct_partial")
+    _check((out.t, out_lse.t), (y, L), (out, out_lse), "correct_partial", kept)
 
 
 def test_combine_planes_writes_only_its_outputs(lsec):
@@ -159,10 +172,11 @@ def test_combine_planes_writes_only_its_outputs(lsec):
     print("[case] combine_planes bounds", flush=True)
     W, Tmax, T, H, D = 8, 96, 61, 8, 128
     og, lg = _inputs(W, Tmax, H, D, "bf16", seed=9)
+    kept = _kept(og, lg)
     out, out_lse = Guarded((T, H, D), torch.bfloat16), Guarded((T, H), torch.float32)
     lsec.lsec_combine_planes(og, lg, T, return_lse=True, out=out.t, out_lse=out_lse.t)
     y, L = lsec.lsec_combine_planes(og, lg, T, return_lse=True)
-    _check((out.t, out_lse.t), (y, L), (out, out_lse), "combine_planes")
+    _check((out.t, out_lse.t), (y, L), (out, out_lse), "combine_planes", kept)
     qsl = torch.tensor([0, 20, 45], dtype=torch.int32, device=DEV)
     out2, lse2 = Guarded((T, H, D), torch.bfloat16), Guarded((T, H), torch.float32)
     lsec.lsec_combine_planes(og, lg, T, return_lse=True, out=out2.t, out_lse=lse2.t,
