@@ -8,8 +8,12 @@
  *
  * Cases: the combine (bf16, tiled path, base e, global LSE), the combine
  * (fp16, row path, base 2), an fp32 result from bf16 partials, pack_send
- * (bit-exact), unpack_combine on the oracle's packed buffer, unpack (bit-exact)
- * and the error statuses of invalid arguments (nothing is launched).
+ * (bit-exact; also over more tiles than the pack's grid has blocks),
+ * unpack_combine on the oracle's packed buffer, unpack (bit-exact), the
+ * token-major merge (both token dims), the corrected partial, the combine of
+ * strided receive planes (with and without the valid count on the device), the
+ * path diagnostics, the status strings and the error statuses of invalid
+ * arguments (nothing is launched).
  * Exit status 0 when every case passes, 1 on a mismatch, 2 when no GPU is
  * usable.
  */
@@ -39,6 +43,11 @@ int oracle_unpack(const void* recv, int64_t N, int64_t B, int64_t Hl, int64_t D,
                   void* outputs, float* lses);
 int oracle_unpack_combine(const void* recv, int dtype, int64_t N, int64_t B, int64_t Hl,
                           int64_t D, int base2, double* y, double* L);
+int oracle_merge(const void* outputs, int dtype, const float* lses, int64_t N, int64_t A,
+                 int64_t C, int64_t D, int token_dim, int base2, double* y, double* L);
+int oracle_correct_partial(const float* lses, int64_t N, int64_t rank, const void* partial,
+                           int dtype, int64_t B, int64_t H, int64_t D, int base2, double* y,
+                           double* L);
 
 enum { DIST_UNIFORM = 0, DIST_NORMAL = 1 };
 enum { OUT_F32 = 1, OUT_BF16 = 2, OUT_F16 = 3 };
@@ -267,6 +276,153 @@ static void valid_count_case(void) {
     free(o), free(l), free(y), free(L), free(ov), free(lv), free(y_ref), free(L_ref);
 }
 
+/* A combining call's results [rows, D] (+ [rows]) copied back and checked. */
+static int fetch_and_check(void* d_y, float* d_L, int64_t rows, int64_t D, int res_dtype,
+                           const double* y_ref, const double* L_ref, double M) {
+    const size_t ybytes = (size_t)(rows * D) * (res_dtype == LSEC_FP32 ? 4 : 2);
+    void* y = malloc(ybytes);
+    float* L = malloc(sizeof(float) * (size_t)rows);
+    HIP_OK(hipMemcpy(y, d_y, ybytes, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(L, d_L, sizeof(float) * (size_t)rows, hipMemcpyDeviceToHost));
+    const int ok = close_enough(y, res_dtype, y_ref, rows * D, M, L, L_ref, rows);
+    free(y), free(L);
+    return ok;
+}
+
+static void merge_case(int token_dim) {
+    const int64_t N = 4, A = 13, C = 6, D = 128, rows = A * C, n_out = N * rows * D;
+    uint16_t* o = malloc(sizeof(uint16_t) * (size_t)n_out);
+    float* l = malloc(sizeof(float) * (size_t)(N * rows));
+    draw(50 + (uint32_t)token_dim, OUT_BF16, n_out, N * rows, o, l, -5.0, 15.0);
+    void* d_o = dev_copy(o, sizeof(uint16_t) * (size_t)n_out);
+    void* d_l = dev_copy(l, sizeof(float) * (size_t)(N * rows));
+    void* d_y = NULL;
+    float* d_L = NULL;
+    HIP_OK(hipMalloc(&d_y, sizeof(uint16_t) * (size_t)(rows * D)));
+    HIP_OK(hipMalloc((void**)&d_L, sizeof(float) * (size_t)rows));
+    const int st = lsec_merge(d_o, (const float*)d_l, N, A, C, D, token_dim, LSEC_BF16,
+                              LSEC_BASE_E, d_y, d_L, NULL);
+    HIP_OK(hipDeviceSynchronize());
+    double* y_ref = malloc(sizeof(double) * (size_t)(rows * D));
+    double* L_ref = malloc(sizeof(double) * (size_t)rows);
+    oracle_merge(o, LSEC_BF16, l, N, A, C, D, token_dim, 0, y_ref, L_ref);
+    check(st == LSEC_OK && fetch_and_check(d_y, d_L, rows, D, LSEC_BF16, y_ref, L_ref,
+                                           max_abs(o, LSEC_BF16, n_out)),
+          token_dim == 1 ? "merge bf16 N=4 A=13 C=6 D=128 token_dim 1"
+                         : "merge bf16 N=4 A=13 C=6 D=128 token_dim 2 (token-major store)");
+    HIP_OK(hipFree(d_o));
+    HIP_OK(hipFree(d_l));
+    HIP_OK(hipFree(d_y));
+    HIP_OK(hipFree(d_L));
+    free(o), free(l), free(y_ref), free(L_ref);
+}
+
+static void correct_case(void) {
+    const int64_t N = 8, B = 21, H = 16, D = 512, rank = 5, rows = B * H;
+    uint16_t* p = malloc(sizeof(uint16_t) * (size_t)(rows * D));
+    float* l = malloc(sizeof(float) * (size_t)(N * rows));
+    draw(60, OUT_BF16, rows * D, N * rows, p, l, -5.0, 15.0);
+    void* d_p = dev_copy(p, sizeof(uint16_t) * (size_t)(rows * D));
+    void* d_l = dev_copy(l, sizeof(float) * (size_t)(N * rows));
+    void* d_y = NULL;
+    float* d_L = NULL;
+    HIP_OK(hipMalloc(&d_y, sizeof(uint16_t) * (size_t)(rows * D)));
+    HIP_OK(hipMalloc((void**)&d_L, sizeof(float) * (size_t)rows));
+    const int st = lsec_correct_partial((const float*)d_l, N, rank, d_p, B, H, D, LSEC_BF16,
+                                        LSEC_BASE_2, d_y, d_L, NULL);
+    HIP_OK(hipDeviceSynchronize());
+    double* y_ref = malloc(sizeof(double) * (size_t)(rows * D));
+    double* L_ref = malloc(sizeof(double) * (size_t)rows);
+    oracle_correct_partial(l, N, rank, p, LSEC_BF16, B, H, D, 1, y_ref, L_ref);
+    check(st == LSEC_OK && fetch_and_check(d_y, d_L, rows, D, LSEC_BF16, y_ref, L_ref,
+                                           max_abs(p, LSEC_BF16, rows * D)),
+          "correct_partial bf16 N=8 B=21 H=16 D=512 rank 5 base 2");
+    HIP_OK(hipFree(d_p));
+    HIP_OK(hipFree(d_l));
+    HIP_OK(hipFree(d_y));
+    HIP_OK(hipFree(d_L));
+    free(p), free(l), free(y_ref), free(L_ref);
+}
+
+/* Planes of Tmax tokens of which the first T are combined (strided planes). */
+static void planes_case(void) {
+    const int64_t N = 4, Tmax = 50, T = 33, H = 4, D = 256, prow = Tmax * H, rows = T * H;
+    uint16_t* o = malloc(sizeof(uint16_t) * (size_t)(N * prow * D));
+    float* l = malloc(sizeof(float) * (size_t)(N * prow));
+    draw(70, OUT_F16, N * prow * D, N * prow, o, l, 0.0, 20.0);
+    void* d_o = dev_copy(o, sizeof(uint16_t) * (size_t)(N * prow * D));
+    void* d_l = dev_copy(l, sizeof(float) * (size_t)(N * prow));
+    void* d_y = NULL;
+    float* d_L = NULL;
+    HIP_OK(hipMalloc(&d_y, sizeof(uint16_t) * (size_t)(rows * D)));
+    HIP_OK(hipMalloc((void**)&d_L, sizeof(float) * (size_t)rows));
+    const int st = lsec_combine_planes(d_o, prow * D, (const float*)d_l, prow, N, T, H, D,
+                                       LSEC_FP16, LSEC_BASE_2, d_y, d_L, NULL);
+    HIP_OK(hipDeviceSynchronize());
+    uint16_t* ov = malloc(sizeof(uint16_t) * (size_t)(N * rows * D));
+    float* lv = malloc(sizeof(float) * (size_t)(N * rows));
+    for (int64_t n = 0; n < N; ++n) {
+        memcpy(ov + n * rows * D, o + n * prow * D, sizeof(uint16_t) * (size_t)(rows * D));
+        memcpy(lv + n * rows, l + n * prow, sizeof(float) * (size_t)rows);
+    }
+    double* y_ref = malloc(sizeof(double) * (size_t)(rows * D));
+    double* L_ref = malloc(sizeof(double) * (size_t)rows);
+    oracle_lse_combine(ov, LSEC_FP16, lv, N, T, H, D, 1, y_ref, L_ref);
+    check(st == LSEC_OK && fetch_and_check(d_y, d_L, rows, D, LSEC_FP16, y_ref, L_ref,
+                                           max_abs(ov, LSEC_FP16, N * rows * D)),
+          "combine_planes fp16 N=4 T=33 of 50 H=4 D=256 base 2");
+    HIP_OK(hipFree(d_o));
+    HIP_OK(hipFree(d_l));
+    HIP_OK(hipFree(d_y));
+    HIP_OK(hipFree(d_L));
+    free(o), free(l), free(ov), free(lv), free(y_ref), free(L_ref);
+}
+
+/* More send rows than the pack's persistent grid takes in one pass: 1025
+ * tiles of 64 rows, the last one partly filled. */
+static void pack_walk_case(void) {
+    const int64_t N = 4, B = 4099, H = 16, D = 128, rows = B * H;
+    const int64_t W = D + lsec_pack_dim(LSEC_BF16);
+    uint16_t* o = malloc(sizeof(uint16_t) * (size_t)(rows * D));
+    float* l = malloc(sizeof(float) * (size_t)rows);
+    draw(80, OUT_BF16, rows * D, rows, o, l, -5.0, 15.0);
+    const size_t send_bytes = sizeof(uint16_t) * (size_t)(rows * W);
+    void* d_o = dev_copy(o, sizeof(uint16_t) * (size_t)(rows * D));
+    void* d_l = dev_copy(l, sizeof(float) * (size_t)rows);
+    void* d_s = NULL;
+    HIP_OK(hipMalloc(&d_s, send_bytes));
+    const int st = lsec_pack_send(d_o, (const float*)d_l, N, B, H, D, LSEC_BF16, d_s, NULL);
+    HIP_OK(hipDeviceSynchronize());
+    uint16_t* s = malloc(send_bytes);
+    uint16_t* s_ref = malloc(send_bytes);
+    HIP_OK(hipMemcpy(s, d_s, send_bytes, hipMemcpyDeviceToHost));
+    oracle_pack_send(o, l, N, B, H, D, 2, s_ref);
+    check(st == LSEC_OK && memcmp(s, s_ref, send_bytes) == 0 &&
+              strcmp(lsec_pack_path(N, B, H, D, LSEC_BF16, 1, 16), "pack_pipe_kernel") == 0,
+          "pack_send bf16 N=4 B=4099 H=16 D=128, 1025 tiles (bit-exact)");
+    HIP_OK(hipFree(d_o));
+    HIP_OK(hipFree(d_l));
+    HIP_OK(hipFree(d_s));
+    free(o), free(l), free(s), free(s_ref);
+}
+
+static void diagnostics_cases(void) {
+    check(strcmp(lsec_combine_path(16, 16384, 32, 128, LSEC_BF16, 0, 1),
+                 "combine_tiled_kernel S=16") == 0 &&
+              strcmp(lsec_combine_path(8, 2048, 8, 128, LSEC_BF16, 1, 1), "combine_span_kernel") == 0 &&
+              strcmp(lsec_pack_path(8, 2048, 64, 128, LSEC_BF16, 1, 4), "pack_rows_kernel") == 0 &&
+              strcmp(lsec_pack_path(8, 2048, 60, 128, LSEC_BF16, 1, 16), "none") == 0,
+          "path diagnostics");
+    int ok = 1;
+    for (int code = LSEC_OK; code <= LSEC_ERR_RANK; ++code) {
+        const char* a = lsec_status_string(code);
+        ok &= a != NULL && strlen(a) > 0;
+        for (int other = LSEC_OK; other < code; ++other) ok &= strcmp(a, lsec_status_string(other)) != 0;
+    }
+    ok &= lsec_status_string(12345) != NULL;
+    check(ok, "a distinct status string for every status");
+}
+
 static void error_cases(void) {
     void* d = NULL;
     HIP_OK(hipMalloc(&d, 4096));
@@ -283,6 +439,12 @@ static void error_cases(void) {
           "odd address -> LSEC_ERR_ALIGNMENT");
     check(strlen(lsec_status_string(LSEC_ERR_SHAPE)) > 0 && lsec_pack_dim(LSEC_FP32) == 1,
           "status strings and pack dims");
+    check(lsec_merge(d, (const float*)d, 2, 1, 1, 8, 3, LSEC_BF16, LSEC_BASE_E, d, NULL, NULL) ==
+              LSEC_ERR_TOKEN_DIM,
+          "token_dim 3 -> LSEC_ERR_TOKEN_DIM");
+    check(lsec_correct_partial((const float*)d, 2, 2, d, 1, 1, 8, LSEC_BF16, LSEC_BASE_E, d, NULL,
+                               NULL) == LSEC_ERR_RANK,
+          "rank N -> LSEC_ERR_RANK");
     HIP_OK(hipFree(d));
 }
 
@@ -300,7 +462,13 @@ int main(void) {
     combine_case("combine bf16 -> fp32 N=4 B=33 H=4 D=256 base e + LSE", 33, 4, 33, 4, 256,
                  LSEC_BF16, LSEC_BASE_E, 1);
     packed_case();
+    pack_walk_case();
     valid_count_case();
+    planes_case();
+    merge_case(1);
+    merge_case(2);
+    correct_case();
+    diagnostics_cases();
     error_cases();
     printf("c_abi_check: %s\n", failures ? "FAILED" : "ok");
     return failures ? 1 : 0;
