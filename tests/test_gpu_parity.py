@@ -161,6 +161,8 @@ SHAPES = [
     (5, 9, 4, 64, "bf16", True),
     (7, 13, 3, 256, "bf16", False),   # tiled, N at run time
     (32, 6, 4, 128, "bf16", False),
+    (100, 5, 3, 128, "f16", True),    # row kernel, N far above 16
+    (257, 2, 2, 64, "bf16", False),   # row kernel, N = 257
     (9, 20, 2, 24, "bf16", True),     # 3 lanes per row, rows straddle waves
     (2, 3, 3, 2048, "f16", False),    # 256 lanes per row
     (4, 10, 3, 1000, "bf16", False),  # row kernel, 125 lanes per row
@@ -803,6 +805,99 @@ def test_all_shards_non_finite(lsec):
         torch.cuda.synchronize()
         assert torch.all(y == 0)
         assert torch.all(torch.isneginf(L))
+
+
+F32_MAX = float(np.finfo(np.float32).max)
+EXTREME_LSE_ROWS = [
+    [F32_MAX, -F32_MAX],           # the whole fp32 range between two shards
+    [3.0e38, 3.0e38],              # equal and huge: the mean, L = l + ln N
+    [-3.0e38, -3.0e38],            # equal and hugely negative, still finite
+    [1.0e-45, -1.0e-45, 0.0, -0.0],  # subnormal and signed-zero LSEs
+    [1.0e38, float("nan"), float("inf"), -1.0e38],
+    [80.0, -80.0, 0.0, 88.7],      # weights down to fp32 underflow
+    [-1.0e30, 5.0],
+]
+# The largest finite value of each 16-bit format (patterns); fp32 partials
+# use 1e38, since a weighted sum of fp32 maxima can round past the fp32 range
+# in any fp32 evaluation of the page's sum.
+EXTREME_OUT = {"bf16": 0x7F7F, "f16": 0x7BFF, "f32": np.float32(1e38)}
+
+
+def _extreme_inputs(N, B, H, D, dtype, seed):
+    o, l = synth.custom_inputs(N, B, H, D, dtype=dtype, seed=seed)
+    rows = l.reshape(N, B * H)
+    for r, pat in enumerate(EXTREME_LSE_ROWS):
+        for n in range(N):
+            rows[n, r] = pat[n % len(pat)]
+    flat = o.reshape(N, B * H, D)
+    flat[:, 1, :] = EXTREME_OUT[dtype]          # the equal, huge LSEs: their maxima
+    flat[0, 0, : D // 2] = EXTREME_OUT[dtype]   # the dominant shard of row 0
+    return o, l
+
+
+def _assert_rows_close(y, y_ref, o, dtype, what):
+    """Rows 0 and 1 hold the format's largest values; the tolerance of the
+    other rows is set by their own inputs."""
+    N, D = o.shape[0], o.shape[-1]
+    of = o.reshape(N, -1, D)
+    yf = y.reshape(-1, D)
+    rf = np.asarray(y_ref).reshape(-1, D)
+    assert_output_close(yf[:2], rf[:2], dtype, max_abs_input(of[:, :2], dtype), what)
+    assert_output_close(yf[2:], rf[2:], dtype, max_abs_input(of[:, 2:], dtype), what)
+
+
+def _assert_lse_close_fp32(L, L_ref, what):
+    """Global LSEs within 1e-5 plus two fp32 ulps of the exact value: beyond
+    |L| = 256 half an fp32 ulp alone exceeds 1e-5."""
+    got = L.cpu().numpy().astype(np.float64).reshape(-1)
+    want = np.asarray(L_ref, dtype=np.float64).reshape(-1)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: non-finite LSEs differ"
+    assert np.array_equal(got[~fin], want[~fin]), f"{what}: non-finite LSEs differ"
+    mag = np.abs(want[fin]).astype(np.float32)
+    ulp = np.spacing(np.nextafter(mag, np.float32(0))).astype(np.float64)  # finite at FLT_MAX
+    err = np.abs(got[fin] - want[fin])
+    assert np.all(err <= 1e-5 + 2 * ulp), f"{what}: max LSE error {err.max()}"
+
+
+@pytest.mark.parametrize("N,B,H,D,dtype,base2", [
+    (8, 40, 8, 128, "bf16", False),  # tiled
+    (4, 40, 8, 128, "f16", True),    # tiled, base 2
+    (4, 40, 8, 128, "f32", False),   # tiled, fp32 partials
+    (20, 9, 3, 128, "bf16", True),   # row kernel
+    (3, 5, 2, 12, "f16", False),     # element kernel
+])
+def test_extreme_finite_lses_and_outputs(lsec, N, B, H, D, dtype, base2):
+    """LSEs at the edges of fp32 (near +-FLT_MAX, subnormal, +-0, mixed with
+    NaN and +-inf) and outputs at the largest finite value of their format:
+    the combine still matches the oracle."""
+    _announce(f"extreme values N={N} B={B} H={H} D={D} {dtype} base2={base2}")
+    o, l = _extreme_inputs(N, B, H, D, dtype, seed=600 + N)
+    y, L = lsec.lsec_combine(to_dev(o, dtype, DEV), f32_to_dev(l, DEV), base_e=not base2,
+                             return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.lse_combine(o, l, dtype, base2)
+    _assert_rows_close(y, y_ref, o, dtype, "extreme")
+    _assert_lse_close_fp32(L, L_ref, "extreme")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_extreme_values_through_the_span_kernels(lsec, dtype):
+    """The same extreme rows through the packed receive side (span kernels)."""
+    N, B, Hl, D = 8, 16, 4, 128
+    _announce(f"extreme values, packed span kernel {dtype}")
+    o, l = _extreme_inputs(N, B, Hl, D, dtype, seed=700)
+    elem = np.uint32 if dtype == "f32" else np.uint16
+    P = 4 // np.dtype(elem).itemsize
+    tail = np.ascontiguousarray(l).view(np.uint32).view(elem).reshape(N, B, Hl, P)
+    recv_h = np.concatenate([np.ascontiguousarray(o).view(elem).reshape(N, B, Hl, D), tail], axis=3)
+    assert lsec.lsec_combine_path(N, B, Hl, D, packed=True, dtype=TDT[dtype]) in (
+        "combine_span_kernel", "combine_span32_kernel")
+    y, L = lsec.lsec_unpack_combine(to_dev(recv_h, dtype, DEV), return_lse=True)
+    torch.cuda.synchronize()
+    y_ref, L_ref = oracle.unpack_combine(recv_h, D, dtype, False)
+    _assert_rows_close(y, y_ref, o, dtype, "extreme packed")
+    _assert_lse_close_fp32(L, L_ref, "extreme packed")
 
 
 def test_nan_output_at_zero_weight_propagates(lsec):
